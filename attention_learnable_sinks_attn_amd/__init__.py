@@ -1,0 +1,181 @@
+"""Python binding of libattn_sink.so: sink attention forward / backward on MI355X (gfx950).
+
+Argument marshalling only: every step of the computation runs in the library's HIP kernels.
+PyTorch provides device memory and the current stream. The functions raise if the library was
+not built (``python -m attention_learnable_sinks_attn_amd.build``); there is no fallback.
+
+The operation (nmedialink.com "惊爆！GPT-OSS-20B强化学习…", section
+"GPT-OSS中的带注意力槽的注意力机制"): softmax over each row's visible scores plus one learnable
+per-head logit S_h, which takes probability mass but adds nothing to the output.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import torch
+
+__all__ = ["fwd", "bwd", "bwd_workspace_bytes", "bwd_kernel_names", "library_path", "load_library",
+           "AttnSinkError", "ERROR_CODES", "HEAD_DIM"]
+
+HEAD_DIM = 64
+_PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG_DIR, "libattn_sink.so")
+_lib = None
+
+ERROR_CODES = {
+    0: "ATTN_SINK_OK", -1: "ATTN_SINK_ERR_NULL_PTR", -2: "ATTN_SINK_ERR_BAD_SHAPE",
+    -3: "ATTN_SINK_ERR_UNSUPPORTED", -4: "ATTN_SINK_ERR_BAD_WINDOW", -5: "ATTN_SINK_ERR_WORKSPACE",
+    -6: "ATTN_SINK_ERR_HIP", -7: "ATTN_SINK_ERR_ALIGN",
+}
+
+
+class AttnSinkError(RuntimeError):
+    def __init__(self, code: int, what: str):
+        super().__init__(f"{what}: {ERROR_CODES.get(code, code)} ({_strerror(code)})")
+        self.code = code
+
+
+class Shape(ctypes.Structure):
+    """Mirror of ``attn_sink_shape`` in include/attn_sink.h."""
+    _fields_ = [("total_tokens", ctypes.c_int32), ("num_seqs", ctypes.c_int32), ("max_seqlen", ctypes.c_int32),
+                ("num_heads_q", ctypes.c_int32), ("num_heads_kv", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("softmax_scale", ctypes.c_float), ("out_dtype", ctypes.c_int32)]
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library() -> ctypes.CDLL:
+    """Load libattn_sink.so from the package directory (raises if it was not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(f"{_LIB_PATH} is missing: build it with `python -m attention_learnable_sinks_attn_amd.build`")
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp, i32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    shp = ctypes.POINTER(Shape)
+    lib.attn_sink_fwd.argtypes = [vp, vp, vp, vp, i32, i32, vp, shp, vp, vp, vp]
+    lib.attn_sink_fwd.restype = i32
+    lib.attn_sink_bwd_workspace_bytes.argtypes = [shp]
+    lib.attn_sink_bwd_workspace_bytes.restype = sz
+    bwd_args = [vp, vp, vp, vp, vp, vp, vp, i32, i32, vp, shp, vp, sz, vp, vp, vp, vp, vp]
+    lib.attn_sink_bwd.argtypes = bwd_args
+    lib.attn_sink_bwd.restype = i32
+    lib.attn_sink_bwd_timed.argtypes = bwd_args + [ctypes.POINTER(ctypes.c_void_p), i32]
+    lib.attn_sink_bwd_timed.restype = i32
+    lib.attn_sink_bwd_num_kernels.argtypes = []
+    lib.attn_sink_bwd_num_kernels.restype = i32
+    lib.attn_sink_bwd_kernel_name.argtypes = [i32]
+    lib.attn_sink_bwd_kernel_name.restype = ctypes.c_char_p
+    lib.attn_sink_strerror.argtypes = [i32]
+    lib.attn_sink_strerror.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _strerror(code: int) -> str:
+    try:
+        return load_library().attn_sink_strerror(int(code)).decode()
+    except Exception:  # pragma: no cover - message only
+        return "?"
+
+
+def make_shape(q: torch.Tensor, k: torch.Tensor, cu_seqlens: torch.Tensor, max_seqlen: int,
+               softmax_scale: Optional[float]) -> Shape:
+    return Shape(int(q.shape[0]), int(cu_seqlens.numel()) - 1, int(max_seqlen), int(q.shape[1]), int(k.shape[1]),
+                 int(q.shape[2]), float(softmax_scale) if softmax_scale else 0.0, 0)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else (t.data_ptr() or None)
+
+
+def _check(t: torch.Tensor, name: str, dtype: torch.dtype, device: torch.device):
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, sinks: torch.Tensor, cu_seqlens: torch.Tensor,
+        max_seqlen: int, causal: bool = True, window: int = 0, softmax_scale: Optional[float] = None,
+        out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None):
+    """Forward. q [T,Hq,64], k/v [T,Hkv,64] bf16; sinks [Hq] fp32; cu_seqlens [B+1] int32 (device).
+    Returns (out [T,Hq,64] fp32, lse [Hq,T] fp32)."""
+    lib = load_library()
+    dev = q.device
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _check(t, n, torch.bfloat16, dev)
+    _check(sinks, "sinks", torch.float32, dev)
+    _check(cu_seqlens, "cu_seqlens", torch.int32, dev)
+    T, Hq, d = q.shape
+    if out is None:
+        out = torch.empty((T, Hq, d), dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty((Hq, T), dtype=torch.float32, device=dev)
+    _check(out, "out", torch.float32, dev)
+    _check(lse, "lse", torch.float32, dev)
+    shape = make_shape(q, k, cu_seqlens, max_seqlen, softmax_scale)
+    rc = lib.attn_sink_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(sinks), int(bool(causal)), int(window), _ptr(cu_seqlens),
+                           ctypes.byref(shape), _ptr(out), _ptr(lse), _stream(dev))
+    if rc != 0:
+        raise AttnSinkError(rc, "attn_sink_fwd")
+    return out, lse
+
+
+def bwd_workspace_bytes(q: torch.Tensor, k: torch.Tensor, cu_seqlens: torch.Tensor, max_seqlen: int) -> int:
+    return int(load_library().attn_sink_bwd_workspace_bytes(ctypes.byref(make_shape(q, k, cu_seqlens, max_seqlen, None))))
+
+
+def bwd_kernel_names() -> Sequence[str]:
+    lib = load_library()
+    return [lib.attn_sink_bwd_kernel_name(i).decode() for i in range(lib.attn_sink_bwd_num_kernels())]
+
+
+def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, sinks: torch.Tensor, out: torch.Tensor, lse: torch.Tensor,
+        dout: torch.Tensor, cu_seqlens: torch.Tensor, max_seqlen: int, causal: bool = True, window: int = 0,
+        softmax_scale: Optional[float] = None, dq: Optional[torch.Tensor] = None, dk: Optional[torch.Tensor] = None,
+        dv: Optional[torch.Tensor] = None, dsinks: Optional[torch.Tensor] = None,
+        workspace: Optional[torch.Tensor] = None, events: Optional[Sequence[int]] = None):
+    """Backward. Returns (dq [T,Hq,64], dk [T,Hkv,64], dv [T,Hkv,64], dsinks [Hq]), all fp32.
+    ``events``: optional raw hipEvent_t handles (num kernels + 1) recorded around each kernel."""
+    lib = load_library()
+    dev = q.device
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (dout, "dout")):
+        _check(t, n, torch.bfloat16, dev)
+    for t, n in ((sinks, "sinks"), (out, "out"), (lse, "lse")):
+        _check(t, n, torch.float32, dev)
+    _check(cu_seqlens, "cu_seqlens", torch.int32, dev)
+    T, Hq, d = q.shape
+    Hkv = k.shape[1]
+    dq = torch.empty((T, Hq, d), dtype=torch.float32, device=dev) if dq is None else dq
+    dk = torch.empty((T, Hkv, d), dtype=torch.float32, device=dev) if dk is None else dk
+    dv = torch.empty((T, Hkv, d), dtype=torch.float32, device=dev) if dv is None else dv
+    dsinks = torch.empty((Hq,), dtype=torch.float32, device=dev) if dsinks is None else dsinks
+    for t, n in ((dq, "dq"), (dk, "dk"), (dv, "dv"), (dsinks, "dsinks")):
+        _check(t, n, torch.float32, dev)
+    shape = make_shape(q, k, cu_seqlens, max_seqlen, softmax_scale)
+    need = int(lib.attn_sink_bwd_workspace_bytes(ctypes.byref(shape)))
+    if workspace is None:
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
+    args = [_ptr(q), _ptr(k), _ptr(v), _ptr(sinks), _ptr(out), _ptr(lse), _ptr(dout), int(bool(causal)), int(window),
+            _ptr(cu_seqlens), ctypes.byref(shape), _ptr(workspace), workspace.numel() * workspace.element_size(),
+            _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dsinks), _stream(dev)]
+    if events is None:
+        rc = lib.attn_sink_bwd(*args)
+    else:
+        arr = (ctypes.c_void_p * len(events))(*events)
+        rc = lib.attn_sink_bwd_timed(*args, arr, len(events))
+    if rc != 0:
+        raise AttnSinkError(rc, "attn_sink_bwd")
+    return dq, dk, dv, dsinks

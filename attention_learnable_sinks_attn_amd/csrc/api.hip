@@ -1,0 +1,185 @@
+// C ABI of libattn_sink.so: argument checks, launch configuration, error mapping.
+// Every check runs on the host before anything is enqueued; the library allocates nothing.
+#include <math.h>
+#include <stdint.h>
+
+#include "attn_sink.h"
+#include "kernels.h"
+
+using namespace attn_sink;
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_shape(const attn_sink_shape* s) {
+  if (s == nullptr) return ATTN_SINK_ERR_NULL_PTR;
+  if (s->total_tokens < 0 || s->num_seqs < 1 || s->num_heads_q < 1 || s->num_heads_kv < 1 ||
+      s->max_seqlen < 0 || s->max_seqlen > s->total_tokens || s->num_heads_q % s->num_heads_kv != 0) {
+    return ATTN_SINK_ERR_BAD_SHAPE;
+  }
+  if (s->head_dim != kHeadDim || s->out_dtype != ATTN_SINK_F32) return ATTN_SINK_ERR_UNSUPPORTED;
+  // Element offsets are 64-bit in the kernels, but grid sizes and per-head row indices are 32-bit.
+  const long long rows_q = (long long)s->total_tokens * s->num_heads_q;
+  if (rows_q > (1LL << 40)) return ATTN_SINK_ERR_BAD_SHAPE;
+  const long long nq = ((long long)s->max_seqlen + 63) / 64;
+  if (nq * s->num_heads_q * (long long)s->num_seqs >= (1LL << 31)) return ATTN_SINK_ERR_BAD_SHAPE;
+  return ATTN_SINK_OK;
+}
+
+int heads_per_group_split(int G) { return G % 4 == 0 ? 4 : (G % 2 == 0 ? 2 : 1); }
+
+float resolve_scale(const attn_sink_shape* s) {
+  return s->softmax_scale > 0.0f ? s->softmax_scale : 1.0f / sqrtf((float)s->head_dim);
+}
+
+int dsink_slots(const attn_sink_shape* s) { return s->total_tokens / kDqRowsPerWave + s->num_seqs + 1; }
+
+size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+size_t workspace_bytes(const attn_sink_shape* s) {
+  return round256((size_t)s->num_heads_q * s->total_tokens * sizeof(float)) +
+         round256((size_t)s->num_heads_q * dsink_slots(s) * sizeof(float));
+}
+
+int bwd_impl(const void* q, const void* k, const void* v, const float* sinks, const void* out, const float* lse,
+             const void* dout, int causal, int window, const int32_t* cu_seqlens, const attn_sink_shape* shape,
+             void* workspace, size_t ws_bytes, float* dq, float* dk, float* dv, float* dsinks, hipStream_t stream,
+             void* const* events, int num_events) {
+  int rc = check_shape(shape);
+  if (rc) return rc;
+  if (window > 0 && !causal) return ATTN_SINK_ERR_BAD_WINDOW;
+  if (sinks == nullptr || cu_seqlens == nullptr || dsinks == nullptr) return ATTN_SINK_ERR_NULL_PTR;
+  const int T = shape->total_tokens;
+  if (T > 0 && (!q || !k || !v || !out || !lse || !dout || !dq || !dk || !dv)) return ATTN_SINK_ERR_NULL_PTR;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(dout) || !aligned16(dq) ||
+      !aligned16(dk) || !aligned16(dv)) {
+    return ATTN_SINK_ERR_ALIGN;
+  }
+  const size_t need = workspace_bytes(shape);
+  if (workspace == nullptr || ws_bytes < need || !aligned16(workspace)) return ATTN_SINK_ERR_WORKSPACE;
+  if (events != nullptr && num_events != kBwdNumKernels + 1) return ATTN_SINK_ERR_BAD_SHAPE;
+
+  BwdArgs a;
+  a.q = static_cast<const __bf16*>(q);
+  a.k = static_cast<const __bf16*>(k);
+  a.v = static_cast<const __bf16*>(v);
+  a.sinks = sinks;
+  a.out = static_cast<const float*>(out);
+  a.lse = lse;
+  a.dout = static_cast<const __bf16*>(dout);
+  a.cu = cu_seqlens;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.dsinks = dsinks;
+  a.dws = static_cast<float*>(workspace);
+  a.dsink_part = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                          round256((size_t)shape->num_heads_q * T * sizeof(float)));
+  a.n_slots = dsink_slots(shape);
+  a.T = T;
+  a.B = shape->num_seqs;
+  a.Hq = shape->num_heads_q;
+  a.Hkv = shape->num_heads_kv;
+  a.G = a.Hq / a.Hkv;
+  a.hpw = heads_per_group_split(a.G);
+  a.kv_waves = heads_per_group_split(a.G);
+  a.n_qblocks = (shape->max_seqlen + kDqRowsPerWave - 1) / kDqRowsPerWave;
+  a.n_kblocks = (shape->max_seqlen + kKvKeysPerBlock - 1) / kKvKeysPerBlock;
+  a.causal = causal ? 1 : 0;
+  a.window = window > 0 ? window : 0;
+  a.scale = resolve_scale(shape);
+  a.scale_log2 = a.scale * kLog2e;
+
+  typedef hipError_t (*launcher)(const BwdArgs&, hipStream_t);
+  const launcher steps[kBwdNumKernels] = {launch_bwd_prep, launch_bwd_dkdv, launch_bwd_dq, launch_bwd_dsink};
+  for (int i = 0; i < kBwdNumKernels; ++i) {
+    if (events && hipEventRecord(static_cast<hipEvent_t>(events[i]), stream) != hipSuccess) return ATTN_SINK_ERR_HIP;
+    if (steps[i](a, stream) != hipSuccess) return ATTN_SINK_ERR_HIP;
+  }
+  if (events && hipEventRecord(static_cast<hipEvent_t>(events[kBwdNumKernels]), stream) != hipSuccess) {
+    return ATTN_SINK_ERR_HIP;
+  }
+  return ATTN_SINK_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_sink_fwd(const void* q, const void* k, const void* v, const float* sinks, int causal, int window,
+                  const int32_t* cu_seqlens, const attn_sink_shape* shape, void* out, float* lse,
+                  hipStream_t stream) {
+  int rc = check_shape(shape);
+  if (rc) return rc;
+  if (window > 0 && !causal) return ATTN_SINK_ERR_BAD_WINDOW;
+  if (sinks == nullptr || cu_seqlens == nullptr) return ATTN_SINK_ERR_NULL_PTR;
+  const int T = shape->total_tokens;
+  if (T > 0 && (!q || !k || !v || !out || !lse)) return ATTN_SINK_ERR_NULL_PTR;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return ATTN_SINK_ERR_ALIGN;
+
+  FwdArgs a;
+  a.q = static_cast<const __bf16*>(q);
+  a.k = static_cast<const __bf16*>(k);
+  a.v = static_cast<const __bf16*>(v);
+  a.sinks = sinks;
+  a.cu = cu_seqlens;
+  a.out = static_cast<float*>(out);
+  a.lse = lse;
+  a.T = T;
+  a.B = shape->num_seqs;
+  a.Hq = shape->num_heads_q;
+  a.Hkv = shape->num_heads_kv;
+  a.G = a.Hq / a.Hkv;
+  a.hpw = heads_per_group_split(a.G);
+  a.n_qblocks = (shape->max_seqlen + kFwdRowsPerWave - 1) / kFwdRowsPerWave;
+  a.causal = causal ? 1 : 0;
+  a.window = window > 0 ? window : 0;
+  a.scale_log2 = resolve_scale(shape) * kLog2e;
+  return launch_fwd(a, stream) == hipSuccess ? ATTN_SINK_OK : ATTN_SINK_ERR_HIP;
+}
+
+size_t attn_sink_bwd_workspace_bytes(const attn_sink_shape* shape) {
+  if (check_shape(shape) != ATTN_SINK_OK) return 0;
+  return workspace_bytes(shape);
+}
+
+int attn_sink_bwd(const void* q, const void* k, const void* v, const float* sinks, const void* out, const float* lse,
+                  const void* dout, int causal, int window, const int32_t* cu_seqlens, const attn_sink_shape* shape,
+                  void* workspace, size_t workspace_bytes, float* dq, float* dk, float* dv, float* dsinks,
+                  hipStream_t stream) {
+  return bwd_impl(q, k, v, sinks, out, lse, dout, causal, window, cu_seqlens, shape, workspace, workspace_bytes, dq,
+                  dk, dv, dsinks, stream, nullptr, 0);
+}
+
+int attn_sink_bwd_timed(const void* q, const void* k, const void* v, const float* sinks, const void* out,
+                        const float* lse, const void* dout, int causal, int window, const int32_t* cu_seqlens,
+                        const attn_sink_shape* shape, void* workspace, size_t workspace_bytes, float* dq, float* dk,
+                        float* dv, float* dsinks, hipStream_t stream, void* const* events, int num_events) {
+  return bwd_impl(q, k, v, sinks, out, lse, dout, causal, window, cu_seqlens, shape, workspace, workspace_bytes, dq,
+                  dk, dv, dsinks, stream, events, num_events);
+}
+
+int attn_sink_bwd_num_kernels(void) { return kBwdNumKernels; }
+
+const char* attn_sink_bwd_kernel_name(int i) {
+  static const char* const names[kBwdNumKernels] = {"attn_sink_bwd_prep_kernel", "attn_sink_bwd_dkdv_kernel",
+                                                    "attn_sink_bwd_dq_kernel", "attn_sink_bwd_dsink_kernel"};
+  return (i >= 0 && i < kBwdNumKernels) ? names[i] : nullptr;
+}
+
+const char* attn_sink_strerror(int code) {
+  switch (code) {
+    case ATTN_SINK_OK: return "success";
+    case ATTN_SINK_ERR_NULL_PTR: return "a required pointer is NULL";
+    case ATTN_SINK_ERR_BAD_SHAPE: return "invalid shape (sizes, head counts or max_seqlen)";
+    case ATTN_SINK_ERR_UNSUPPORTED: return "unsupported head_dim or output dtype (head_dim 64, float32 outputs)";
+    case ATTN_SINK_ERR_BAD_WINDOW: return "a sliding window requires causal attention";
+    case ATTN_SINK_ERR_WORKSPACE: return "workspace missing or smaller than attn_sink_bwd_workspace_bytes()";
+    case ATTN_SINK_ERR_HIP: return "a HIP launch failed";
+    case ATTN_SINK_ERR_ALIGN: return "a tensor base pointer is not 16-byte aligned";
+    default: return "unknown error code";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,138 @@
+// Device-side building blocks shared by the sink-attention kernels (gfx950 / CDNA4 only).
+//
+// Matrix products use v_mfma_f32_32x32x16_bf16 (bf16 inputs, fp32 accumulation). Operand layout
+// of one 64-lane wave for C[32x32] += A[32x16] * B[16x32]:
+//   A: lane l holds row (l % 32), eight consecutive k slots 8*(l/32) .. 8*(l/32)+7
+//   B: lane l holds column (l % 32), the same eight k slots
+//   C: lane l holds column (l % 32), rows 8*(i/4) + 4*(l/32) + (i%4) for i = 0..15
+// Only the pairing of k slots between A and B matters to the product, so a kernel may put any
+// logical index in a slot as long as A and B agree.
+//
+// Row permutation used throughout: when a 32-row A block is loaded with row r holding element
+// swap23(r) (bits 2 and 3 of r exchanged), lane group g = l/32 of the C result holds, in its
+// registers 8c..8c+7, the eight CONSECUTIVE elements 16c + 8g + (0..7). That makes the C block
+// directly usable as the B operand of a second product that contracts over those rows, and lets
+// the matching A operand be read from LDS as one 16-byte vector.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn_sink {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kHeadDim = 64;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegInf = -__builtin_inff();
+
+__device__ __forceinline__ f32x16 mfma_32x32x16(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ int swap23(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
+
+// Index (within a 32-row C block) of register i held by lane group g, after the swap23 load.
+__device__ __forceinline__ int c_row(int i, int g) { return 16 * (i >> 3) + 8 * g + (i & 7); }
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// Registers 8c..8c+7 of a C block, rounded to bf16 (round to nearest even).
+__device__ __forceinline__ bf16x8 pack8(const f32x16& c, int chunk) {
+  f32x8 v;
+  if (chunk == 0) {
+    v = (f32x8){c[0], c[1], c[2], c[3], c[4], c[5], c[6], c[7]};
+  } else {
+    v = (f32x8){c[8], c[9], c[10], c[11], c[12], c[13], c[14], c[15]};
+  }
+  return __builtin_convertvector(v, bf16x8);
+}
+
+// Rounding residual of pack8: bf16(c - hi), so that hi + lo carries about 16 significant bits.
+__device__ __forceinline__ bf16x8 residual8(const f32x16& c, int chunk, const bf16x8& hi) {
+  f32x8 r;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) r[e] = c[8 * chunk + e] - (float)hi[e];
+  return __builtin_convertvector(r, bf16x8);
+}
+
+// Probabilities above this value make the bf16 rounding of P and dS visible in the sums over
+// query rows and heads (dK, dV) and over keys (dQ); tiles that hold one get the residual product.
+constexpr float kSplitThreshold = 0.0625f;
+
+__device__ __forceinline__ bool wave_any(bool pred) { return __builtin_amdgcn_ballot_w64(pred) != 0; }
+
+__device__ __forceinline__ bf16x8 load_bf16x8(const __bf16* p) { return *reinterpret_cast<const bf16x8*>(p); }
+
+__device__ __forceinline__ bf16x8 zero_bf16x8() {
+  bf16x8 z;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) z[i] = (__bf16)0.0f;
+  return z;
+}
+
+__device__ __forceinline__ f32x16 zero_f32x16() {
+  f32x16 z;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = 0.0f;
+  return z;
+}
+
+__device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32); }
+
+// Visibility of key j from query i inside one sequence (the sink is always visible).
+__device__ __forceinline__ bool visible(int i, int j, int len, int causal, int window) {
+  bool ok = j < len;
+  if (causal) ok = ok && (j <= i);
+  if (window > 0) ok = ok && (j > i - window);
+  return ok;
+}
+
+// Work descriptors (filled on the host).
+struct FwdArgs {
+  const __bf16* q;
+  const __bf16* k;
+  const __bf16* v;
+  const float* sinks;
+  const int32_t* cu;
+  float* out;
+  float* lse;
+  int T, B, Hq, Hkv, G;  // G = Hq / Hkv
+  int hpw;               // query heads per workgroup (= waves per workgroup), divides G
+  int n_qblocks;         // ceil(max_seqlen / rows per wave)
+  int causal, window;
+  float scale_log2;      // softmax scale * log2(e)
+};
+
+struct BwdArgs {
+  const __bf16* q;
+  const __bf16* k;
+  const __bf16* v;
+  const float* sinks;
+  const float* out;
+  const float* lse;
+  const __bf16* dout;
+  const int32_t* cu;
+  float* dq;
+  float* dk;
+  float* dv;
+  float* dsinks;
+  float* dws;        // D_i = rowsum(dO * O), [Hq, T]
+  float* dsink_part; // per (head, row-block slot) partial sums of P_sink * D~, [Hq, n_slots]
+  int n_slots;
+  int T, B, Hq, Hkv, G;
+  int hpw;            // dQ kernel: query heads per workgroup
+  int kv_waves;       // dK/dV kernel: waves per workgroup (each takes G / kv_waves heads)
+  int n_qblocks;      // dQ kernel grid rows
+  int n_kblocks;      // dK/dV kernel grid rows
+  int causal, window;
+  float scale;        // softmax scale
+  float scale_log2;   // softmax scale * log2(e)
+};
+
+}  // namespace attn_sink

@@ -1,0 +1,21 @@
+// Host-side launchers of the sink-attention kernels (one translation unit per pass).
+#pragma once
+
+#include "common.h"
+
+namespace attn_sink {
+
+constexpr int kFwdRowsPerWave = 64;   // queries per wave in the forward
+constexpr int kDqRowsPerWave = 64;    // queries per wave in the row-parallel dQ / dSink pass
+constexpr int kKvKeysPerBlock = 64;   // keys per workgroup in the column-parallel dK / dV pass
+
+hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
+
+// Backward passes, in enqueue order.
+constexpr int kBwdNumKernels = 4;
+hipError_t launch_bwd_prep(const BwdArgs& a, hipStream_t stream);      // D_i, zero dSink partials
+hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream);      // dK, dV
+hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream);        // dQ, dSink partials
+hipError_t launch_bwd_dsink(const BwdArgs& a, hipStream_t stream);     // dSink = -sum partials
+
+}  // namespace attn_sink

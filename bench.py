@@ -1,0 +1,195 @@
+"""Benchmark: sink-attention forward + backward on one MI355X.
+
+One step = attn_sink_fwd + attn_sink_bwd over one batch of synthetic GPT-OSS-shaped inputs that are
+already resident in HBM. Default workload: 4096 tokens, 64 query heads sharing 8 KV heads,
+head_dim 64, causal, bf16 inputs (the headline configuration).
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload causal4k] [--no-cpu-baseline]
+
+Prints one JSON line. ``value`` is algorithmic TFLOP/s over the timed steps: 4*d FLOPs per visible
+(query, key, head) in the forward (QK^T and PV) plus 10*d in the backward (S, dP, dV, dK, dQ);
+recomputation and masked tile work are not counted. ``roofline`` describes the kernel with the
+largest share of the step time, timed with HIP events recorded on the stream the kernels run on.
+``cpu_baseline`` times the fp64 CPU oracle on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import math
+import os
+import sys
+import time
+
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import attention_learnable_sinks_attn_amd as asa  # noqa: E402
+from workloads import WORKLOAD_NAMES, make_workload_inputs, visible_pairs, workload  # noqa: E402
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+HBM_PEAK_GBS = 8000.0
+METRIC = "sink-attention fwd+bwd bf16 TFLOP/s + % MFMA peak (GQA 64/8, d=64, 4k causal)"
+
+# Algorithmic FLOPs per visible (query, key, head) pair, per kernel, in units of head_dim:
+# forward QK^T + PV; dK/dV pass S, dP, dV, dK; dQ pass dQ only (its S/dP recomputation is not counted).
+KERNEL_FLOPS_PER_PAIR_D = {
+    "attn_sink_fwd_kernel": 4,
+    "attn_sink_bwd_prep_kernel": 0,
+    "attn_sink_bwd_dkdv_kernel": 8,
+    "attn_sink_bwd_dq_kernel": 2,
+    "attn_sink_bwd_dsink_kernel": 0,
+}
+
+
+class Hip:
+    """The few HIP runtime calls needed for events on an arbitrary stream."""
+
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so")
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def event(self):
+        e = ctypes.c_void_p()
+        rc = self.lib.hipEventCreate(ctypes.byref(e))
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreate failed: {rc}")
+        return e.value
+
+    def record(self, ev, stream):
+        rc = self.lib.hipEventRecord(ev, stream)
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed: {rc}")
+
+    def elapsed_ms(self, a, b):
+        out = ctypes.c_float()
+        rc = self.lib.hipEventElapsedTime(ctypes.byref(out), a, b)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed: {rc}")
+        return out.value
+
+
+def cpu_baseline(inp, w, max_heads_kv: int):
+    """Time the fp64 oracle (forward + backward) on the first `max_heads_kv` KV groups."""
+    import numpy as np  # noqa: F401
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    G = w.hq // w.hkv
+    hq_s = G * max_heads_kv
+    q = inp.q[:, :hq_s]
+    dout = inp.dout[:, :hq_s]
+    k = inp.k[:, :max_heads_kv]
+    v = inp.v[:, :max_heads_kv]
+    sinks = inp.sinks[:hq_s]
+    t0 = time.perf_counter()
+    oracle.backward(q, k, v, sinks, dout, inp.cu_seqlens, inp.causal, inp.window, return_forward=True)
+    dt = time.perf_counter() - t0
+    flops = visible_pairs(inp.lengths, inp.causal, inp.window) * hq_s * 14 * w.d
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{w.name}: all {inp.total_tokens} rows of {max_heads_kv} KV group(s) ({hq_s} query heads), "
+                      f"fwd+bwd in fp64 numpy, {dt:.2f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="causal4k", choices=WORKLOAD_NAMES)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-kv-groups", type=int, default=8)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+
+    w = workload(args.workload, args.seed)
+    inp = make_workload_inputs(args.workload, args.seed)
+    dev = torch.device("cuda:0")
+    q, k, v, dout = (t.to(dev) for t in (inp.q, inp.k, inp.v, inp.dout))
+    sinks = inp.sinks.to(dev)
+    cu = inp.cu_seqlens.to(dev)
+    T, Hq, d = q.shape
+    Hkv = k.shape[1]
+    out = torch.empty((T, Hq, d), dtype=torch.float32, device=dev)
+    lse = torch.empty((Hq, T), dtype=torch.float32, device=dev)
+    dq = torch.empty_like(out)
+    dk = torch.empty((T, Hkv, d), dtype=torch.float32, device=dev)
+    dv = torch.empty_like(dk)
+    dsinks = torch.empty((Hq,), dtype=torch.float32, device=dev)
+    ws = torch.empty((asa.bwd_workspace_bytes(q, k, cu, inp.max_seqlen),), dtype=torch.uint8, device=dev)
+    names = ["attn_sink_fwd_kernel"] + list(asa.bwd_kernel_names())
+
+    hip = Hip()
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    nk = len(names)
+    events = [[hip.event() for _ in range(nk + 1)] for _ in range(args.steps)]
+
+    def step(evs=None):
+        if evs is not None:
+            hip.record(evs[0], stream)
+        asa.fwd(q, k, v, sinks, cu, inp.max_seqlen, inp.causal, inp.window, out=out, lse=lse)
+        asa.bwd(q, k, v, sinks, out, lse, dout, cu, inp.max_seqlen, inp.causal, inp.window, dq=dq, dk=dk, dv=dv,
+                dsinks=dsinks, workspace=ws, events=None if evs is None else evs[1:])
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record()
+    for s in range(args.steps):
+        step(events[s])
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = start.elapsed_time(end) / args.steps
+
+    per_kernel = {n: 0.0 for n in names}
+    for s in range(args.steps):
+        for i, n in enumerate(names):
+            per_kernel[n] += hip.elapsed_ms(events[s][i], events[s][i + 1]) / args.steps
+
+    pairs = visible_pairs(inp.lengths, inp.causal, inp.window) * Hq
+    flops = pairs * 14 * d
+    tflops = flops / (ms_step * 1e-3) / 1e12
+    dom = max(per_kernel, key=per_kernel.get)
+    dom_flops = pairs * KERNEL_FLOPS_PER_PAIR_D[dom] * d
+    achieved = dom_flops / (per_kernel[dom] * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                "avg_launch_ms": round(per_kernel[dom], 4)}
+    res = {
+        "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "tokens": int(T), "seqs": len(inp.lengths), "heads_q": int(Hq),
+                   "heads_kv": int(Hkv), "head_dim": int(d), "causal": inp.causal, "window": inp.window,
+                   "seed": args.seed, "parallelism": "none (1 GPU)"},
+        "pct_mfma_peak": round(100 * tflops / MFMA_BF16_PEAK_TFLOPS, 2),
+        "kernel_ms": {n: round(t, 4) for n, t in per_kernel.items()},
+        "wall_s_timed": round(wall, 4),
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(inp, w, args.cpu_kv_groups)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,133 @@
+/*
+ * attn_sink.h - C ABI of the MI355X (gfx950) sink-attention library (libattn_sink.so).
+ *
+ * Operation. Scaled dot-product attention in which every query head h owns one learnable
+ * logit S_h (the "sink"). The sink joins each row's softmax denominator but has no value row,
+ * so it takes probability mass without adding to the output:
+ *     S_ij  = scale * q_i . k_j
+ *     P_ij  = exp(S_ij) / (sum_{j' visible} exp(S_ij') + exp(S_h))
+ *     O_i   = sum_{j visible} P_ij v_j
+ * Defined on the nmedialink.com page "惊爆！GPT-OSS-20B强化学习，训练速度狂飙、超稳定！",
+ * section "GPT-OSS中的带注意力槽的注意力机制" (concat the sink column, softmax, drop it,
+ * multiply by V) and section "数学公式深入解读" (eq. P_ij and the sink probability P_{i,h}).
+ * The backward returns dQ, dK, dV and dL/dS_h = -sum_i P_{i,h} D_i with
+ * D_i = sum_j P_ij dO_i.v_j = dO_i.O_i (same page, section "反向传播的实现", simplified
+ * equation).
+ *
+ * Conventions shared by every entry point
+ *  - Packed varlen layout: B sequences are stored back to back; rows cu_seqlens[b] ..
+ *    cu_seqlens[b+1]-1 belong to sequence b. Attention never crosses a sequence boundary
+ *    (same page, section "结合Flash Attention V3的序列并行技术": padding removed, tokens
+ *    packed into one list). A fixed-shape batch is B = 1, cu_seqlens = {0, N}.
+ *  - Tensors (device pointers, contiguous, row-major, base 16-byte aligned):
+ *      q, dout   [T, Hq, 64]  bfloat16
+ *      k, v      [T, Hkv, 64] bfloat16
+ *      sinks     [Hq]         float32 (one logit per query head, natural-log units, NOT scaled)
+ *      out       [T, Hq, 64]  float32
+ *      lse       [Hq, T]      float32, natural log of the full denominator (sink included)
+ *      dq        [T, Hq, 64]  float32;  dk, dv [T, Hkv, 64] float32;  dsinks [Hq] float32
+ *      cu_seqlens [B+1] int32 on the device, cu[0] = 0, non-decreasing, cu[B] = T
+ *  - GQA: query head h reads KV head h / (Hq / Hkv); Hq must be a multiple of Hkv.
+ *  - Masks: causal != 0 lets query i see keys j <= i of its own sequence. window = W > 0
+ *    (requires causal) further restricts to j > i - W, i.e. exactly the last W keys including
+ *    itself. window <= 0 means no window. The sink is visible from every row, is never masked and
+ *    does not count toward W. The sink is added after scaling: it is never multiplied by scale.
+ *  - Outputs are overwritten, never accumulated into. The caller owns every buffer; the library
+ *    allocates nothing, keeps no global state, and only enqueues work on `stream` (NULL = the
+ *    default stream). Calls return before the GPU work finishes; errors raised by the device
+ *    surface at the caller's next synchronisation.
+ *  - Errors: 0 on success, a negative ATTN_SINK_ERR_* code otherwise. All argument checks run on
+ *    the host before anything is enqueued; a failing call enqueues nothing. The contents of
+ *    cu_seqlens are trusted (they live on the device).
+ */
+#ifndef ATTN_SINK_H_
+#define ATTN_SINK_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Same type as HIP's hipStream_t; repeated here so that C callers need no HIP headers. */
+typedef struct ihipStream_t* hipStream_t;
+
+enum {
+  ATTN_SINK_OK = 0,
+  ATTN_SINK_ERR_NULL_PTR = -1,    /* a required pointer (or the shape struct) is NULL */
+  ATTN_SINK_ERR_BAD_SHAPE = -2,   /* T < 0, B < 1, Hq < 1, Hkv < 1, Hq % Hkv != 0, max_seqlen < 0
+                                     or max_seqlen > T, or a size that overflows 32-bit indexing */
+  ATTN_SINK_ERR_UNSUPPORTED = -3, /* head_dim != 64 or out_dtype != ATTN_SINK_F32 */
+  ATTN_SINK_ERR_BAD_WINDOW = -4,  /* window > 0 without causal */
+  ATTN_SINK_ERR_WORKSPACE = -5,   /* workspace NULL or smaller than attn_sink_bwd_workspace_bytes() */
+  ATTN_SINK_ERR_HIP = -6,         /* a HIP launch failed (hipGetLastError after the launch) */
+  ATTN_SINK_ERR_ALIGN = -7        /* a tensor base pointer is not 16-byte aligned */
+};
+
+enum { ATTN_SINK_F32 = 0, ATTN_SINK_BF16 = 1 };
+
+/* Problem description, passed by pointer; read on the host only, never retained. */
+typedef struct attn_sink_shape {
+  int32_t total_tokens;  /* T = cu_seqlens[B] */
+  int32_t num_seqs;      /* B >= 1 */
+  int32_t max_seqlen;    /* >= every cu[b+1]-cu[b]; sizes the grid (a larger value only adds idle blocks) */
+  int32_t num_heads_q;   /* Hq */
+  int32_t num_heads_kv;  /* Hkv, divides Hq */
+  int32_t head_dim;      /* must be 64 */
+  float softmax_scale;   /* <= 0 selects 1/sqrt(head_dim) */
+  int32_t out_dtype;     /* must be ATTN_SINK_F32 (out, dq, dk, dv are float32) */
+} attn_sink_shape;
+
+/*
+ * Forward: writes out [T, Hq, 64] (float32) and lse [Hq, T] (float32, natural log, sink included:
+ * lse_i = log(sum_j exp(S_ij) + exp(S_h))). Rows of zero-length sequences are not touched (there
+ * are none). Inputs are read only.
+ */
+int attn_sink_fwd(const void* q, const void* k, const void* v, const float* sinks, int causal, int window,
+                  const int32_t* cu_seqlens, const attn_sink_shape* shape, void* out, float* lse,
+                  hipStream_t stream);
+
+/*
+ * Bytes of device workspace attn_sink_bwd needs for this shape (D_i rows and per-block dSink
+ * partial sums, 256-byte aligned). Returns 0 if `shape` is NULL or invalid.
+ */
+size_t attn_sink_bwd_workspace_bytes(const attn_sink_shape* shape);
+
+/*
+ * Backward of L with upstream gradient dout = dL/dO, given the forward's out and lse:
+ *   dq [T, Hq, 64], dk / dv [T, Hkv, 64] (float32, summed over the query heads of each KV group),
+ *   dsinks [Hq] (float32, dL/dS_h summed over every row of every sequence).
+ * workspace: caller-owned device memory of at least attn_sink_bwd_workspace_bytes(shape) bytes;
+ * its contents on entry do not matter and are clobbered. The result is deterministic: no atomics
+ * decide any output, so repeated calls on the same inputs give bitwise identical results.
+ */
+int attn_sink_bwd(const void* q, const void* k, const void* v, const float* sinks, const void* out,
+                  const float* lse, const void* dout, int causal, int window, const int32_t* cu_seqlens,
+                  const attn_sink_shape* shape, void* workspace, size_t workspace_bytes, float* dq, float* dk,
+                  float* dv, float* dsinks, hipStream_t stream);
+
+/*
+ * Same as attn_sink_bwd, and additionally records events[0..num_events-1] on `stream` around the
+ * backward's kernels (events[i] before kernel i, events[num_kernels] after the last), for
+ * per-kernel timing. `events` holds hipEvent_t handles created by the caller; num_events must be
+ * attn_sink_bwd_num_kernels() + 1. Passing events == NULL behaves like attn_sink_bwd.
+ */
+int attn_sink_bwd_timed(const void* q, const void* k, const void* v, const float* sinks, const void* out,
+                        const float* lse, const void* dout, int causal, int window, const int32_t* cu_seqlens,
+                        const attn_sink_shape* shape, void* workspace, size_t workspace_bytes, float* dq,
+                        float* dk, float* dv, float* dsinks, hipStream_t stream, void* const* events,
+                        int num_events);
+
+/* Number of kernels attn_sink_bwd enqueues, and the name of kernel i (static string, or NULL). */
+int attn_sink_bwd_num_kernels(void);
+const char* attn_sink_bwd_kernel_name(int i);
+
+/* Static, human-readable description of an ATTN_SINK_* code (never NULL). */
+const char* attn_sink_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_SINK_H_ */

@@ -1,0 +1,200 @@
+"""Parity of the HIP path (through the C ABI) against the fp64 CPU oracle.
+
+Tolerances (GPU vs oracle): max-abs 1e-2 on O, dQ, dK, dV (fp32 outputs of bf16 ~N(0,1) inputs),
+max-abs 1e-3 on the fp32 LSE, and 1e-2 relative error per head on dSink.
+
+Small cases compare every element; they span several 64-row / 64-key tiles and end in ragged
+tails. The full-size GPT-OSS-shaped workloads run in the same launch configuration the bench
+times and are compared on sampled rows, keys and heads that the oracle evaluates one by one.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import attention_learnable_sinks_attn_amd as asa
+import oracle
+from workloads import make_inputs, make_workload_inputs
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"out": 1e-2, "dq": 1e-2, "dk": 1e-2, "dv": 1e-2, "lse": 1e-3}
+TOL_DSINK_REL = 1e-2
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def run_gpu(inp, scale=None, repeat_bwd=False):
+    dev = torch.device("cuda:0")
+    q, k, v, dout = (t.to(dev).contiguous() for t in (inp.q, inp.k, inp.v, inp.dout))
+    sinks = inp.sinks.to(dev)
+    cu = inp.cu_seqlens.to(dev)
+    out, lse = asa.fwd(q, k, v, sinks, cu, inp.max_seqlen, inp.causal, inp.window, scale)
+    dq, dk, dv, ds = asa.bwd(q, k, v, sinks, out, lse, dout, cu, inp.max_seqlen, inp.causal, inp.window, scale)
+    res = {"out": out, "lse": lse, "dq": dq, "dk": dk, "dv": dv, "dsinks": ds}
+    if repeat_bwd:
+        res2 = asa.bwd(q, k, v, sinks, out, lse, dout, cu, inp.max_seqlen, inp.causal, inp.window, scale)
+        res["again"] = res2
+    torch.cuda.synchronize()
+    return res
+
+
+def maxabs(a, b):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    if a.size == 0:
+        return 0.0
+    return float(np.max(np.abs(a - b)))
+
+
+def check_dsink(got, ref, heads=None, label=""):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    rel = np.abs(got - ref) / np.maximum(np.abs(ref), 1e-30)
+    exact_zero = (ref == 0) & (got == 0)
+    rel = np.where(exact_zero, 0.0, rel)
+    worst = int(np.argmax(rel)) if rel.size else 0
+    say(f"  dsinks{label}: max per-head rel err {rel.max() if rel.size else 0:.3e} (head {heads[worst] if heads else worst})")
+    assert (rel <= TOL_DSINK_REL).all(), f"dSink rel err {rel.max():.3e} > {TOL_DSINK_REL}"
+
+
+def check_full(inp, g, scale=None):
+    out, lse = oracle.forward(inp.q, inp.k, inp.v, inp.sinks, inp.cu_seqlens, inp.causal, inp.window, scale)
+    dq, dk, dv, ds = oracle.backward(inp.q, inp.k, inp.v, inp.sinks, inp.dout, inp.cu_seqlens, inp.causal,
+                                     inp.window, scale)
+    ref = {"out": out, "lse": lse, "dq": dq, "dk": dk, "dv": dv}
+    for name, r in ref.items():
+        x = g[name].double().cpu().numpy()
+        assert np.isfinite(x).all(), f"{name} has non-finite values"
+        err = maxabs(x, r)
+        say(f"  {name}: max-abs err {err:.3e} (max |ref| {np.abs(r).max() if r.size else 0:.3f})")
+        assert err <= TOL[name], f"{name}: max-abs err {err:.3e} > {TOL[name]}"
+    check_dsink(g["dsinks"].double().cpu().numpy(), ds)
+
+
+SMALL_CASES = {
+    # name: (lengths, hq, hkv, causal, window, extra)
+    "mha_causal_ragged": ((300,), 2, 2, True, 0, {}),
+    "gqa8_varlen_causal": ((130, 0, 1, 257, 64, 200), 16, 2, True, 0, {}),
+    "gqa2_window37": ((300, 77), 4, 2, True, 37, {}),
+    "gqa8_window128": ((513, 129), 8, 1, True, 128, {}),
+    "gqa4_noncausal": ((190, 65, 1), 8, 2, False, 0, {}),
+    "mha_single_tokens": ((1, 1, 3, 1), 2, 2, True, 0, {}),
+    "window_ge_len": ((150, 40), 4, 1, True, 1000, {}),
+    "window1": ((97,), 2, 1, True, 1, {}),
+    "sink_neg_inf_window": ((200, 63), 4, 2, True, 20, {"sinks": [-math.inf] * 4}),
+    "sink_neg_inf_causal": ((130,), 2, 1, True, 0, {"sinks": [-math.inf, 0.5]}),
+    "sink_plus20": ((160,), 2, 1, True, 0, {"sinks": [20.0, -3.0]}),
+    "sinks_x3": ((300,), 4, 1, True, 0, {"sink_scale": 3.0}),
+    "scale_0p07": ((140,), 2, 2, True, 0, {"scale": 0.07}),
+    "exact_tiles": ((256, 128), 8, 8, True, 64, {}),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL_CASES))
+def test_small_parity(name):
+    lengths, hq, hkv, causal, window, extra = SMALL_CASES[name]
+    inp = make_inputs(lengths, hq, hkv, 64, causal=causal, window=window, seed=7,
+                      sink_scale=extra.get("sink_scale", 1.0), sinks_override=extra.get("sinks"))
+    scale = extra.get("scale")
+    say(f"[gpu] small case {name}: lengths={lengths} hq={hq} hkv={hkv} causal={causal} window={window}")
+    g = run_gpu(inp, scale)
+    check_full(inp, g, scale)
+
+
+def test_tiny_workload_full_parity():
+    inp = make_workload_inputs("tiny")
+    say("[gpu] workload tiny (1 head, 128 tokens, causal)")
+    check_full(inp, run_gpu(inp))
+
+
+def test_empty_input():
+    say("[gpu] empty input (T = 0)")
+    inp = make_inputs((0,), 4, 2, 64, seed=1)
+    g = run_gpu(inp)
+    assert g["out"].numel() == 0
+    assert torch.all(g["dsinks"] == 0)
+
+
+def test_backward_is_deterministic():
+    inp = make_inputs((700, 333), 16, 2, 64, causal=True, window=0, seed=2)
+    say("[gpu] determinism: two backward calls on the same inputs")
+    g = run_gpu(inp, repeat_bwd=True)
+    for a, b in zip((g["dq"], g["dk"], g["dv"], g["dsinks"]), g["again"]):
+        assert torch.equal(a, b)
+
+
+# ---------------------------------------------------------------------------------------------
+# Full-size workloads: the bench's launch configuration, checked on sampled outputs.
+# ---------------------------------------------------------------------------------------------
+
+def _sample_rows(cu, rng, n):
+    T = int(cu[-1])
+    rows = set(rng.integers(0, T, size=n).tolist())
+    for b in range(len(cu) - 1):          # sequence boundaries and tails
+        a, e = int(cu[b]), int(cu[b + 1])
+        if e > a:
+            rows.update({a, e - 1})
+    return sorted(rows)[: n + 2 * (len(cu) - 1)]
+
+
+def _sample_keys(cu, causal, window, rng, n):
+    keys = set()
+    for b in range(len(cu) - 1):
+        a, e = int(cu[b]), int(cu[b + 1])
+        L = e - a
+        if L == 0:
+            continue
+        if window > 0 or L <= 4096:
+            keys.update({a, e - 1, a + int(rng.integers(0, L))})
+        else:                                   # causal long sequence: keys near the end are cheap
+            keys.update({e - 1, e - 1 - int(rng.integers(0, 256))})
+    keys = sorted(keys)
+    if len(keys) > n:
+        keys = sorted(rng.choice(keys, size=n, replace=False).tolist())
+    return keys
+
+
+@pytest.mark.parametrize("name", ["causal4k", "window4k", "varlen_causal", "varlen_window", "long32k"])
+def test_full_size_sampled(name):
+    inp = make_workload_inputs(name)
+    say(f"[gpu] full-size workload {name}: T={inp.total_tokens} B={len(inp.lengths)} window={inp.window}")
+    g = run_gpu(inp)
+    cu = inp.cu_seqlens.numpy()
+    rng = np.random.default_rng(123)
+    Hq, Hkv = inp.q.shape[1], inp.k.shape[1]
+    for name_t in ("out", "lse", "dq", "dk", "dv", "dsinks"):
+        assert torch.isfinite(g[name_t]).all(), f"{name_t} has non-finite values"
+    rows = _sample_rows(cu, rng, 24)
+    heads = sorted(rng.choice(Hq, size=6, replace=False).tolist())
+    o_ref, l_ref = oracle.forward_rows(inp.q, inp.k, inp.v, inp.sinks, cu, rows, heads, inp.causal, inp.window)
+    dq_ref = oracle.dq_rows(inp.q, inp.k, inp.v, inp.sinks, inp.dout, cu, rows, heads, inp.causal, inp.window)
+    idx_r = torch.tensor(rows)
+    idx_h = torch.tensor(heads)
+    o_gpu = g["out"].cpu()[idx_r][:, idx_h].double().numpy()
+    l_gpu = g["lse"].cpu()[idx_h][:, idx_r].double().numpy()
+    dq_gpu = g["dq"].cpu()[idx_r][:, idx_h].double().numpy()
+    for label, x, r, tol in (("out", o_gpu, o_ref, TOL["out"]), ("lse", l_gpu, l_ref, TOL["lse"]),
+                             ("dq", dq_gpu, dq_ref, TOL["dq"])):
+        err = maxabs(x, r)
+        say(f"  {label} ({len(rows)} rows x {len(heads)} heads): max-abs err {err:.3e}")
+        assert err <= tol
+    keys = _sample_keys(cu, inp.causal, inp.window, rng, 12)
+    kvh = sorted(rng.choice(Hkv, size=2, replace=False).tolist())
+    dk_ref, dv_ref = oracle.dkdv_keys(inp.q, inp.k, inp.v, inp.sinks, inp.dout, cu, keys, kvh, inp.causal,
+                                      inp.window)
+    idx_k = torch.tensor(keys)
+    idx_g = torch.tensor(kvh)
+    for label, t, r in (("dk", g["dk"], dk_ref), ("dv", g["dv"], dv_ref)):
+        x = t.cpu()[idx_k][:, idx_g].double().numpy()
+        err = maxabs(x, r)
+        say(f"  {label} ({len(keys)} keys x {len(kvh)} kv heads): max-abs err {err:.3e}")
+        assert err <= TOL[label]
+    ds_heads = heads[:2]
+    ds_ref = oracle.dsink_heads(inp.q, inp.k, inp.v, inp.sinks, inp.dout, cu, ds_heads, inp.causal, inp.window)
+    check_dsink(g["dsinks"].cpu().double().numpy()[ds_heads], ds_ref, ds_heads, label=f" (heads {ds_heads})")
