@@ -22,6 +22,8 @@ int check_shape(const attn_sink_shape* s) {
   // Element offsets are 64-bit in the kernels, but grid sizes and per-head row indices are 32-bit.
   const long long rows_q = (long long)s->total_tokens * s->num_heads_q;
   if (rows_q > (1LL << 40)) return ATTN_SINK_ERR_BAD_SHAPE;
+  // Within one sequence, element offsets (row * heads * 64) are 32-bit.
+  if ((long long)s->max_seqlen * s->num_heads_q * s->head_dim >= (1LL << 31)) return ATTN_SINK_ERR_BAD_SHAPE;
   const long long nq = ((long long)s->max_seqlen + 63) / 64;
   if (nq * s->num_heads_q * (long long)s->num_seqs >= (1LL << 31)) return ATTN_SINK_ERR_BAD_SHAPE;
   return ATTN_SINK_OK;
@@ -83,7 +85,7 @@ int bwd_impl(const void* q, const void* k, const void* v, const float* sinks, co
   a.Hkv = shape->num_heads_kv;
   a.G = a.Hq / a.Hkv;
   a.hpw = heads_per_group_split(a.G);
-  a.kv_waves = heads_per_group_split(a.G);
+  a.kv_waves = a.G % 2 == 0 ? 4 : 2;  // two key halves x (two head streams when G is even)
   a.n_qblocks = (shape->max_seqlen + kDqRowsPerWave - 1) / kDqRowsPerWave;
   a.n_kblocks = (shape->max_seqlen + kKvKeysPerBlock - 1) / kKvKeysPerBlock;
   a.causal = causal ? 1 : 0;

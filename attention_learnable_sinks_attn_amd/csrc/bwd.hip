@@ -12,15 +12,19 @@
 //
 // Passes (all on the caller's stream, no atomics, bitwise reproducible):
 //  1. prep:  D_i = rowsum(dO * O) for every (row, head); clear the dSink partial sums.
-//  2. dkdv:  column-parallel. A workgroup owns 64 keys of one KV head; its waves split the
-//            query heads of the group and stream 32-row query tiles, keeping dK^T and dV^T of
-//            their keys in registers; the waves' partial sums are added in LDS at the end.
-//  3. dq:    row-parallel. A workgroup owns 64 query rows of `hpw` heads of one group (one head
-//            per wave) and streams 64-key tiles of K, V and K^T through LDS. Besides dQ it
-//            accumulates D~_i = sum_j P_ij dP_ij from the fp32 P and dP it already holds and
-//            writes sum_i P_{i,h} D~_i for its rows. D~ equals D mathematically but does not
-//            carry the bf16 rounding of the forward's P.V product, which matters because the
-//            terms of dL/dS_h cancel heavily.
+//  2. dkdv:  column-parallel. A workgroup owns 64 keys of one KV head: two key halves of 32
+//            times one or two "head streams" (the group's query heads split between streams).
+//            For each step (head, 64 query rows) the Q, dO, LSE and D rows are staged once per
+//            stream in LDS, double-buffered with the next step's global loads issued ahead;
+//            the transposed Q^T / dO^T operands come from transposing LDS loads. dK^T and dV^T of each wave's 32 keys stay in
+//            registers; the two streams' partial sums are added in LDS at the end.
+//  3. dq:    row-parallel. A workgroup owns 32 query rows of `hpw` heads of one group (one head
+//            per wave) and streams double-buffered 64-key tiles of K and V through LDS (K^T
+//            operands come from transposing LDS loads of the K tile).
+//            Besides dQ it accumulates D~_i = sum_j P_ij dP_ij from the fp32 P and dP it already
+//            holds and writes sum_i P_{i,h} D~_i for its rows. D~ equals D mathematically but
+//            does not carry the bf16 rounding of the forward's P.V product, which matters
+//            because the terms of dL/dS_h cancel heavily.
 //  4. dsink: dL/dS_h = -(sum of the partials of head h), summed in a fixed order.
 #include "kernels.h"
 
@@ -29,6 +33,7 @@ namespace attn_sink {
 namespace {
 
 constexpr int kLdsStride = 72;  // bf16 per staged 64-element row (16-byte aligned, 8 pad)
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 // ------------------------------------------------------------------------------------------
 // 1. D_i = sum_d dO[i,h,d] * O[i,h,d]; 16 lanes per (row, head), 4 elements each.
@@ -64,230 +69,266 @@ __global__ __launch_bounds__(256) void attn_sink_bwd_prep_kernel(BwdArgs a) {
 // ------------------------------------------------------------------------------------------
 // 2. dK, dV: column-parallel over 64-key blocks.
 // ------------------------------------------------------------------------------------------
-constexpr int kKvQTile = 32;                    // query rows per step
-constexpr int kKvStageStride = kKvQTile + 8;    // transposed staging row: 32 queries + pad
-constexpr int kKvStageElems = kHeadDim * kKvStageStride;
-constexpr int kKvRedStride = kHeadDim + 4;      // fp32 reduction row
+constexpr int kKvSub = 32;                             // query rows per product block
+constexpr int kKvStageRows = 64;                       // query rows staged per step (2 blocks)
+constexpr int kKvNatElems = kKvStageRows * kLdsStride; // [query][d] tile
+// One stream's stage: Q and dO rows (natural layout), then LSE (log2 units) and D of those rows.
+constexpr int kKvStageBytes = 2 * kKvNatElems * 2 + 2 * kKvStageRows * 4;
+constexpr int kKvRedStride = kHeadDim + 4;             // fp32 reduction row
 
-__global__ __launch_bounds__(256, 1) void attn_sink_bwd_dkdv_kernel(BwdArgs a) {
-  // Per wave: Q^T and dO^T of the current query tile, [d][query]. Reused afterwards for the
-  // cross-wave reduction of dK / dV ([key][d] fp32).
-  __shared__ __attribute__((aligned(16))) unsigned char smem[4 * 2 * kKvStageElems * 2];
-  static_assert(sizeof(smem) >= kKvKeysPerBlock * kKvRedStride * 4, "reduction buffer fits");
+template <int NS>  // head streams: 1 or 2 (waves = 2 * NS)
+__global__ __launch_bounds__(128 * NS, 2) void attn_sink_bwd_dkdv_kernel(BwdArgs a) {
+  constexpr int NW = 2 * NS;
+  constexpr int NT = 64 * NW;
+  constexpr int kRR = kKvStageRows * 8 / NT;  // 16-byte pieces per thread and staged tile
+  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * NS * kKvStageBytes];
+  static_assert(sizeof(smem) >= 4 * 32 * kKvRedStride * 4, "reduction buffer fits");
 
-  const int nw = a.kv_waves;
+  // Block order: key blocks 0, 1, ... for the first half of the grid and n-1, n-2, ... for the
+  // second, so that blocks i and i + half (likely co-resident on a CU) carry complementary
+  // amounts of causal work.
   const int bid = blockIdx.x;
   const int g = bid % a.Hkv;
   const int rest = bid / a.Hkv;
   const int b = rest % a.B;
-  const int kb = rest / a.B;  // ascending: under a causal mask the first key blocks carry the most rows
+  const int j = rest / a.B;
+  const int half = (a.n_kblocks + 1) / 2;
+  const int kb = j < half ? j : a.n_kblocks - 1 - (j - half);
   const int cs = a.cu[b];
   const int len = a.cu[b + 1] - cs;
-  const int k0 = kb * kKvKeysPerBlock;
-  if (k0 >= len) return;
+  const int kblk = kb * kKvKeysPerBlock;
+  if (kblk >= len) return;
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = wave_id();
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int grp = lane >> 5;
+  const int kh = wave & 1;        // key half
+  const int st = wave >> 1;       // head stream
+  const int k0 = kblk + 32 * kh;  // this wave's 32 keys
+  const int heads_per_stream = a.G / NS;
 
-  __bf16* qt_lds = reinterpret_cast<__bf16*>(smem) + wave * 2 * kKvStageElems;
-  __bf16* dot_lds = qt_lds + kKvStageElems;
-
-  // K^T and V^T as B operands (k = d, n = key): lane holds key k0 + 32nb + l32, d = 16c + 8grp.
-  bf16x8 kf[2][4], vf[2][4];
+  // K^T and V^T as B operands (k = d, n = key): lane holds key k0 + l32, d = 16c + 8grp + (0..7).
+  bf16x8 kf[4], vf[4];
   const size_t kv_tok = (size_t)a.Hkv * kHeadDim;
-#pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    const int key = k0 + 32 * nb + l32;
+  {
+    const int key = min(k0 + l32, len - 1);  // keys past the end are masked
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const size_t off = (size_t)(cs + key) * kv_tok + (size_t)g * kHeadDim + 16 * c + 8 * grp;
-      kf[nb][c] = key < len ? load_bf16x8(a.k + off) : zero_bf16x8();
-      vf[nb][c] = key < len ? load_bf16x8(a.v + off) : zero_bf16x8();
+      kf[c] = load_bf16x8(a.k + off);
+      vf[c] = load_bf16x8(a.v + off);
     }
   }
+  f32x16 dk[2], dv[2];  // [d block], C layout of dK^T / dV^T (rows d, columns this wave's keys)
+  dk[0] = dk[1] = dv[0] = dv[1] = zero_f32x16();
 
-  f32x16 dk[2][2], dv[2][2];  // [d block][key block], C layout of dK^T / dV^T
-#pragma unroll
-  for (int x = 0; x < 2; ++x) {
-#pragma unroll
-    for (int y = 0; y < 2; ++y) {
-      dk[x][y] = zero_f32x16();
-      dv[x][y] = zero_f32x16();
-    }
-  }
-
-  // Query rows that can see any key of [k0, k0+64).
-  const int kmax = min(len, k0 + kKvKeysPerBlock) - 1;
-  const int i_begin = a.causal ? k0 : 0;
+  // Query rows that can see a key of [kblk, kblk + 64), in 64-row stages.
+  const int kmax = min(len, kblk + kKvKeysPerBlock) - 1;
+  const int i_begin = a.causal ? kblk : 0;
   const int i_end = a.window > 0 ? min(len, kmax + a.window) : len;  // exclusive
-  const int t_begin = i_begin / kKvQTile;
-  const int t_end = (i_end + kKvQTile - 1) / kKvQTile;
+  const int t_begin = i_begin / kKvStageRows;
+  const int n_t = (i_end + kKvStageRows - 1) / kKvStageRows - t_begin;
+  const int n_steps = heads_per_stream * n_t;
 
-  for (int hh = wave; hh < a.G; hh += nw) {
-    const int h = g * a.G + hh;
-    for (int t = t_begin; t < t_end; ++t) {
-      const int i0 = t * kKvQTile;
-      // Q and dO rows as A operands (m = query, k = d); row r holds query i0 + swap23(r).
-      const int qrow = i0 + swap23(l32);
-      bf16x8 qa[4], da[4];
+  // Staging: per thread, row (tid >> 3) + (NT / 8) * rr, chunk (tid & 7) of each of the 2 * NS
+  // tiles (stream t >> 1, Q or dO by t & 1), plus one LSE or D value. Rows past the sequence end
+  // are clamped onto its last row (finite data; those rows are masked out).
+  bf16x8 pre[2 * NS][kRR];
+  float pre_ld = 0.0f;
+  auto stage_ptr = [&](int buf, int s) { return smem + (size_t)(buf * NS + s) * kKvStageBytes; };
+  const int prow = tid >> 3, pc8 = tid & 7;
+  auto prefetch = [&](int hj, int i0) {
+#pragma unroll
+    for (int t = 0; t < 2 * NS; ++t) {
+      const int h = g * a.G + (t >> 1) + NS * hj;
+      const __bf16* base = ((t & 1) ? a.dout : a.q) + ((size_t)cs * a.Hq + h) * kHeadDim;
+#pragma unroll
+      for (int rr = 0; rr < kRR; ++rr) {
+        const int qi = min(i0 + prow + (NT / 8) * rr, len - 1);
+        pre[t][rr] = load_bf16x8(base + (unsigned)(qi * a.Hq * kHeadDim + 8 * pc8));
+      }
+    }
+    if (tid < NS * 2 * kKvStageRows) {
+      const int s = tid / (2 * kKvStageRows);
+      const int which = (tid / kKvStageRows) & 1;
+      const int h = g * a.G + s + NS * hj;
+      const int qi = min(i0 + (tid & (kKvStageRows - 1)), len - 1);
+      const float v = (which ? a.dws : a.lse)[(size_t)h * a.T + cs + qi];
+      pre_ld = which ? v : v * kLog2e;
+    }
+  };
+  auto commit = [&](int buf) {
+#pragma unroll
+    for (int t = 0; t < 2 * NS; ++t) {
+      __bf16* nat = reinterpret_cast<__bf16*>(stage_ptr(buf, t >> 1)) + (t & 1) * kKvNatElems;
+#pragma unroll
+      for (int rr = 0; rr < kRR; ++rr) {
+        *reinterpret_cast<bf16x8*>(&nat[(prow + (NT / 8) * rr) * kLdsStride + 8 * pc8]) = pre[t][rr];
+      }
+    }
+    if (tid < NS * 2 * kKvStageRows) {
+      float* f = reinterpret_cast<float*>(stage_ptr(buf, tid / (2 * kKvStageRows)) + 2 * kKvNatElems * 2);
+      f[tid & (2 * kKvStageRows - 1)] = pre_ld;
+    }
+  };
+
+  int hj = 0, ti = 0;  // current step = (head index within the stream, stage index)
+  if (n_steps > 0) {
+    prefetch(0, t_begin * kKvStageRows);
+    commit(0);
+  }
+  __syncthreads();
+
+  for (int step = 0; step < n_steps; ++step) {
+    const int cur = step & 1;
+    const bool has_next = step + 1 < n_steps;
+    const int hj_n = ti + 1 < n_t ? hj : hj + 1;
+    const int ti_n = ti + 1 < n_t ? ti + 1 : 0;
+    if (has_next) prefetch(hj_n, (t_begin + ti_n) * kKvStageRows);
+
+    const unsigned char* sp = stage_ptr(cur, st);
+    const __bf16* qn = reinterpret_cast<const __bf16*>(sp);
+    const __bf16* dn = qn + kKvNatElems;
+    const float* lsep = reinterpret_cast<const float*>(sp + 2 * kKvNatElems * 2);
+    const float* ddp = lsep + kKvStageRows;
+
+#pragma unroll
+    for (int sub = 0; sub < kKvStageRows / kKvSub; ++sub) {
+      const int i0 = (t_begin + ti) * kKvStageRows + kKvSub * sub;
+      // Skip blocks in which no (query, key) pair of this wave is visible (wave-uniform).
+      const bool live = (!a.causal || k0 <= i0 + kKvSub - 1) && (a.window <= 0 || i0 <= k0 + 30 + a.window) &&
+                        k0 < len && i0 < len;
+      if (!live) continue;
+      const __bf16* qs = qn + kKvSub * sub * kLdsStride;
+      const __bf16* ds = dn + kKvSub * sub * kLdsStride;
+
+      // S = Q K^T and dP = dO V^T: A rows hold query swap23(r); C: lane = key, registers = queries.
+      f32x16 s = zero_f32x16(), dp = zero_f32x16();
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        const size_t off = ((size_t)(cs + qrow) * a.Hq + h) * kHeadDim + 16 * c + 8 * grp;
-        qa[c] = qrow < len ? load_bf16x8(a.q + off) : zero_bf16x8();
-        da[c] = qrow < len ? load_bf16x8(a.dout + off) : zero_bf16x8();
+        const int off = swap23(l32) * kLdsStride + 16 * c + 8 * grp;
+        s = mfma_32x32x16(load_bf16x8(&qs[off]), kf[c], s);
+        dp = mfma_32x32x16(load_bf16x8(&ds[off]), vf[c], dp);
       }
-      // LSE (log2 units) and D of the 16 query rows this lane's C registers hold.
-      float lse2[16], dd[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int qi = i0 + c_row(i, grp);
-        const bool ok = qi < len;
-        lse2[i] = ok ? a.lse[(size_t)h * a.T + cs + qi] * kLog2e : 0.0f;
-        dd[i] = ok ? a.dws[(size_t)h * a.T + cs + qi] : 0.0f;
-      }
-      // Stage Q^T and dO^T ([d][query], query slot = local row index) for the second products.
-      const int lrow = swap23(l32);
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          qt_lds[(16 * c + 8 * grp + e) * kKvStageStride + lrow] = qa[c][e];
-          dot_lds[(16 * c + 8 * grp + e) * kKvStageStride + lrow] = da[c][e];
-        }
-      }
+      // LSE / D of the 16 query rows held in this lane's registers: rows 16(i/8) + 8grp + (i%8).
+      const f32x4* l4 = reinterpret_cast<const f32x4*>(lsep + kKvSub * sub);
+      const f32x4* d4 = reinterpret_cast<const f32x4*>(ddp + kKvSub * sub);
+      const f32x4 la = l4[2 * grp], lb = l4[2 * grp + 1], lc = l4[4 + 2 * grp], ld = l4[4 + 2 * grp + 1];
+      const f32x4 da_ = d4[2 * grp], db_ = d4[2 * grp + 1], dc = d4[4 + 2 * grp], dd_ = d4[4 + 2 * grp + 1];
+      const float lse2[16] = {la[0], la[1], la[2], la[3], lb[0], lb[1], lb[2], lb[3],
+                              lc[0], lc[1], lc[2], lc[3], ld[0], ld[1], ld[2], ld[3]};
+      const float dd[16] = {da_[0], da_[1], da_[2], da_[3], db_[0], db_[1], db_[2], db_[3],
+                            dc[0], dc[1], dc[2], dc[3], dd_[0], dd_[1], dd_[2], dd_[3]};
 
-      // S = Q K^T and dP = dO V^T, C layout: lane = key column, registers = query rows.
-      f32x16 s[2], dp[2];
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        s[nb] = zero_f32x16();
-        dp[nb] = zero_f32x16();
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          s[nb] = mfma_32x32x16(qa[c], kf[nb][c], s[nb]);
-          dp[nb] = mfma_32x32x16(da[c], vf[nb][c], dp[nb]);
-        }
-      }
-
-      const bool need_mask = (i0 + kKvQTile > len) || (k0 + kKvKeysPerBlock > len) ||
-                             (a.causal && k0 + kKvKeysPerBlock - 1 > i0) ||
-                             (a.window > 0 && k0 <= i0 + kKvQTile - 1 - a.window);
-      bf16x8 pb[2][2], dsb[2][2];  // [key block][query chunk]
-      float pmax = 0.0f;
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        const int kj = k0 + 32 * nb + l32;
+      const bool need_mask = (i0 + kKvSub > len) || (k0 + 32 > len) || (a.causal && k0 + 31 > i0) ||
+                             (a.window > 0 && k0 <= i0 + kKvSub - 1 - a.window);
+      if (need_mask) {  // wave-uniform: only diagonal, window-edge and ragged blocks
+        const int kj = k0 + l32;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          float p = fast_exp2(__builtin_fmaf(s[nb][i], a.scale_log2, -lse2[i]));
-          if (need_mask) {
-            const int qi = i0 + c_row(i, grp);
-            if (!(qi < len && visible(qi, kj, len, a.causal, a.window))) p = 0.0f;
-          }
-          pmax = fmaxf(pmax, p);
-          s[nb][i] = p;
-          dp[nb][i] = p * (dp[nb][i] - dd[i]);
+          const int qi = i0 + c_row(i, grp);
+          if (!(qi < len && visible(qi, kj, len, a.causal, a.window))) s[i] = kNegInf;
         }
-        pb[nb][0] = pack8(s[nb], 0);
-        pb[nb][1] = pack8(s[nb], 1);
-        dsb[nb][0] = pack8(dp[nb], 0);
-        dsb[nb][1] = pack8(dp[nb], 1);
       }
+      float pmax = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float p = fast_exp2(__builtin_fmaf(s[i], a.scale_log2, -lse2[i]));
+        pmax = fmaxf(pmax, p);
+        s[i] = p;
+        dp[i] = p * (dp[i] - dd[i]);
+      }
+      const bf16x8 pb0 = pack8(s, 0), pb1 = pack8(s, 1);
+      const bf16x8 ds0 = pack8(dp, 0), ds1 = pack8(dp, 1);
       // Large probabilities: add the products of the bf16 rounding residuals of P and dS.
       const bool split = wave_any(pmax > kSplitThreshold);
 
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      // dV^T += dO^T P and dK^T += Q^T dS over the block's 32 queries; the transposed operands
+      // come straight from the natural tiles through transposing LDS loads.
+#pragma unroll
+      for (int db = 0; db < 2; ++db) {
+        const bf16x8 doa0 = load_tr8(ds, kLdsStride, 0, 32 * db), doa1 = load_tr8(ds, kLdsStride, 16, 32 * db);
+        const bf16x8 qta0 = load_tr8(qs, kLdsStride, 0, 32 * db), qta1 = load_tr8(qs, kLdsStride, 16, 32 * db);
+        dv[db] = mfma_32x32x16(doa0, pb0, dv[db]);
+        dv[db] = mfma_32x32x16(doa1, pb1, dv[db]);
+        dk[db] = mfma_32x32x16(qta0, ds0, dk[db]);
+        dk[db] = mfma_32x32x16(qta1, ds1, dk[db]);
+        if (split) {
+          dv[db] = mfma_32x32x16(doa0, residual8(s, 0, pb0), dv[db]);
+          dv[db] = mfma_32x32x16(doa1, residual8(s, 1, pb1), dv[db]);
+          dk[db] = mfma_32x32x16(qta0, residual8(dp, 0, ds0), dk[db]);
+          dk[db] = mfma_32x32x16(qta1, residual8(dp, 1, ds1), dk[db]);
+        }
+      }
+    }
 
-      // dV^T += dO^T P and dK^T += Q^T dS (contract over the tile's 32 queries).
+    if (has_next) commit(cur ^ 1);
+    hj = hj_n;
+    ti = ti_n;
+    __syncthreads();
+  }
+
+  // Add the second stream's partial sums (LDS, [key][d] fp32 per key half), then store rows.
+  float* red = reinterpret_cast<float*>(smem) + kh * 32 * kKvRedStride;
+  if (NS == 2 && st == 1) {
+#pragma unroll
+    for (int db = 0; db < 2; ++db) {
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int d = 32 * db + 8 * r4 + 4 * grp;
+        *reinterpret_cast<f32x4*>(&red[l32 * kKvRedStride + d]) =
+            (f32x4){dk[db][4 * r4], dk[db][4 * r4 + 1], dk[db][4 * r4 + 2], dk[db][4 * r4 + 3]};
+        *reinterpret_cast<f32x4*>(&red[(64 + l32) * kKvRedStride + d]) =
+            (f32x4){dv[db][4 * r4], dv[db][4 * r4 + 1], dv[db][4 * r4 + 2], dv[db][4 * r4 + 3]};
+      }
+    }
+  }
+  if (NS == 2) __syncthreads();
+  if (st == 0) {
+    const int key = k0 + l32;
+    if (key < len) {
+      float* dkrow = a.dk + ((size_t)(cs + key) * a.Hkv + g) * kHeadDim;
+      float* dvrow = a.dv + ((size_t)(cs + key) * a.Hkv + g) * kHeadDim;
 #pragma unroll
       for (int db = 0; db < 2; ++db) {
 #pragma unroll
-        for (int cc = 0; cc < 2; ++cc) {
-          const bf16x8 doa = load_bf16x8(&dot_lds[(32 * db + l32) * kKvStageStride + 16 * cc + 8 * grp]);
-          const bf16x8 qta = load_bf16x8(&qt_lds[(32 * db + l32) * kKvStageStride + 16 * cc + 8 * grp]);
-#pragma unroll
-          for (int nb = 0; nb < 2; ++nb) {
-            dv[db][nb] = mfma_32x32x16(doa, pb[nb][cc], dv[db][nb]);
-            dk[db][nb] = mfma_32x32x16(qta, dsb[nb][cc], dk[db][nb]);
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int d = 32 * db + 8 * r4 + 4 * grp;
+          f32x4 kv = {dk[db][4 * r4], dk[db][4 * r4 + 1], dk[db][4 * r4 + 2], dk[db][4 * r4 + 3]};
+          f32x4 vv = {dv[db][4 * r4], dv[db][4 * r4 + 1], dv[db][4 * r4 + 2], dv[db][4 * r4 + 3]};
+          if (NS == 2) {
+            kv += *reinterpret_cast<const f32x4*>(&red[l32 * kKvRedStride + d]);
+            vv += *reinterpret_cast<const f32x4*>(&red[(64 + l32) * kKvRedStride + d]);
           }
-          if (split) {
-#pragma unroll
-            for (int nb = 0; nb < 2; ++nb) {
-              dv[db][nb] = mfma_32x32x16(doa, residual8(s[nb], cc, pb[nb][cc]), dv[db][nb]);
-              dk[db][nb] = mfma_32x32x16(qta, residual8(dp[nb], cc, dsb[nb][cc]), dk[db][nb]);
-            }
-          }
+          *reinterpret_cast<f32x4*>(dkrow + d) = kv * a.scale;
+          *reinterpret_cast<f32x4*>(dvrow + d) = vv;
         }
-      }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    }
-  }
-
-  // Sum the waves' partial dK^T / dV^T in LDS, then store [key][d] rows (dK scaled).
-  float* red = reinterpret_cast<float*>(smem);
-#pragma unroll
-  for (int which = 0; which < 2; ++which) {
-    for (int w = 0; w < nw; ++w) {
-      __syncthreads();
-      if (wave == w) {
-#pragma unroll
-        for (int db = 0; db < 2; ++db) {
-#pragma unroll
-          for (int nb = 0; nb < 2; ++nb) {
-            const f32x16& acc = which == 0 ? dk[db][nb] : dv[db][nb];
-            const int key = 32 * nb + l32;
-#pragma unroll
-            for (int r4 = 0; r4 < 4; ++r4) {
-              f32x4* dst = reinterpret_cast<f32x4*>(&red[key * kKvRedStride + 32 * db + 8 * r4 + 4 * grp]);
-              f32x4 val = {acc[4 * r4], acc[4 * r4 + 1], acc[4 * r4 + 2], acc[4 * r4 + 3]};
-              if (w == 0) {
-                *dst = val;
-              } else {
-                *dst = *dst + val;
-              }
-            }
-          }
-        }
-      }
-    }
-    __syncthreads();
-    float* dst = which == 0 ? a.dk : a.dv;
-    const float mul = which == 0 ? a.scale : 1.0f;
-    for (int u = tid; u < kKvKeysPerBlock * (kHeadDim / 4); u += blockDim.x) {
-      const int key = u / (kHeadDim / 4);
-      const int c4 = u % (kHeadDim / 4);
-      if (k0 + key < len) {
-        f32x4 val = *reinterpret_cast<const f32x4*>(&red[key * kKvRedStride + 4 * c4]);
-        *reinterpret_cast<f32x4*>(dst + ((size_t)(cs + k0 + key) * a.Hkv + g) * kHeadDim + 4 * c4) = val * mul;
       }
     }
   }
 }
 
 // ------------------------------------------------------------------------------------------
-// 3. dQ and the dSink partials: row-parallel over 64-row query blocks.
+// 3. dQ and the dSink partials: row-parallel over 32-row query blocks.
 // ------------------------------------------------------------------------------------------
 constexpr int kDqTileKeys = 64;
+constexpr int kDqTileElems = kDqTileKeys * kLdsStride;
 
-template <int NB>
-__global__ __launch_bounds__(256) void attn_sink_bwd_dq_kernel(BwdArgs a) {
-  __shared__ __attribute__((aligned(16))) __bf16 k_lds[kDqTileKeys * kLdsStride];
-  __shared__ __attribute__((aligned(16))) __bf16 v_lds[kDqTileKeys * kLdsStride];
-  __shared__ __attribute__((aligned(16))) __bf16 kt_lds[kHeadDim * kLdsStride];
+template <int HPW>
+__global__ __launch_bounds__(64 * HPW, 2) void attn_sink_bwd_dq_kernel(BwdArgs a) {
+  constexpr int NT = 64 * HPW;
+  constexpr int kRows = kDqRowsPerWave;
+  constexpr int KU = kDqTileKeys * 8 / NT;  // 16-byte K (and V) pieces per thread and tile
+  __shared__ __attribute__((aligned(16))) __bf16 k_lds[2 * kDqTileElems];
+  __shared__ __attribute__((aligned(16))) __bf16 v_lds[2 * kDqTileElems];
 
-  constexpr int kRows = 32 * NB;
-  const int n_hs = a.Hq / a.hpw;
+  const int n_hs = a.Hq / HPW;
   const int bid = blockIdx.x;
   const int inner = bid % n_hs;
   const int rest = bid / n_hs;
-  const int spg = a.G / a.hpw;
+  const int spg = a.G / HPW;
   const int hs = (inner % a.Hkv) * spg + inner / a.Hkv;
   const int b = rest % a.B;
   const int qb = a.n_qblocks - 1 - rest / a.B;
@@ -297,38 +338,29 @@ __global__ __launch_bounds__(256) void attn_sink_bwd_dq_kernel(BwdArgs a) {
   if (q0 >= len) return;
 
   const int tid = threadIdx.x;
-  const int nthreads = blockDim.x;
-  const int wave = tid >> 6;
+  const int wave = wave_id();
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int grp = lane >> 5;
-  const int h = hs * a.hpw + wave;
+  const int h = hs * HPW + wave;
   const int g = h / a.G;
 
-  // Q^T and dO^T as B operands: lane holds query q0 + 32nb + l32, d = 16c + 8grp + (0..7).
-  bf16x8 qf[NB][4], df[NB][4];
-  float lse2[NB], dd[NB], dsum[NB];
+  // Q^T and dO^T as B operands: lane holds query q0 + l32, d = 16c + 8grp + (0..7).
+  const int qi = q0 + l32;
+  const bool qok = qi < len;
+  const int qc = min(qi, len - 1);  // rows past the end compute on the last row and are not stored
+  bf16x8 qf[4], df[4];
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    const int qi = q0 + 32 * nb + l32;
-    const bool ok = qi < len;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const size_t off = ((size_t)(cs + qi) * a.Hq + h) * kHeadDim + 16 * c + 8 * grp;
-      qf[nb][c] = ok ? load_bf16x8(a.q + off) : zero_bf16x8();
-      df[nb][c] = ok ? load_bf16x8(a.dout + off) : zero_bf16x8();
-    }
-    lse2[nb] = ok ? a.lse[(size_t)h * a.T + cs + qi] * kLog2e : 0.0f;
-    dd[nb] = ok ? a.dws[(size_t)h * a.T + cs + qi] : 0.0f;
-    dsum[nb] = 0.0f;
+  for (int c = 0; c < 4; ++c) {
+    const size_t off = ((size_t)(cs + qc) * a.Hq + h) * kHeadDim + 16 * c + 8 * grp;
+    qf[c] = load_bf16x8(a.q + off);
+    df[c] = load_bf16x8(a.dout + off);
   }
-
-  f32x16 acc[2][NB];  // dQ^T, [d block][query block]
-#pragma unroll
-  for (int db = 0; db < 2; ++db) {
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) acc[db][nb] = zero_f32x16();
-  }
+  const float lse2 = a.lse[(size_t)h * a.T + cs + qc] * kLog2e;
+  const float dd = a.dws[(size_t)h * a.T + cs + qc];
+  float dsum = 0.0f;
+  f32x16 acc[2];  // dQ^T, [d block]
+  acc[0] = acc[1] = zero_f32x16();
 
   const int kend = a.causal ? min(len, q0 + kRows) : len;
   const int kbeg = a.window > 0 ? max(0, q0 - a.window + 1) : 0;
@@ -338,84 +370,90 @@ __global__ __launch_bounds__(256) void attn_sink_bwd_dq_kernel(BwdArgs a) {
   const __bf16* kbase = a.k + (size_t)cs * tok_stride + (size_t)g * kHeadDim;
   const __bf16* vbase = a.v + (size_t)cs * tok_stride + (size_t)g * kHeadDim;
 
-  for (int kt = kt_begin; kt < kt_end; ++kt) {
-    const int k0 = kt * kDqTileKeys;
-    __syncthreads();
-    for (int u = tid; u < kDqTileKeys * 8; u += nthreads) {
-      const int r = u >> 3, c8 = u & 7;
-      const int key = k0 + r;
-      const bool ok = key < len;
-      *reinterpret_cast<bf16x8*>(&k_lds[r * kLdsStride + 8 * c8]) =
-          ok ? load_bf16x8(kbase + (size_t)key * tok_stride + 8 * c8) : zero_bf16x8();
-      *reinterpret_cast<bf16x8*>(&v_lds[r * kLdsStride + 8 * c8]) =
-          ok ? load_bf16x8(vbase + (size_t)key * tok_stride + 8 * c8) : zero_bf16x8();
-    }
-    for (int u = tid; u < (kDqTileKeys / 2) * 8; u += nthreads) {
-      const int c8 = u & 7, p = u >> 3;
-      const int key = k0 + 2 * p;
-      bf16x8 k0v = key < len ? load_bf16x8(kbase + (size_t)key * tok_stride + 8 * c8) : zero_bf16x8();
-      bf16x8 k1v = key + 1 < len ? load_bf16x8(kbase + (size_t)(key + 1) * tok_stride + 8 * c8) : zero_bf16x8();
+  // K and V tiles in natural [key][d] layout; K^T operands come from transposing LDS loads.
+  // Keys past the sequence end are clamped onto its last key (finite data; they are masked).
+  bf16x8 kpre[KU], vpre[KU];
+  auto prefetch = [&](int kt) {
+    const int kk = kt * kDqTileKeys;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-        bf16x2 pr = {k0v[j], k1v[j]};
-        *reinterpret_cast<bf16x2*>(&kt_lds[(8 * c8 + j) * kLdsStride + 2 * p]) = pr;
-      }
+    for (int u = 0; u < KU; ++u) {
+      const int idx = tid + u * NT;
+      const unsigned off = (unsigned)(min(kk + (idx >> 3), len - 1) * (int)tok_stride + 8 * (idx & 7));
+      kpre[u] = load_bf16x8(kbase + off);
+      vpre[u] = load_bf16x8(vbase + off);
     }
-    __syncthreads();
+  };
+  auto commit = [&](int buf) {
+    __bf16* kl = k_lds + buf * kDqTileElems;
+    __bf16* vl = v_lds + buf * kDqTileElems;
+#pragma unroll
+    for (int u = 0; u < KU; ++u) {
+      const int idx = tid + u * NT;
+      const int off = (idx >> 3) * kLdsStride + 8 * (idx & 7);
+      *reinterpret_cast<bf16x8*>(&kl[off]) = kpre[u];
+      *reinterpret_cast<bf16x8*>(&vl[off]) = vpre[u];
+    }
+  };
+
+  if (kt_begin < kt_end) {
+    prefetch(kt_begin);
+    commit(0);
+  }
+  __syncthreads();
+
+  for (int kt = kt_begin; kt < kt_end; ++kt) {
+    const int cur = (kt - kt_begin) & 1;
+    const bool has_next = kt + 1 < kt_end;
+    if (has_next) prefetch(kt + 1);
+    const __bf16* kl = k_lds + cur * kDqTileElems;
+    const __bf16* vl = v_lds + cur * kDqTileElems;
+    const int k0 = kt * kDqTileKeys;
 
     // S^T = K Q^T and dP^T = V dO^T (rows = keys, loaded with the swap23 permutation).
-    f32x16 s[2][NB], dp[2][NB];
+    f32x16 s[2], dp[2];
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        s[mb][nb] = zero_f32x16();
-        dp[mb][nb] = zero_f32x16();
-      }
+      s[mb] = zero_f32x16();
+      dp[mb] = zero_f32x16();
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const int row = (32 * mb + swap23(l32)) * kLdsStride + 16 * c + 8 * grp;
-        const bf16x8 ka = load_bf16x8(&k_lds[row]);
-        const bf16x8 va = load_bf16x8(&v_lds[row]);
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-          s[mb][nb] = mfma_32x32x16(ka, qf[nb][c], s[mb][nb]);
-          dp[mb][nb] = mfma_32x32x16(va, df[nb][c], dp[mb][nb]);
-        }
+        s[mb] = mfma_32x32x16(load_bf16x8(&kl[row]), qf[c], s[mb]);
+        dp[mb] = mfma_32x32x16(load_bf16x8(&vl[row]), df[c], dp[mb]);
       }
     }
 
     const bool need_mask = (k0 + kDqTileKeys > len) || (a.causal && k0 + kDqTileKeys - 1 > q0) ||
                            (a.window > 0 && k0 <= q0 + kRows - 1 - a.window);
-    bf16x8 dsb[2][2][NB];
-    float pmax = 0.0f;
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      const int qi = q0 + 32 * nb + l32;
-      float part = 0.0f;
+    if (need_mask) {  // uniform: only diagonal, window-edge and ragged tiles
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          float p = fast_exp2(__builtin_fmaf(s[mb][nb][i], a.scale_log2, -lse2[nb]));
-          if (need_mask) {
-            const int kj = k0 + 32 * mb + c_row(i, grp);
-            if (!visible(qi, kj, len, a.causal, a.window)) p = 0.0f;
-          }
-          pmax = fmaxf(pmax, p);
-          const float pdp = p * dp[mb][nb][i];
-          part += pdp;
-          dp[mb][nb][i] = pdp - p * dd[nb];
+          const int kj = k0 + 32 * mb + c_row(i, grp);
+          if (!visible(qi, kj, len, a.causal, a.window)) s[mb][i] = kNegInf;
         }
-        dsb[mb][0][nb] = pack8(dp[mb][nb], 0);
-        dsb[mb][1][nb] = pack8(dp[mb][nb], 1);
       }
-      dsum[nb] += part;
     }
-
+    bf16x8 dsb[2][2];
+    float pmax = 0.0f, part = 0.0f;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float p = fast_exp2(__builtin_fmaf(s[mb][i], a.scale_log2, -lse2));
+        pmax = fmaxf(pmax, p);
+        const float pdp = p * dp[mb][i];
+        part += pdp;
+        dp[mb][i] = __builtin_fmaf(-p, dd, pdp);
+      }
+      dsb[mb][0] = pack8(dp[mb], 0);
+      dsb[mb][1] = pack8(dp[mb], 1);
+    }
+    dsum += part;
     // Large probabilities: also multiply the bf16 rounding residual of dS.
     const bool split = wave_any(pmax > kSplitThreshold);
+
     // dQ^T += K^T dS^T (A = K^T from LDS, contracting over the tile's keys).
 #pragma unroll
     for (int db = 0; db < 2; ++db) {
@@ -423,40 +461,31 @@ __global__ __launch_bounds__(256) void attn_sink_bwd_dq_kernel(BwdArgs a) {
       for (int mb = 0; mb < 2; ++mb) {
 #pragma unroll
         for (int cc = 0; cc < 2; ++cc) {
-          const bf16x8 kta = load_bf16x8(&kt_lds[(32 * db + l32) * kLdsStride + 32 * mb + 16 * cc + 8 * grp]);
-#pragma unroll
-          for (int nb = 0; nb < NB; ++nb) acc[db][nb] = mfma_32x32x16(kta, dsb[mb][cc][nb], acc[db][nb]);
-          if (split) {
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb) {
-              acc[db][nb] = mfma_32x32x16(kta, residual8(dp[mb][nb], cc, dsb[mb][cc][nb]), acc[db][nb]);
-            }
-          }
+          const bf16x8 kta = load_tr8(kl, kLdsStride, 32 * mb + 16 * cc, 32 * db);  // K^T rows d, keys
+          acc[db] = mfma_32x32x16(kta, dsb[mb][cc], acc[db]);
+          if (split) acc[db] = mfma_32x32x16(kta, residual8(dp[mb], cc, dsb[mb][cc]), acc[db]);
         }
       }
     }
+
+    if (has_next) commit(cur ^ 1);
+    __syncthreads();
   }
 
-  // dQ rows, and this wave's share of sum_i P_{i,h} D~_i.
-  const float sink = a.sinks[h];
+  // dQ row, and this wave's share of sum_i P_{i,h} D~_i.
+  const float dtot = sum_xor32(dsum);
   float wsum = 0.0f;
+  if (qok) {
+    float* qrow = a.dq + ((size_t)(cs + qi) * a.Hq + h) * kHeadDim;
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    const int qi = q0 + 32 * nb + l32;
-    const float dtot = dsum[nb] + xor32(dsum[nb]);
-    if (qi < len) {
-      float* qrow = a.dq + ((size_t)(cs + qi) * a.Hq + h) * kHeadDim;
+    for (int db = 0; db < 2; ++db) {
 #pragma unroll
-      for (int db = 0; db < 2; ++db) {
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          f32x4 val = {acc[db][nb][4 * r4], acc[db][nb][4 * r4 + 1], acc[db][nb][4 * r4 + 2],
-                       acc[db][nb][4 * r4 + 3]};
-          *reinterpret_cast<f32x4*>(qrow + 32 * db + 8 * r4 + 4 * grp) = val * a.scale;
-        }
+      for (int r4 = 0; r4 < 4; ++r4) {
+        f32x4 val = {acc[db][4 * r4], acc[db][4 * r4 + 1], acc[db][4 * r4 + 2], acc[db][4 * r4 + 3]};
+        *reinterpret_cast<f32x4*>(qrow + 32 * db + 8 * r4 + 4 * grp) = val * a.scale;
       }
-      if (grp == 0) wsum += fast_exp2(__builtin_fmaf(sink, kLog2e, -lse2[nb])) * dtot;
     }
+    if (grp == 0) wsum = fast_exp2(__builtin_fmaf(a.sinks[h], kLog2e, -lse2)) * dtot;
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) wsum += __shfl_xor(wsum, off);
@@ -492,15 +521,23 @@ hipError_t launch_bwd_prep(const BwdArgs& a, hipStream_t stream) {
 hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream) {
   const long long nblocks = (long long)a.n_kblocks * a.B * a.Hkv;
   if (nblocks <= 0) return hipSuccess;
-  hipLaunchKernelGGL(attn_sink_bwd_dkdv_kernel, dim3((unsigned)nblocks), dim3(64 * a.kv_waves), 0, stream, a);
+  if (a.kv_waves == 4) {
+    hipLaunchKernelGGL(attn_sink_bwd_dkdv_kernel<2>, dim3((unsigned)nblocks), dim3(256), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL(attn_sink_bwd_dkdv_kernel<1>, dim3((unsigned)nblocks), dim3(128), 0, stream, a);
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream) {
-  constexpr int NB = kDqRowsPerWave / 32;
   const long long nblocks = (long long)a.n_qblocks * (a.Hq / a.hpw) * a.B;
   if (nblocks <= 0) return hipSuccess;
-  hipLaunchKernelGGL(attn_sink_bwd_dq_kernel<NB>, dim3((unsigned)nblocks), dim3(64 * a.hpw), 0, stream, a);
+  const dim3 grid((unsigned)nblocks), block(64 * a.hpw);
+  switch (a.hpw) {
+    case 4: hipLaunchKernelGGL(attn_sink_bwd_dq_kernel<4>, grid, block, 0, stream, a); break;
+    case 2: hipLaunchKernelGGL(attn_sink_bwd_dq_kernel<2>, grid, block, 0, stream, a); break;
+    default: hipLaunchKernelGGL(attn_sink_bwd_dq_kernel<1>, grid, block, 0, stream, a); break;
+  }
   return hipGetLastError();
 }
 

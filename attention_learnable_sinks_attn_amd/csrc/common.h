@@ -65,9 +65,30 @@ __device__ __forceinline__ bf16x8 residual8(const f32x16& c, int chunk, const bf
 // query rows and heads (dK, dV) and over keys (dQ); tiles that hold one get the residual product.
 constexpr float kSplitThreshold = 0.0625f;
 
+// Wave index within the workgroup, as a value the compiler knows to be wave-uniform (SGPR), so
+// that branches and addresses derived from it stay scalar.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
 __device__ __forceinline__ bool wave_any(bool pred) { return __builtin_amdgcn_ballot_w64(pred) != 0; }
 
 __device__ __forceinline__ bf16x8 load_bf16x8(const __bf16* p) { return *reinterpret_cast<const bf16x8*>(p); }
+
+// Operand fragment of a TRANSPOSED tile, read from X stored row-major in LDS (`stride` bf16 per
+// row) with two ds_read_b64_tr_b16: lane l receives X[k0 + 8*(l/32) + e][m0 + l%32], e = 0..7,
+// i.e. the MFMA operand whose row (or column) index runs along X's columns and whose k slots run
+// along X's rows. ds_read_b64_tr_b16 works on 16-lane groups: when the group's lanes address a
+// 4-row x 16-column block (lane s at row s/4, columns 4*(s%4)..+3), lane t of the group gets
+// column t of the block, rows 0..3.
+__device__ __forceinline__ bf16x8 load_tr8(const __bf16* lds, int stride, int k0, int m0) {
+  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+  const int l = threadIdx.x & 63;
+  const int s = l & 15;
+  const __bf16* p = lds + (k0 + 8 * (l >> 5) + (s >> 2)) * stride + m0 + 16 * ((l >> 4) & 1) + 4 * (s & 3);
+  const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p));
+  const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p + 4 * stride));
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
 
 __device__ __forceinline__ bf16x8 zero_bf16x8() {
   bf16x8 z;
@@ -84,6 +105,17 @@ __device__ __forceinline__ f32x16 zero_f32x16() {
 }
 
 __device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32); }
+
+// Reductions over the lane pair (l, l ^ 32) with one v_permlane32_swap: the swap leaves the
+// low-half values in both halves of one register and the high-half values in the other.
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 // Visibility of key j from query i inside one sequence (the sink is always visible).
 __device__ __forceinline__ bool visible(int i, int j, int len, int causal, int window) {

@@ -7,16 +7,23 @@
 // and the running denominator at exp(S_h - S_h) = 1, while the output accumulator starts at 0
 // because the sink has no value row. LSE = max + log(denominator) therefore includes the sink.
 //
-// Work split. A workgroup owns one block of 64 query rows of one sequence and `hpw` query heads
-// that share one KV head (GQA); wave w handles head hs*hpw + w. K and V tiles of 64 keys are
-// staged in LDS once and read by all of the workgroup's waves. Per tile each wave computes
+// Work split. A workgroup owns one block of 64 query rows of one sequence and HPW query heads
+// that share one KV head (GQA); wave w handles head hs*HPW + w. K and V tiles of 64 keys are
+// double-buffered in LDS and shared by the workgroup's waves; the next tile's global loads are
+// issued before the current tile's math so their latency is hidden, and one barrier per tile
+// suffices. Per tile each wave computes
 //   S^T = K Q^T   (32x32x16 MFMA; keys on the C rows, the wave's 64 queries on the columns)
-// so that each lane owns one query: the row max and row sum are mostly lane-local (one exchange
-// with lane ^ 32), and the probabilities, rounded to bf16, are already laid out as the B operand
+// so that each lane owns one query: the row max and row sum are lane-local plus one exchange
+// with lane ^ 32, and the probabilities, rounded to bf16, are already laid out as the B operand
 // of the second product
 //   O^T += V^T P^T,
-// whose A operand (V^T) is staged transposed in LDS. Causal and window tiles outside a block's
-// key range are skipped; only boundary tiles evaluate the mask.
+// whose V^T operand is read from the natural [key][d] V tile with transposing LDS loads.
+// The two 32-query column blocks are processed one after the other, so the second block's
+// softmax (VALU) can overlap the first block's P.V products (MFMA).
+//
+// The running max is exact (so each row's largest probability is exactly 1.0, which bf16 holds
+// without rounding); the sum and the accumulator are only rescaled when some row of the wave
+// sees a larger max in the tile.
 #include "kernels.h"
 
 namespace attn_sink {
@@ -24,21 +31,25 @@ namespace attn_sink {
 namespace {
 
 constexpr int kTileKeys = 64;
-constexpr int kLdsStride = 72;  // bf16 elements per staged row (64 + 8 pad: 16-byte aligned rows)
+constexpr int kLdsStride = 72;            // bf16 elements per staged row (64 + 8 pad: 16-byte aligned rows)
+constexpr int kTileElems = 64 * kLdsStride;
 
-template <int NB>  // 32-query column blocks per wave
-__global__ __launch_bounds__(256) void attn_sink_fwd_kernel(FwdArgs a) {
-  __shared__ __attribute__((aligned(16))) __bf16 k_lds[kTileKeys * kLdsStride];
-  __shared__ __attribute__((aligned(16))) __bf16 vt_lds[kHeadDim * kLdsStride];
-
+template <int HPW>
+__global__ __launch_bounds__(64 * HPW, 2) void attn_sink_fwd_kernel(FwdArgs a) {
+  constexpr int NT = 64 * HPW;
+  constexpr int KU = kTileKeys * 8 / NT;        // 16-byte K (and V) pieces per thread and tile
+  constexpr int NB = 2;                         // 32-query column blocks per wave
   constexpr int kRows = 32 * NB;
-  const int n_hs = a.Hq / a.hpw;
+  __shared__ __attribute__((aligned(16))) __bf16 k_lds[2 * kTileElems];
+  __shared__ __attribute__((aligned(16))) __bf16 v_lds[2 * kTileElems];
+
+  const int n_hs = a.Hq / HPW;
   const int bid = blockIdx.x;
   const int inner = bid % n_hs;
   const int rest = bid / n_hs;
   // Consecutive block ids walk the KV groups first, so the round-robin placement of
   // workgroups on the 8 XCDs keeps each group's K/V in few L2s.
-  const int spg = a.G / a.hpw;
+  const int spg = a.G / HPW;
   const int hs = (inner % a.Hkv) * spg + inner / a.Hkv;
   const int b = rest % a.B;
   const int qb = a.n_qblocks - 1 - rest / a.B;  // longest causal rows first
@@ -49,12 +60,11 @@ __global__ __launch_bounds__(256) void attn_sink_fwd_kernel(FwdArgs a) {
   if (q0 >= len) return;
 
   const int tid = threadIdx.x;
-  const int nthreads = blockDim.x;
-  const int wave = tid >> 6;
+  const int wave = wave_id();
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int grp = lane >> 5;
-  const int h = hs * a.hpw + wave;
+  const int h = hs * HPW + wave;
   const int g = h / a.G;
 
   // Q^T as the B operand of S^T = K Q^T: lane holds query q0 + 32nb + l32, d = 16c + 8grp + (0..7).
@@ -64,8 +74,8 @@ __global__ __launch_bounds__(256) void attn_sink_fwd_kernel(FwdArgs a) {
     const int qi = q0 + 32 * nb + l32;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      qf[nb][c] = qi < len ? load_bf16x8(a.q + ((size_t)(cs + qi) * a.Hq + h) * kHeadDim + 16 * c + 8 * grp)
-                           : zero_bf16x8();
+      // Rows past the end compute on the last row; their results are not stored.
+      qf[nb][c] = load_bf16x8(a.q + ((size_t)(cs + min(qi, len - 1)) * a.Hq + h) * kHeadDim + 16 * c + 8 * grp);
     }
   }
 
@@ -86,34 +96,49 @@ __global__ __launch_bounds__(256) void attn_sink_fwd_kernel(FwdArgs a) {
   const int kt_begin = kbeg / kTileKeys;
   const int kt_end = (kend + kTileKeys - 1) / kTileKeys;
 
-  const __bf16* kbase = a.k + (size_t)cs * a.Hkv * kHeadDim + (size_t)g * kHeadDim;
-  const __bf16* vbase = a.v + (size_t)cs * a.Hkv * kHeadDim + (size_t)g * kHeadDim;
   const size_t tok_stride = (size_t)a.Hkv * kHeadDim;
+  const __bf16* kbase = a.k + (size_t)cs * tok_stride + (size_t)g * kHeadDim;
+  const __bf16* vbase = a.v + (size_t)cs * tok_stride + (size_t)g * kHeadDim;
+
+  // Register staging of one K / V tile (global -> registers -> LDS), both in natural [key][d]
+  // layout; V^T operands are read with transposing LDS loads. Keys past the sequence end are
+  // clamped onto its last key (finite data; they are masked).
+  bf16x8 kpre[KU], vpre[KU];
+  auto prefetch = [&](int kt) {
+    const int k0 = kt * kTileKeys;
+#pragma unroll
+    for (int u = 0; u < KU; ++u) {
+      const int idx = tid + u * NT;
+      const unsigned off = (unsigned)(min(k0 + (idx >> 3), len - 1) * (int)tok_stride + 8 * (idx & 7));
+      kpre[u] = load_bf16x8(kbase + off);
+      vpre[u] = load_bf16x8(vbase + off);
+    }
+  };
+  auto commit = [&](int buf) {
+    __bf16* kl = k_lds + buf * kTileElems;
+    __bf16* vl = v_lds + buf * kTileElems;
+#pragma unroll
+    for (int u = 0; u < KU; ++u) {
+      const int idx = tid + u * NT;
+      const int off = (idx >> 3) * kLdsStride + 8 * (idx & 7);
+      *reinterpret_cast<bf16x8*>(&kl[off]) = kpre[u];
+      *reinterpret_cast<bf16x8*>(&vl[off]) = vpre[u];
+    }
+  };
+
+  if (kt_begin < kt_end) {
+    prefetch(kt_begin);
+    commit(0);
+  }
+  __syncthreads();
 
   for (int kt = kt_begin; kt < kt_end; ++kt) {
+    const int cur = (kt - kt_begin) & 1;
+    const bool has_next = kt + 1 < kt_end;
+    if (has_next) prefetch(kt + 1);
+    const __bf16* kl = k_lds + cur * kTileElems;
+    const __bf16* vl = v_lds + cur * kTileElems;
     const int k0 = kt * kTileKeys;
-    __syncthreads();  // every wave is done reading the previous tile
-    // K tile, natural layout [key][d].
-    for (int u = tid; u < kTileKeys * 8; u += nthreads) {
-      const int r = u >> 3, c8 = u & 7;
-      const int key = k0 + r;
-      bf16x8 val = key < len ? load_bf16x8(kbase + (size_t)key * tok_stride + 8 * c8) : zero_bf16x8();
-      *reinterpret_cast<bf16x8*>(&k_lds[r * kLdsStride + 8 * c8]) = val;
-    }
-    // V tile, transposed [d][key]: each thread takes two keys and writes packed pairs.
-    for (int u = tid; u < (kTileKeys / 2) * 8; u += nthreads) {
-      const int c8 = u & 7, p = u >> 3;
-      const int key = k0 + 2 * p;
-      bf16x8 v0 = key < len ? load_bf16x8(vbase + (size_t)key * tok_stride + 8 * c8) : zero_bf16x8();
-      bf16x8 v1 = key + 1 < len ? load_bf16x8(vbase + (size_t)(key + 1) * tok_stride + 8 * c8) : zero_bf16x8();
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-        bf16x2 pr = {v0[j], v1[j]};
-        *reinterpret_cast<bf16x2*>(&vt_lds[(8 * c8 + j) * kLdsStride + 2 * p]) = pr;
-      }
-    }
-    __syncthreads();
 
     // S^T = K Q^T for two 32-key row blocks.
     f32x16 s[2][NB];
@@ -123,7 +148,7 @@ __global__ __launch_bounds__(256) void attn_sink_fwd_kernel(FwdArgs a) {
       for (int nb = 0; nb < NB; ++nb) s[mb][nb] = zero_f32x16();
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        const bf16x8 ka = load_bf16x8(&k_lds[(32 * mb + swap23(l32)) * kLdsStride + 16 * c + 8 * grp]);
+        const bf16x8 ka = load_bf16x8(&kl[(32 * mb + swap23(l32)) * kLdsStride + 16 * c + 8 * grp]);
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) s[mb][nb] = mfma_32x32x16(ka, qf[nb][c], s[mb][nb]);
       }
@@ -146,20 +171,37 @@ __global__ __launch_bounds__(256) void attn_sink_fwd_kernel(FwdArgs a) {
       }
     }
 
-    bf16x8 pb[2][2][NB];
+    // Row maxima of the tile (raw scores; the scale is positive).
+    float tmax[NB];
+    bool grow = false;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      float tmax = kNegInf;
+      float t = kNegInf;
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, s[mb][nb][i]);
+        for (int i = 0; i < 16; ++i) t = fmaxf(t, s[mb][nb][i]);
       }
-      tmax = fmaxf(tmax, xor32(tmax));
-      const float mnew = fmaxf(m[nb], tmax * a.scale_log2);
-      const float moff = mnew == kNegInf ? 0.0f : mnew;  // a row with nothing visible yet stays at 0
-      const float alpha = fast_exp2(m[nb] - moff);
+      tmax[nb] = max_xor32(t) * a.scale_log2;
+      grow = grow || (tmax[nb] > m[nb]);
+    }
+    if (wave_any(grow)) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const float mnew = fmaxf(m[nb], tmax[nb]);
+        const float alpha = mnew == kNegInf ? 1.0f : fast_exp2(m[nb] - mnew);
+        lsum[nb] *= alpha;
+        o[0][nb] *= alpha;
+        o[1][nb] *= alpha;
+        m[nb] = mnew;
+      }
+    }
+
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const float moff = m[nb] == kNegInf ? 0.0f : m[nb];  // nothing visible yet: exp2(-inf) = 0
       float rs = 0.0f;
+      bf16x8 pb[2][2];
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) {
 #pragma unroll
@@ -168,34 +210,32 @@ __global__ __launch_bounds__(256) void attn_sink_fwd_kernel(FwdArgs a) {
           s[mb][nb][i] = p;
           rs += p;
         }
-        pb[mb][0][nb] = pack8(s[mb][nb], 0);
-        pb[mb][1][nb] = pack8(s[mb][nb], 1);
+        pb[mb][0] = pack8(s[mb][nb], 0);
+        pb[mb][1] = pack8(s[mb][nb], 1);
       }
-      lsum[nb] = lsum[nb] * alpha + rs;
-      o[0][nb] *= alpha;
-      o[1][nb] *= alpha;
-      m[nb] = mnew;
-    }
-
-    // O^T += V^T P^T, contracting over the tile's 64 keys in four 16-key chunks.
+      lsum[nb] += rs;
+      // O^T += V^T P^T for this column block, contracting over the tile's 64 keys.
 #pragma unroll
-    for (int db = 0; db < 2; ++db) {
+      for (int db = 0; db < 2; ++db) {
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
+        for (int mb = 0; mb < 2; ++mb) {
 #pragma unroll
-        for (int cc = 0; cc < 2; ++cc) {
-          const bf16x8 va = load_bf16x8(&vt_lds[(32 * db + l32) * kLdsStride + 32 * mb + 16 * cc + 8 * grp]);
-#pragma unroll
-          for (int nb = 0; nb < NB; ++nb) o[db][nb] = mfma_32x32x16(va, pb[mb][cc][nb], o[db][nb]);
+          for (int cc = 0; cc < 2; ++cc) {
+            const bf16x8 va = load_tr8(vl, kLdsStride, 32 * mb + 16 * cc, 32 * db);  // V^T rows d, keys
+            o[db][nb] = mfma_32x32x16(va, pb[mb][cc], o[db][nb]);
+          }
         }
       }
     }
+
+    if (has_next) commit(cur ^ 1);
+    __syncthreads();
   }
 
   // Epilogue: combine the two lane halves' partial denominators, normalise, store.
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
-    const float ltot = lsum[nb] + xor32(lsum[nb]);
+    const float ltot = sum_xor32(lsum[nb]);
     const float inv = ltot > 0.0f ? 1.0f / ltot : 0.0f;
     const int qi = q0 + 32 * nb + l32;
     if (qi < len) {
@@ -219,10 +259,14 @@ __global__ __launch_bounds__(256) void attn_sink_fwd_kernel(FwdArgs a) {
 }  // namespace
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
-  constexpr int NB = kFwdRowsPerWave / 32;
   const long long nblocks = (long long)a.n_qblocks * (a.Hq / a.hpw) * a.B;
   if (nblocks <= 0) return hipSuccess;
-  hipLaunchKernelGGL(attn_sink_fwd_kernel<NB>, dim3((unsigned)nblocks), dim3(64 * a.hpw), 0, stream, a);
+  const dim3 grid((unsigned)nblocks), block(64 * a.hpw);
+  switch (a.hpw) {
+    case 4: hipLaunchKernelGGL(attn_sink_fwd_kernel<4>, grid, block, 0, stream, a); break;
+    case 2: hipLaunchKernelGGL(attn_sink_fwd_kernel<2>, grid, block, 0, stream, a); break;
+    default: hipLaunchKernelGGL(attn_sink_fwd_kernel<1>, grid, block, 0, stream, a); break;
+  }
   return hipGetLastError();
 }
 

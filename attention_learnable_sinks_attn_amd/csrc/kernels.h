@@ -6,7 +6,7 @@
 namespace attn_sink {
 
 constexpr int kFwdRowsPerWave = 64;   // queries per wave in the forward
-constexpr int kDqRowsPerWave = 64;    // queries per wave in the row-parallel dQ / dSink pass
+constexpr int kDqRowsPerWave = 32;    // queries per wave in the row-parallel dQ / dSink pass
 constexpr int kKvKeysPerBlock = 64;   // keys per workgroup in the column-parallel dK / dV pass
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);

@@ -57,7 +57,8 @@ enum {
   ATTN_SINK_OK = 0,
   ATTN_SINK_ERR_NULL_PTR = -1,    /* a required pointer (or the shape struct) is NULL */
   ATTN_SINK_ERR_BAD_SHAPE = -2,   /* T < 0, B < 1, Hq < 1, Hkv < 1, Hq % Hkv != 0, max_seqlen < 0
-                                     or max_seqlen > T, or a size that overflows 32-bit indexing */
+                                     or max_seqlen > T, or max_seqlen * Hq * 64 >= 2^31 (offsets
+                                     inside one sequence are 32-bit) */
   ATTN_SINK_ERR_UNSUPPORTED = -3, /* head_dim != 64 or out_dtype != ATTN_SINK_F32 */
   ATTN_SINK_ERR_BAD_WINDOW = -4,  /* window > 0 without causal */
   ATTN_SINK_ERR_WORKSPACE = -5,   /* workspace NULL or smaller than attn_sink_bwd_workspace_bytes() */
