@@ -39,9 +39,15 @@ int dsink_slots(const attn_sink_shape* s) { return s->total_tokens / kDqRowsPerW
 
 size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+int kv_halves(const attn_sink_shape* s) { return (s->num_heads_q / s->num_heads_kv) % 2 == 0 ? 2 : 1; }
+
+size_t dkv_part_bytes(const attn_sink_shape* s) {
+  return (size_t)2 * kv_halves(s) * s->total_tokens * s->num_heads_kv * s->head_dim * sizeof(float);
+}
+
 size_t workspace_bytes(const attn_sink_shape* s) {
   return round256((size_t)s->num_heads_q * s->total_tokens * sizeof(float)) +
-         round256((size_t)s->num_heads_q * dsink_slots(s) * sizeof(float));
+         round256((size_t)s->num_heads_q * dsink_slots(s) * sizeof(float)) + round256(dkv_part_bytes(s));
 }
 
 int bwd_impl(const void* q, const void* k, const void* v, const float* sinks, const void* out, const float* lse,
@@ -79,13 +85,16 @@ int bwd_impl(const void* q, const void* k, const void* v, const float* sinks, co
   a.dsink_part = reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                           round256((size_t)shape->num_heads_q * T * sizeof(float)));
   a.n_slots = dsink_slots(shape);
+  a.dkv_part = reinterpret_cast<float*>(reinterpret_cast<char*>(a.dsink_part) +
+                                        round256((size_t)shape->num_heads_q * a.n_slots * sizeof(float)));
+  a.n_halves = kv_halves(shape);
   a.T = T;
   a.B = shape->num_seqs;
   a.Hq = shape->num_heads_q;
   a.Hkv = shape->num_heads_kv;
   a.G = a.Hq / a.Hkv;
   a.hpw = heads_per_group_split(a.G);
-  a.kv_waves = a.G % 2 == 0 ? 4 : 2;  // two key halves x (two head streams when G is even)
+  a.kv_waves = (a.G / a.n_halves) % 2 == 0 ? 4 : 2;  // two key halves x (two head streams if possible)
   a.n_qblocks = (shape->max_seqlen + kDqRowsPerWave - 1) / kDqRowsPerWave;
   a.n_kblocks = (shape->max_seqlen + kKvKeysPerBlock - 1) / kKvKeysPerBlock;
   a.causal = causal ? 1 : 0;
@@ -94,7 +103,8 @@ int bwd_impl(const void* q, const void* k, const void* v, const float* sinks, co
   a.scale_log2 = a.scale * kLog2e;
 
   typedef hipError_t (*launcher)(const BwdArgs&, hipStream_t);
-  const launcher steps[kBwdNumKernels] = {launch_bwd_prep, launch_bwd_dkdv, launch_bwd_dq, launch_bwd_dsink};
+  const launcher steps[kBwdNumKernels] = {launch_bwd_prep, launch_bwd_dkdv, launch_bwd_dkdv_sum, launch_bwd_dq,
+                                           launch_bwd_dsink};
   for (int i = 0; i < kBwdNumKernels; ++i) {
     if (events && hipEventRecord(static_cast<hipEvent_t>(events[i]), stream) != hipSuccess) return ATTN_SINK_ERR_HIP;
     if (steps[i](a, stream) != hipSuccess) return ATTN_SINK_ERR_HIP;
@@ -166,7 +176,8 @@ int attn_sink_bwd_num_kernels(void) { return kBwdNumKernels; }
 
 const char* attn_sink_bwd_kernel_name(int i) {
   static const char* const names[kBwdNumKernels] = {"attn_sink_bwd_prep_kernel", "attn_sink_bwd_dkdv_kernel",
-                                                    "attn_sink_bwd_dq_kernel", "attn_sink_bwd_dsink_kernel"};
+                                                    "attn_sink_bwd_dkdv_sum_kernel", "attn_sink_bwd_dq_kernel",
+                                                    "attn_sink_bwd_dsink_kernel"};
   return (i >= 0 && i < kBwdNumKernels) ? names[i] : nullptr;
 }
 

@@ -12,12 +12,16 @@
 //
 // Passes (all on the caller's stream, no atomics, bitwise reproducible):
 //  1. prep:  D_i = rowsum(dO * O) for every (row, head); clear the dSink partial sums.
-//  2. dkdv:  column-parallel. A workgroup owns 64 keys of one KV head: two key halves of 32
-//            times one or two "head streams" (the group's query heads split between streams).
+//  2. dkdv:  column-parallel. A workgroup owns 64 keys of one KV head and one half of the
+//            group's query heads: two key halves of 32 times one or two "head streams".
 //            For each step (head, 64 query rows) the Q, dO, LSE and D rows are staged once per
 //            stream in LDS, double-buffered with the next step's global loads issued ahead;
 //            the transposed Q^T / dO^T operands come from transposing LDS loads. dK^T and dV^T of each wave's 32 keys stay in
-//            registers; the two streams' partial sums are added in LDS at the end.
+//            registers; the two streams' partial sums are added in LDS at the end, and each
+//            head half writes its own fp32 partial. Splitting the heads doubles the number of
+//            workgroups, so that (launched longest first) they keep two per CU busy under a
+//            causal mask instead of leaving a long block alone on its CU.
+//  2b. dkdv_sum: dK = scale * (sum of the halves), dV = sum of the halves.
 //  3. dq:    row-parallel. A workgroup owns 32 query rows of `hpw` heads of one group (one head
 //            per wave) and streams double-buffered 64-key tiles of K and V through LDS (K^T
 //            operands come from transposing LDS loads of the K tile).
@@ -81,19 +85,21 @@ __global__ __launch_bounds__(128 * NS, 2) void attn_sink_bwd_dkdv_kernel(BwdArgs
   constexpr int NW = 2 * NS;
   constexpr int NT = 64 * NW;
   constexpr int kRR = kKvStageRows * 8 / NT;  // 16-byte pieces per thread and staged tile
+  static_assert(NT == NS * 2 * kKvStageRows, "one LSE or D value per thread and stage");
   __shared__ __attribute__((aligned(16))) unsigned char smem[2 * NS * kKvStageBytes];
   static_assert(sizeof(smem) >= 4 * 32 * kKvRedStride * 4, "reduction buffer fits");
 
-  // Block order: key blocks 0, 1, ... for the first half of the grid and n-1, n-2, ... for the
-  // second, so that blocks i and i + half (likely co-resident on a CU) carry complementary
-  // amounts of causal work.
+  // Block order: KV group fastest (consecutive ids land on different XCDs, each XCD keeps few
+  // groups' rows in its L2), then head half, sequence, and key block ascending: under a causal
+  // mask the first key blocks carry the most query rows, so the longest blocks start first and
+  // the short ones fill in as slots free up.
   const int bid = blockIdx.x;
   const int g = bid % a.Hkv;
-  const int rest = bid / a.Hkv;
+  int rest = bid / a.Hkv;
+  const int hh = rest % a.n_halves;
+  rest /= a.n_halves;
   const int b = rest % a.B;
-  const int j = rest / a.B;
-  const int half = (a.n_kblocks + 1) / 2;
-  const int kb = j < half ? j : a.n_kblocks - 1 - (j - half);
+  const int kb = rest / a.B;
   const int cs = a.cu[b];
   const int len = a.cu[b + 1] - cs;
   const int kblk = kb * kKvKeysPerBlock;
@@ -107,7 +113,9 @@ __global__ __launch_bounds__(128 * NS, 2) void attn_sink_bwd_dkdv_kernel(BwdArgs
   const int kh = wave & 1;        // key half
   const int st = wave >> 1;       // head stream
   const int k0 = kblk + 32 * kh;  // this wave's 32 keys
-  const int heads_per_stream = a.G / NS;
+  const int heads_half = a.G / a.n_halves;
+  const int heads_per_stream = heads_half / NS;
+  const int h_base = g * a.G + hh * heads_half;  // stream s takes heads h_base + s + NS * j
 
   // K^T and V^T as B operands (k = d, n = key): lane holds key k0 + l32, d = 16c + 8grp + (0..7).
   bf16x8 kf[4], vf[4];
@@ -142,7 +150,7 @@ __global__ __launch_bounds__(128 * NS, 2) void attn_sink_bwd_dkdv_kernel(BwdArgs
   auto prefetch = [&](int hj, int i0) {
 #pragma unroll
     for (int t = 0; t < 2 * NS; ++t) {
-      const int h = g * a.G + (t >> 1) + NS * hj;
+      const int h = h_base + (t >> 1) + NS * hj;
       const __bf16* base = ((t & 1) ? a.dout : a.q) + ((size_t)cs * a.Hq + h) * kHeadDim;
 #pragma unroll
       for (int rr = 0; rr < kRR; ++rr) {
@@ -150,13 +158,12 @@ __global__ __launch_bounds__(128 * NS, 2) void attn_sink_bwd_dkdv_kernel(BwdArgs
         pre[t][rr] = load_bf16x8(base + (unsigned)(qi * a.Hq * kHeadDim + 8 * pc8));
       }
     }
-    if (tid < NS * 2 * kKvStageRows) {
+    {  // exactly one LSE or D value per thread (NT == NS * 2 * kKvStageRows)
       const int s = tid / (2 * kKvStageRows);
       const int which = (tid / kKvStageRows) & 1;
-      const int h = g * a.G + s + NS * hj;
+      const int h = h_base + s + NS * hj;
       const int qi = min(i0 + (tid & (kKvStageRows - 1)), len - 1);
-      const float v = (which ? a.dws : a.lse)[(size_t)h * a.T + cs + qi];
-      pre_ld = which ? v : v * kLog2e;
+      pre_ld = (which ? a.dws : a.lse)[(size_t)h * a.T + cs + qi];  // consumed only in commit
     }
   };
   auto commit = [&](int buf) {
@@ -168,17 +175,22 @@ __global__ __launch_bounds__(128 * NS, 2) void attn_sink_bwd_dkdv_kernel(BwdArgs
         *reinterpret_cast<bf16x8*>(&nat[(prow + (NT / 8) * rr) * kLdsStride + 8 * pc8]) = pre[t][rr];
       }
     }
-    if (tid < NS * 2 * kKvStageRows) {
+    {
       float* f = reinterpret_cast<float*>(stage_ptr(buf, tid / (2 * kKvStageRows)) + 2 * kKvNatElems * 2);
-      f[tid & (2 * kKvStageRows - 1)] = pre_ld;
+      f[tid & (2 * kKvStageRows - 1)] = ((tid / kKvStageRows) & 1) ? pre_ld : pre_ld * kLog2e;  // LSE in log2 units
     }
   };
 
+  // Stages run from the last query rows backwards: every workgroup's causal range ends at the
+  // sequence end, so workgroups of one KV group stream the same rows at about the same time and
+  // mostly hit in L2.
+  auto stage_row = [&](int t) { return (t_begin + n_t - 1 - t) * kKvStageRows; };
   int hj = 0, ti = 0;  // current step = (head index within the stream, stage index)
-  if (n_steps > 0) {
-    prefetch(0, t_begin * kKvStageRows);
-    commit(0);
-  }
+  // Unconditional (n_steps > 0 here): every load issued so far, including K and V, is complete
+  // on every path into the loop, so the loop only waits on its prefetch when committing it.
+  prefetch(0, stage_row(0));
+  commit(0);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): nothing issued before the loop stays in flight
   __syncthreads();
 
   for (int step = 0; step < n_steps; ++step) {
@@ -186,7 +198,7 @@ __global__ __launch_bounds__(128 * NS, 2) void attn_sink_bwd_dkdv_kernel(BwdArgs
     const bool has_next = step + 1 < n_steps;
     const int hj_n = ti + 1 < n_t ? hj : hj + 1;
     const int ti_n = ti + 1 < n_t ? ti + 1 : 0;
-    if (has_next) prefetch(hj_n, (t_begin + ti_n) * kKvStageRows);
+    if (has_next) prefetch(hj_n, stage_row(ti_n));
 
     const unsigned char* sp = stage_ptr(cur, st);
     const __bf16* qn = reinterpret_cast<const __bf16*>(sp);
@@ -196,7 +208,7 @@ __global__ __launch_bounds__(128 * NS, 2) void attn_sink_bwd_dkdv_kernel(BwdArgs
 
 #pragma unroll
     for (int sub = 0; sub < kKvStageRows / kKvSub; ++sub) {
-      const int i0 = (t_begin + ti) * kKvStageRows + kKvSub * sub;
+      const int i0 = stage_row(ti) + kKvSub * sub;
       // Skip blocks in which no (query, key) pair of this wave is visible (wave-uniform).
       const bool live = (!a.causal || k0 <= i0 + kKvSub - 1) && (a.window <= 0 || i0 <= k0 + 30 + a.window) &&
                         k0 < len && i0 < len;
@@ -256,10 +268,17 @@ __global__ __launch_bounds__(128 * NS, 2) void attn_sink_bwd_dkdv_kernel(BwdArgs
         dk[db] = mfma_32x32x16(qta0, ds0, dk[db]);
         dk[db] = mfma_32x32x16(qta1, ds1, dk[db]);
         if (split) {
-          dv[db] = mfma_32x32x16(doa0, residual8(s, 0, pb0), dv[db]);
-          dv[db] = mfma_32x32x16(doa1, residual8(s, 1, pb1), dv[db]);
-          dk[db] = mfma_32x32x16(qta0, residual8(dp, 0, ds0), dk[db]);
-          dk[db] = mfma_32x32x16(qta1, residual8(dp, 1, ds1), dk[db]);
+          // The opaque copies of the packed values keep the residual arithmetic inside this
+          // rarely taken branch (it depends on them), without copying the fp32 tiles.
+          bf16x8 h0 = pb0, h1 = pb1, e0 = ds0, e1 = ds1;
+          opaque(h0);
+          opaque(h1);
+          opaque(e0);
+          opaque(e1);
+          dv[db] = mfma_32x32x16(doa0, residual8(s, 0, h0), dv[db]);
+          dv[db] = mfma_32x32x16(doa1, residual8(s, 1, h1), dv[db]);
+          dk[db] = mfma_32x32x16(qta0, residual8(dp, 0, e0), dk[db]);
+          dk[db] = mfma_32x32x16(qta1, residual8(dp, 1, e1), dk[db]);
         }
       }
     }
@@ -289,8 +308,10 @@ __global__ __launch_bounds__(128 * NS, 2) void attn_sink_bwd_dkdv_kernel(BwdArgs
   if (st == 0) {
     const int key = k0 + l32;
     if (key < len) {
-      float* dkrow = a.dk + ((size_t)(cs + key) * a.Hkv + g) * kHeadDim;
-      float* dvrow = a.dv + ((size_t)(cs + key) * a.Hkv + g) * kHeadDim;
+      // This head half's partial sums (unscaled); attn_sink_bwd_dkdv_sum_kernel adds the halves.
+      const size_t plane = (size_t)a.T * a.Hkv * kHeadDim;
+      float* dkrow = a.dkv_part + hh * plane + ((size_t)(cs + key) * a.Hkv + g) * kHeadDim;
+      float* dvrow = a.dkv_part + (a.n_halves + hh) * plane + ((size_t)(cs + key) * a.Hkv + g) * kHeadDim;
 #pragma unroll
       for (int db = 0; db < 2; ++db) {
 #pragma unroll
@@ -302,11 +323,28 @@ __global__ __launch_bounds__(128 * NS, 2) void attn_sink_bwd_dkdv_kernel(BwdArgs
             kv += *reinterpret_cast<const f32x4*>(&red[l32 * kKvRedStride + d]);
             vv += *reinterpret_cast<const f32x4*>(&red[(64 + l32) * kKvRedStride + d]);
           }
-          *reinterpret_cast<f32x4*>(dkrow + d) = kv * a.scale;
+          *reinterpret_cast<f32x4*>(dkrow + d) = kv;
           *reinterpret_cast<f32x4*>(dvrow + d) = vv;
         }
       }
     }
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// 2b. dK = scale * (sum of the head halves' partials), dV = sum of the partials.
+// ------------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void attn_sink_bwd_dkdv_sum_kernel(BwdArgs a) {
+  const size_t plane4 = (size_t)a.T * a.Hkv * (kHeadDim / 4);  // float4 per partial plane
+  const f32x4* p = reinterpret_cast<const f32x4*>(a.dkv_part);
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < plane4; i += (size_t)gridDim.x * blockDim.x) {
+    f32x4 k4 = p[i], v4 = p[a.n_halves * plane4 + i];
+    for (int hh = 1; hh < a.n_halves; ++hh) {
+      k4 += p[hh * plane4 + i];
+      v4 += p[(a.n_halves + hh) * plane4 + i];
+    }
+    reinterpret_cast<f32x4*>(a.dk)[i] = k4 * a.scale;
+    reinterpret_cast<f32x4*>(a.dv)[i] = v4;
   }
 }
 
@@ -395,10 +433,11 @@ __global__ __launch_bounds__(64 * HPW, 2) void attn_sink_bwd_dq_kernel(BwdArgs a
     }
   };
 
-  if (kt_begin < kt_end) {
-    prefetch(kt_begin);
-    commit(0);
-  }
+  // Unconditional (the range is never empty here): every load issued so far is complete on every
+  // path into the loop, so the loop only waits on its prefetch when committing it.
+  prefetch(kt_begin);
+  commit(0);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): nothing issued before the loop stays in flight
   __syncthreads();
 
   for (int kt = kt_begin; kt < kt_end; ++kt) {
@@ -463,7 +502,11 @@ __global__ __launch_bounds__(64 * HPW, 2) void attn_sink_bwd_dq_kernel(BwdArgs a
         for (int cc = 0; cc < 2; ++cc) {
           const bf16x8 kta = load_tr8(kl, kLdsStride, 32 * mb + 16 * cc, 32 * db);  // K^T rows d, keys
           acc[db] = mfma_32x32x16(kta, dsb[mb][cc], acc[db]);
-          if (split) acc[db] = mfma_32x32x16(kta, residual8(dp[mb], cc, dsb[mb][cc]), acc[db]);
+          if (split) {
+            bf16x8 hi = dsb[mb][cc];
+            opaque(hi);  // keeps the residual arithmetic inside this rarely taken branch
+            acc[db] = mfma_32x32x16(kta, residual8(dp[mb], cc, hi), acc[db]);
+          }
         }
       }
     }
@@ -518,8 +561,17 @@ hipError_t launch_bwd_prep(const BwdArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+hipError_t launch_bwd_dkdv_sum(const BwdArgs& a, hipStream_t stream) {
+  const long long n4 = (long long)a.T * a.Hkv * (kHeadDim / 4);
+  if (n4 <= 0) return hipSuccess;
+  long long nblocks = (n4 + 255) / 256;
+  if (nblocks > 8192) nblocks = 8192;
+  hipLaunchKernelGGL(attn_sink_bwd_dkdv_sum_kernel, dim3((unsigned)nblocks), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream) {
-  const long long nblocks = (long long)a.n_kblocks * a.B * a.Hkv;
+  const long long nblocks = (long long)a.n_kblocks * a.B * a.Hkv * a.n_halves;
   if (nblocks <= 0) return hipSuccess;
   if (a.kv_waves == 4) {
     hipLaunchKernelGGL(attn_sink_bwd_dkdv_kernel<2>, dim3((unsigned)nblocks), dim3(256), 0, stream, a);

@@ -117,12 +117,24 @@ __device__ __forceinline__ float sum_xor32(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Visibility of key j from query i inside one sequence (the sink is always visible).
+// Visibility of key j from query i inside one sequence (the sink is always visible). Bitwise
+// operators keep it branch-free.
 __device__ __forceinline__ bool visible(int i, int j, int len, int causal, int window) {
-  bool ok = j < len;
-  if (causal) ok = ok && (j <= i);
-  if (window > 0) ok = ok && (j > i - window);
-  return ok;
+  return (j < len) & ((causal == 0) | (j <= i)) & ((window <= 0) | (j > i - window));
+}
+
+// Makes a register value opaque to the optimiser (no instruction is emitted). Used at the top of
+// rarely taken branches so that their arithmetic is not speculated onto the common path.
+__device__ __forceinline__ void opaque(f32x16& x) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) asm volatile("" : "+v"(x[i]));
+}
+__device__ __forceinline__ void opaque(bf16x8& x) {
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  u32x4 u = __builtin_bit_cast(u32x4, x);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(u[i]));
+  x = __builtin_bit_cast(bf16x8, u);
 }
 
 // Work descriptors (filled on the host).
@@ -156,10 +168,12 @@ struct BwdArgs {
   float* dsinks;
   float* dws;        // D_i = rowsum(dO * O), [Hq, T]
   float* dsink_part; // per (head, row-block slot) partial sums of P_sink * D~, [Hq, n_slots]
+  float* dkv_part;   // dK / dV partial sums per head half: [2][n_halves][T][Hkv][64] (unscaled)
   int n_slots;
+  int n_halves;      // query-head halves of a KV group processed by separate dK/dV workgroups
   int T, B, Hq, Hkv, G;
   int hpw;            // dQ kernel: query heads per workgroup
-  int kv_waves;       // dK/dV kernel: waves per workgroup (each takes G / kv_waves heads)
+  int kv_waves;       // dK/dV kernel: waves per workgroup (2 key halves x head streams)
   int n_qblocks;      // dQ kernel grid rows
   int n_kblocks;      // dK/dV kernel grid rows
   int causal, window;

@@ -126,10 +126,14 @@ __global__ __launch_bounds__(64 * HPW, 2) void attn_sink_fwd_kernel(FwdArgs a) {
     }
   };
 
-  if (kt_begin < kt_end) {
-    prefetch(kt_begin);
-    commit(0);
-  }
+  // Unconditional (the range is never empty here): every load issued so far, including the Q
+  // operands, is complete on every path into the loop, so the loop only waits on its prefetch
+  // when committing it.
+  prefetch(kt_begin);
+  commit(0);
+  // vmcnt(0): the Q loads may have been scheduled after the tile loads; make sure nothing issued
+  // before the loop is still in flight, or the loop would wait on its own prefetch at the top.
+  __builtin_amdgcn_s_waitcnt(0x0F70);
   __syncthreads();
 
   for (int kt = kt_begin; kt < kt_end; ++kt) {

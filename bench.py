@@ -41,6 +41,7 @@ KERNEL_FLOPS_PER_PAIR_D = {
     "attn_sink_fwd_kernel": 4,
     "attn_sink_bwd_prep_kernel": 0,
     "attn_sink_bwd_dkdv_kernel": 8,
+    "attn_sink_bwd_dkdv_sum_kernel": 0,
     "attn_sink_bwd_dq_kernel": 2,
     "attn_sink_bwd_dsink_kernel": 0,
 }
