@@ -19,9 +19,10 @@ int check_shape(const attn_sink_shape* s) {
     return ATTN_SINK_ERR_BAD_SHAPE;
   }
   if (s->head_dim != kHeadDim || s->out_dtype != ATTN_SINK_F32) return ATTN_SINK_ERR_UNSUPPORTED;
-  // Element offsets are 64-bit in the kernels, but grid sizes and per-head row indices are 32-bit.
+  // Element offsets are 64-bit in the kernels, but grid sizes (the prep pass launches T * Hq / 16
+  // workgroups) and per-head row indices are 32-bit.
   const long long rows_q = (long long)s->total_tokens * s->num_heads_q;
-  if (rows_q > (1LL << 40)) return ATTN_SINK_ERR_BAD_SHAPE;
+  if (rows_q > (1LL << 34)) return ATTN_SINK_ERR_BAD_SHAPE;
   // Within one sequence, element offsets (row * heads * 64) are 32-bit.
   if ((long long)s->max_seqlen * s->num_heads_q * s->head_dim >= (1LL << 31)) return ATTN_SINK_ERR_BAD_SHAPE;
   const long long nq = ((long long)s->max_seqlen + 63) / 64;
@@ -45,9 +46,18 @@ size_t dkv_part_bytes(const attn_sink_shape* s) {
   return (size_t)2 * kv_halves(s) * s->total_tokens * s->num_heads_kv * s->head_dim * sizeof(float);
 }
 
+// Workspace: -LSE/scale [Hq, T], -D [Hq, T], dSink partials [Hq, n_slots], dK/dV partials per head
+// half, each 256-byte aligned.
+size_t row_plane_bytes(const attn_sink_shape* s) {
+  return round256((size_t)s->num_heads_q * s->total_tokens * sizeof(float));
+}
+
+size_t dsink_part_bytes(const attn_sink_shape* s) {
+  return round256((size_t)s->num_heads_q * dsink_slots(s) * sizeof(float));
+}
+
 size_t workspace_bytes(const attn_sink_shape* s) {
-  return round256((size_t)s->num_heads_q * s->total_tokens * sizeof(float)) +
-         round256((size_t)s->num_heads_q * dsink_slots(s) * sizeof(float)) + round256(dkv_part_bytes(s));
+  return 2 * row_plane_bytes(s) + dsink_part_bytes(s) + round256(dkv_part_bytes(s));
 }
 
 int bwd_impl(const void* q, const void* k, const void* v, const float* sinks, const void* out, const float* lse,
@@ -81,12 +91,12 @@ int bwd_impl(const void* q, const void* k, const void* v, const float* sinks, co
   a.dk = dk;
   a.dv = dv;
   a.dsinks = dsinks;
-  a.dws = static_cast<float*>(workspace);
-  a.dsink_part = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                          round256((size_t)shape->num_heads_q * T * sizeof(float)));
+  a.nlse = static_cast<float*>(workspace);
+  a.negd = reinterpret_cast<float*>(static_cast<char*>(workspace) + row_plane_bytes(shape));
+  a.dsink_part = reinterpret_cast<float*>(static_cast<char*>(workspace) + 2 * row_plane_bytes(shape));
+  a.dkv_part = reinterpret_cast<float*>(static_cast<char*>(workspace) + 2 * row_plane_bytes(shape) +
+                                        dsink_part_bytes(shape));
   a.n_slots = dsink_slots(shape);
-  a.dkv_part = reinterpret_cast<float*>(reinterpret_cast<char*>(a.dsink_part) +
-                                        round256((size_t)shape->num_heads_q * a.n_slots * sizeof(float)));
   a.n_halves = kv_halves(shape);
   a.T = T;
   a.B = shape->num_seqs;
@@ -94,7 +104,7 @@ int bwd_impl(const void* q, const void* k, const void* v, const float* sinks, co
   a.Hkv = shape->num_heads_kv;
   a.G = a.Hq / a.Hkv;
   a.hpw = heads_per_group_split(a.G);
-  a.kv_waves = (a.G / a.n_halves) % 2 == 0 ? 4 : 2;  // two key halves x (two head streams if possible)
+  a.kv_streams = (a.G / a.n_halves) % 2 == 0 ? 2 : 1;  // two key halves x (two head streams if possible)
   a.n_qblocks = (shape->max_seqlen + kDqRowsPerWave - 1) / kDqRowsPerWave;
   a.n_kblocks = (shape->max_seqlen + kKvKeysPerBlock - 1) / kKvKeysPerBlock;
   a.causal = causal ? 1 : 0;

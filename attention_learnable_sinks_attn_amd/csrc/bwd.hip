@@ -11,16 +11,19 @@
 //   dQ = scale dS K,  dK = scale dS^T Q,  dV = P^T dO.
 //
 // Passes (all on the caller's stream, no atomics, bitwise reproducible):
-//  1. prep:  D_i = rowsum(dO * O) for every (row, head); clear the dSink partial sums.
+//  1. prep:  -LSE_i / scale and -D_i = -rowsum(dO * O) for every (head, row), in the workspace;
+//            clear the dSink partial sums.
 //  2. dkdv:  column-parallel. A workgroup owns 64 keys of one KV head and one half of the
-//            group's query heads: two key halves of 32 times one or two "head streams".
-//            For each step (head, 64 query rows) the Q, dO, LSE and D rows are staged once per
-//            stream in LDS, double-buffered with the next step's global loads issued ahead;
-//            the transposed Q^T / dO^T operands come from transposing LDS loads. dK^T and dV^T of each wave's 32 keys stay in
-//            registers; the two streams' partial sums are added in LDS at the end, and each
-//            head half writes its own fp32 partial. Splitting the heads doubles the number of
-//            workgroups, so that (launched longest first) they keep two per CU busy under a
-//            causal mask instead of leaving a long block alone on its CU.
+//            group's query heads: two key halves of 32 (one per wave) times one or two "head
+//            streams". Each stream streams its query rows 32 at a time through a 3-slot LDS ring
+//            filled by direct global->LDS copies issued two steps ahead (the two key halves of a
+//            stream split the copies and share the tiles); one barrier per step. The row tiles
+//            are stored with an XOR swizzle of their 16-byte chunks, which keeps both the
+//            fragment reads (rows permuted by swap23) and the transposing reads of Q^T / dO^T
+//            free of bank conflicts. dK^T and dV^T of each wave's 32 keys stay in registers; the
+//            two streams' partial sums are added in LDS at the end, and each head half writes its
+//            own fp32 partial. Splitting the heads doubles the number of workgroups, so that
+//            (launched longest first) they keep two per CU busy under a causal mask.
 //  2b. dkdv_sum: dK = scale * (sum of the halves), dV = sum of the halves.
 //  3. dq:    row-parallel. A workgroup owns 32 query rows of `hpw` heads of one group (one head
 //            per wave) and streams double-buffered 64-key tiles of K and V through LDS (K^T
@@ -30,6 +33,8 @@
 //            does not carry the bf16 rounding of the forward's P.V product, which matters
 //            because the terms of dL/dS_h cancel heavily.
 //  4. dsink: dL/dS_h = -(sum of the partials of head h), summed in a fixed order.
+#include <type_traits>
+
 #include "kernels.h"
 
 namespace attn_sink {
@@ -40,14 +45,18 @@ constexpr int kLdsStride = 72;  // bf16 per staged 64-element row (16-byte align
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 // ------------------------------------------------------------------------------------------
-// 1. D_i = sum_d dO[i,h,d] * O[i,h,d]; 16 lanes per (row, head), 4 elements each.
+// 1. -D_i = -sum_d dO[i,h,d] * O[i,h,d] and -LSE_i / scale. A block handles 16 consecutive rows
+//    of one head (16 lanes per row, 4 elements each), so the [Hq, T] results are written
+//    contiguously.
 // ------------------------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void attn_sink_bwd_prep_kernel(BwdArgs a) {
-  const long long rows = (long long)a.T * a.Hq;
-  const long long row = (long long)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int tblocks = (a.T + 15) / 16;
+  const int h = blockIdx.x / tblocks;
+  const int t = (blockIdx.x - h * tblocks) * 16 + (threadIdx.x >> 4);
   const int part = threadIdx.x & 15;
   float acc = 0.0f;
-  if (row < rows) {
+  if (h < a.Hq && t < a.T) {
+    const size_t row = (size_t)t * a.Hq + h;
     const f32x4 o = *reinterpret_cast<const f32x4*>(a.out + row * kHeadDim + 4 * part);
     typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
     const bf16x4 d = *reinterpret_cast<const bf16x4*>(a.dout + row * kHeadDim + 4 * part);
@@ -57,10 +66,10 @@ __global__ __launch_bounds__(256) void attn_sink_bwd_prep_kernel(BwdArgs a) {
   acc += __shfl_xor(acc, 4, 16);
   acc += __shfl_xor(acc, 2, 16);
   acc += __shfl_xor(acc, 1, 16);
-  if (row < rows && part == 0) {
-    const long long t = row / a.Hq;
-    const int h = (int)(row - t * a.Hq);
-    a.dws[(size_t)h * a.T + t] = acc;
+  if (h < a.Hq && t < a.T && part == 0) {
+    const size_t o = (size_t)h * a.T + t;
+    a.negd[o] = -acc;
+    a.nlse[o] = -a.lse[o] / a.scale;
   }
   // Clear the dSink partials (rows of the dq pass that exit early never write theirs).
   const long long nparts = (long long)a.Hq * a.n_slots;
@@ -73,58 +82,63 @@ __global__ __launch_bounds__(256) void attn_sink_bwd_prep_kernel(BwdArgs a) {
 // ------------------------------------------------------------------------------------------
 // 2. dK, dV: column-parallel over 64-key blocks.
 // ------------------------------------------------------------------------------------------
-constexpr int kKvSub = 32;                             // query rows per product block
-constexpr int kKvStageRows = 64;                       // query rows staged per step (2 blocks)
-constexpr int kKvNatElems = kKvStageRows * kLdsStride; // [query][d] tile
-// One stream's stage: Q and dO rows (natural layout), then LSE (log2 units) and D of those rows.
-constexpr int kKvStageBytes = 2 * kKvNatElems * 2 + 2 * kKvStageRows * 4;
-constexpr int kKvRedStride = kHeadDim + 4;             // fp32 reduction row
+constexpr int kKvSub = 32;                                        // query rows per product block
+constexpr int kKvRows = 64;                                       // query rows per step (2 blocks)
+constexpr int kKvRing = 2;                                        // LDS ring slots per head stream
+constexpr int kKvTileBytes = kKvRows * kHeadDim * 2;              // one 64 x 64 bf16 row tile
+constexpr int kKvSlotBytes = 2 * kKvTileBytes + 2 * kKvRows * 4;  // Q, dO, -LSE/scale, -D
+constexpr int kKvStreamBytes = kKvRing * kKvSlotBytes;
+constexpr int kKvRedStride = kHeadDim + 4;                        // fp32 row of the final sum
 
-template <int NS>  // head streams: 1 or 2 (waves = 2 * NS)
+// Chunk swizzle of a 128-byte LDS row: logical 16-byte chunk k of tile row r is stored in chunk
+// k ^ kv_swz(r). Over any 16 consecutive rows, rows of equal parity get distinct values (so the
+// 16-byte fragment reads of 16 rows, permuted by swap23, hit distinct banks), and rows r and r + 2
+// with r % 4 == 0 differ in bit 2 (so the transposing 8-byte reads of 4 consecutive rows x 32
+// columns do too). kv_swz(r + 16) == kv_swz(r).
+__device__ __forceinline__ int kv_swz(int r) {
+  const int x = (r >> 1) & 7;
+  return ((x & 1) << 2) | (x >> 1);
+}
+
+template <int NS>  // head streams per workgroup: 1 or 2 (waves = 2 key halves x NS)
 __global__ __launch_bounds__(128 * NS, 2) void attn_sink_bwd_dkdv_kernel(BwdArgs a) {
-  constexpr int NW = 2 * NS;
-  constexpr int NT = 64 * NW;
-  constexpr int kRR = kKvStageRows * 8 / NT;  // 16-byte pieces per thread and staged tile
-  static_assert(NT == NS * 2 * kKvStageRows, "one LSE or D value per thread and stage");
-  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * NS * kKvStageBytes];
-  static_assert(sizeof(smem) >= 4 * 32 * kKvRedStride * 4, "reduction buffer fits");
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[NS * kKvStreamBytes];
+  static_assert(sizeof(smem) >= (NS == 2 ? 2 * 2 * 32 * kKvRedStride * 4 : 0), "final sum fits");
+  static_assert(kKvRing == 2, "the waits below assume one step in flight");
 
-  // Block order: KV group fastest (consecutive ids land on different XCDs, each XCD keeps few
-  // groups' rows in its L2), then head half, sequence, and key block ascending: under a causal
-  // mask the first key blocks carry the most query rows, so the longest blocks start first and
-  // the short ones fill in as slots free up.
+  // Block order: KV group fastest (consecutive ids go to different XCDs, so each XCD works on
+  // few groups and their query rows stay in its L2), then head half, sequence, and key blocks
+  // ascending: under a causal mask the first key blocks see the most query rows, so the longest
+  // workgroups start first and the short ones fill in.
   const int bid = blockIdx.x;
   const int g = bid % a.Hkv;
   int rest = bid / a.Hkv;
   const int hh = rest % a.n_halves;
   rest /= a.n_halves;
   const int b = rest % a.B;
-  const int kb = rest / a.B;
+  const int kblk = (rest / a.B) * kKvKeysPerBlock;
   const int cs = a.cu[b];
   const int len = a.cu[b + 1] - cs;
-  const int kblk = kb * kKvKeysPerBlock;
-  if (kblk >= len) return;
+  if (kblk >= len) return;  // uniform over the workgroup
 
-  const int tid = threadIdx.x;
   const int wave = wave_id();
-  const int lane = tid & 63;
+  const int lane = threadIdx.x & 63;
   const int l32 = lane & 31;
   const int grp = lane >> 5;
   const int kh = wave & 1;        // key half
   const int st = wave >> 1;       // head stream
   const int k0 = kblk + 32 * kh;  // this wave's 32 keys
   const int heads_half = a.G / a.n_halves;
-  const int heads_per_stream = heads_half / NS;
-  const int h_base = g * a.G + hh * heads_half;  // stream s takes heads h_base + s + NS * j
+  const int hps = heads_half / NS;
+  const int h0 = g * a.G + hh * heads_half + st;  // stream st takes heads h0 + NS * j
 
-  // K^T and V^T as B operands (k = d, n = key): lane holds key k0 + l32, d = 16c + 8grp + (0..7).
+  // K^T and V^T as B operands (k = d, n = key): lane holds key k0 + l32, d = 16c + 8grp + 0..7.
   bf16x8 kf[4], vf[4];
-  const size_t kv_tok = (size_t)a.Hkv * kHeadDim;
   {
     const int key = min(k0 + l32, len - 1);  // keys past the end are masked
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      const size_t off = (size_t)(cs + key) * kv_tok + (size_t)g * kHeadDim + 16 * c + 8 * grp;
+      const size_t off = ((size_t)(cs + key) * a.Hkv + g) * kHeadDim + 16 * c + 8 * grp;
       kf[c] = load_bf16x8(a.k + off);
       vf[c] = load_bf16x8(a.v + off);
     }
@@ -132,179 +146,210 @@ __global__ __launch_bounds__(128 * NS, 2) void attn_sink_bwd_dkdv_kernel(BwdArgs
   f32x16 dk[2], dv[2];  // [d block], C layout of dK^T / dV^T (rows d, columns this wave's keys)
   dk[0] = dk[1] = dv[0] = dv[1] = zero_f32x16();
 
-  // Query rows that can see a key of [kblk, kblk + 64), in 64-row stages.
+  // Query rows that can see a key of [kblk, kblk + 64), in 32-row steps from the last backwards
+  // (every workgroup's causal range ends at the sequence end, so the workgroups of one KV group
+  // stream the same rows at about the same time and mostly hit in L2). Both key halves and both
+  // streams run the same number of steps, so one barrier per step serves the whole workgroup.
   const int kmax = min(len, kblk + kKvKeysPerBlock) - 1;
   const int i_begin = a.causal ? kblk : 0;
   const int i_end = a.window > 0 ? min(len, kmax + a.window) : len;  // exclusive
-  const int t_begin = i_begin / kKvStageRows;
-  const int n_t = (i_end + kKvStageRows - 1) / kKvStageRows - t_begin;
-  const int n_steps = heads_per_stream * n_t;
+  const int n_sub = (i_end - i_begin + kKvRows - 1) / kKvRows;
+  const int n_steps = hps * n_sub;
 
-  // Staging: per thread, row (tid >> 3) + (NT / 8) * rr, chunk (tid & 7) of each of the 2 * NS
-  // tiles (stream t >> 1, Q or dO by t & 1), plus one LSE or D value. Rows past the sequence end
-  // are clamped onto its last row (finite data; those rows are masked out).
-  bf16x8 pre[2 * NS][kRR];
-  float pre_ld = 0.0f;
-  auto stage_ptr = [&](int buf, int s) { return smem + (size_t)(buf * NS + s) * kKvStageBytes; };
-  const int prow = tid >> 3, pc8 = tid & 7;
-  auto prefetch = [&](int hj, int i0) {
+  // Each stream owns a ring of 3 slots; step s lives in slot s % 3. The two key halves of a
+  // stream split the copies of a step: half 0 copies the Q tile and the -LSE/scale, -D rows,
+  // half 1 the dO tile. Lane l of copy u fetches tile row 8u + l/8, logical chunk
+  // (l % 8) ^ kv_swz(row), which lands at physical chunk l % 8 of that row.
+  unsigned char* ring = smem + st * kKvStreamBytes;
+  const int qstride = a.Hq * kHeadDim;  // elements per token row of q / dout
+  const int crow = lane >> 3;
+  const int coff0 = crow * qstride + 8 * ((lane & 7) ^ kv_swz(crow));      // rows 8u + crow, u even
+  const int coff1 = crow * qstride + 8 * ((lane & 7) ^ kv_swz(8 + crow));  // u odd
+  auto issue = [&](int j, int t, int slot) {
+    const int h = h0 + NS * j;
+    const int i0 = i_begin + kKvRows * (n_sub - 1 - t);
+    unsigned char* dst = ring + slot * kKvSlotBytes + kh * kKvTileBytes;
+    const __bf16* src = (kh ? a.dout : a.q) + ((size_t)(cs + i0) * a.Hq + h) * kHeadDim;
+    if (i0 + kKvRows <= len) {
 #pragma unroll
-    for (int t = 0; t < 2 * NS; ++t) {
-      const int h = h_base + (t >> 1) + NS * hj;
-      const __bf16* base = ((t & 1) ? a.dout : a.q) + ((size_t)cs * a.Hq + h) * kHeadDim;
+      for (int u = 0; u < kKvTileBytes / 1024; ++u) {
+        dma16(src + 8 * u * qstride + ((u & 1) ? coff1 : coff0), dst + 1024 * u);
+      }
+    } else {  // last, partial tile: rows past the end repeat the last row (they are masked)
 #pragma unroll
-      for (int rr = 0; rr < kRR; ++rr) {
-        const int qi = min(i0 + prow + (NT / 8) * rr, len - 1);
-        pre[t][rr] = load_bf16x8(base + (unsigned)(qi * a.Hq * kHeadDim + 8 * pc8));
+      for (int u = 0; u < kKvTileBytes / 1024; ++u) {
+        const int r = 8 * u + crow;
+        dma16(src + (min(i0 + r, len - 1) - i0) * qstride + 8 * ((lane & 7) ^ kv_swz(r)), dst + 1024 * u);
       }
     }
-    {  // exactly one LSE or D value per thread (NT == NS * 2 * kKvStageRows)
-      const int s = tid / (2 * kKvStageRows);
-      const int which = (tid / kKvStageRows) & 1;
-      const int h = h_base + s + NS * hj;
-      const int qi = min(i0 + (tid & (kKvStageRows - 1)), len - 1);
-      pre_ld = (which ? a.dws : a.lse)[(size_t)h * a.T + cs + qi];  // consumed only in commit
+    if (kh == 0) {  // -LSE/scale rows, then -D rows (64 each)
+      const float* nl = a.nlse + (size_t)h * a.T + cs;
+      const float* nd = a.negd + (size_t)h * a.T + cs;
+      dma4(nl + min(i0 + lane, len - 1), ring + slot * kKvSlotBytes + 2 * kKvTileBytes);
+      dma4(nd + min(i0 + lane, len - 1), ring + slot * kKvSlotBytes + 2 * kKvTileBytes + 4 * kKvRows);
     }
   };
-  auto commit = [&](int buf) {
+  auto wait_own_step = [&]() { wait_vmcnt<0>(); };  // this wave's copies of the current step
+
+  // Per-lane LDS byte offsets within a tile. Fragment reads (A operands, k = d): row
+  // swap23(l32), logical chunk 2c + grp.
+  const int ar = swap23(l32);
+  int aoff[4];
 #pragma unroll
-    for (int t = 0; t < 2 * NS; ++t) {
-      __bf16* nat = reinterpret_cast<__bf16*>(stage_ptr(buf, t >> 1)) + (t & 1) * kKvNatElems;
+  for (int c = 0; c < 4; ++c) aoff[c] = ar * 128 + (((2 * c + grp) ^ kv_swz(ar)) << 4);
+  // Transposing reads (A operands, k = query): rows 8grp + s/4 (+4), logical columns
+  // m0 + 16*((l>>4)&1) + 4*(s%4), s = l % 16; m0 = 32 * db; rows +16 for the second query half.
+  const int s16 = lane & 15;
+  const int trow = 8 * grp + (s16 >> 2);
+  const int tch = 2 * ((lane >> 4) & 1) + ((s16 & 3) >> 1);
+  int toff[2][2];  // [d block][+0 / +4 rows]
 #pragma unroll
-      for (int rr = 0; rr < kRR; ++rr) {
-        *reinterpret_cast<bf16x8*>(&nat[(prow + (NT / 8) * rr) * kLdsStride + 8 * pc8]) = pre[t][rr];
-      }
+  for (int db = 0; db < 2; ++db) {
+#pragma unroll
+    for (int hi = 0; hi < 2; ++hi) {
+      const int r = trow + 4 * hi;
+      toff[db][hi] = r * 128 + (((4 * db + tch) ^ kv_swz(r)) << 4) + 8 * (s16 & 1);
     }
-    {
-      float* f = reinterpret_cast<float*>(stage_ptr(buf, tid / (2 * kKvStageRows)) + 2 * kKvNatElems * 2);
-      f[tid & (2 * kKvStageRows - 1)] = ((tid / kKvStageRows) & 1) ? pre_ld : pre_ld * kLog2e;  // LSE in log2 units
+  }
+  // Transposed operands (see load_tr8): Q^T (tile 0) or dO^T (tile 1) rows d = 32db + l32, k
+  // slots = query rows 16*half + 8grp + 0..7 of the slot at LDS address `slot_lds`.
+  auto tr8 = [&](unsigned slot_lds, auto tile_tag, int db, auto half_tag, u32x2& lo, u32x2& hi) {
+    constexpr int OFF = decltype(tile_tag)::value * kKvTileBytes + 2048 * decltype(half_tag)::value;
+    lo = ds_read_tr16_b64_asm<OFF>(slot_lds + toff[db][0]);
+    hi = ds_read_tr16_b64_asm<OFF>(slot_lds + toff[db][1]);
+  };
+  auto tr_all = [&](unsigned slot_lds, u32x2 (&tr)[16]) {  // [d block][query half][Q / dO][lo / hi]
+#pragma unroll
+    for (int db = 0; db < 2; ++db) {
+      tr8(slot_lds, std::integral_constant<int, 0>(), db, std::integral_constant<int, 0>(), tr[8 * db], tr[8 * db + 1]);
+      tr8(slot_lds, std::integral_constant<int, 1>(), db, std::integral_constant<int, 0>(), tr[8 * db + 2], tr[8 * db + 3]);
+      tr8(slot_lds, std::integral_constant<int, 0>(), db, std::integral_constant<int, 1>(), tr[8 * db + 4], tr[8 * db + 5]);
+      tr8(slot_lds, std::integral_constant<int, 1>(), db, std::integral_constant<int, 1>(), tr[8 * db + 6], tr[8 * db + 7]);
     }
   };
+  const unsigned ring_lds = lds_addr(ring);
 
-  // Stages run from the last query rows backwards: every workgroup's causal range ends at the
-  // sequence end, so workgroups of one KV group stream the same rows at about the same time and
-  // mostly hit in L2.
-  auto stage_row = [&](int t) { return (t_begin + n_t - 1 - t) * kKvStageRows; };
-  int hj = 0, ti = 0;  // current step = (head index within the stream, stage index)
-  // Unconditional (n_steps > 0 here): every load issued so far, including K and V, is complete
-  // on every path into the loop, so the loop only waits on its prefetch when committing it.
-  prefetch(0, stage_row(0));
-  commit(0);
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): nothing issued before the loop stays in flight
-  __syncthreads();
-
-  for (int step = 0; step < n_steps; ++step) {
-    const int cur = step & 1;
-    const bool has_next = step + 1 < n_steps;
-    const int hj_n = ti + 1 < n_t ? hj : hj + 1;
-    const int ti_n = ti + 1 < n_t ? ti + 1 : 0;
-    if (has_next) prefetch(hj_n, stage_row(ti_n));
-
-    const unsigned char* sp = stage_ptr(cur, st);
-    const __bf16* qn = reinterpret_cast<const __bf16*>(sp);
-    const __bf16* dn = qn + kKvNatElems;
-    const float* lsep = reinterpret_cast<const float*>(sp + 2 * kKvNatElems * 2);
-    const float* ddp = lsep + kKvStageRows;
-
-#pragma unroll
-    for (int sub = 0; sub < kKvStageRows / kKvSub; ++sub) {
-      const int i0 = stage_row(ti) + kKvSub * sub;
-      // Skip blocks in which no (query, key) pair of this wave is visible (wave-uniform).
-      const bool live = (!a.causal || k0 <= i0 + kKvSub - 1) && (a.window <= 0 || i0 <= k0 + 30 + a.window) &&
-                        k0 < len && i0 < len;
-      if (!live) continue;
-      const __bf16* qs = qn + kKvSub * sub * kLdsStride;
-      const __bf16* ds = dn + kKvSub * sub * kLdsStride;
-
-      // S = Q K^T and dP = dO V^T: A rows hold query swap23(r); C: lane = key, registers = queries.
-      f32x16 s = zero_f32x16(), dp = zero_f32x16();
+  // One step: S' = Q K^T - LSE/scale and dP' = dO V^T - D for the 32 rows x 32 keys (the row
+  // values preloaded as the accumulators; C: lane = key, registers = rows 16(i/8) + 8grp + i%8),
+  // P = exp2(S' * scale * log2e), dS = P dP'; then dV^T += dO^T P and dK^T += Q^T dS. When some
+  // probability of the step exceeds kSplitThreshold, the step runs a second time in residual
+  // mode, multiplying the bf16 rounding residuals of P and dS instead (same instructions, so the
+  // accumulators are not split over two code paths).
+  auto step = [&](int si, int sub, int i0, bool need_mask) {
+    const unsigned char* slot = ring + si * kKvSlotBytes + 4096 * sub;  // 32-row block `sub` of the tiles
+    const unsigned slot_lds = ring_lds + si * kKvSlotBytes + 4096 * sub;
+    const float* lp = reinterpret_cast<const float*>(ring + si * kKvSlotBytes + 2 * kKvTileBytes) + kKvSub * sub;
+    bool residual = false;
+    bool again;
+    do {
+      f32x16 sc = load_rows16(lp, grp);
+      f32x16 dp = load_rows16(lp + kKvRows, grp);  // -D rows follow the 64 -LSE/scale rows
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        const int off = swap23(l32) * kLdsStride + 16 * c + 8 * grp;
-        s = mfma_32x32x16(load_bf16x8(&qs[off]), kf[c], s);
-        dp = mfma_32x32x16(load_bf16x8(&ds[off]), vf[c], dp);
+        sc = mfma_32x32x16(*reinterpret_cast<const bf16x8*>(slot + aoff[c]), kf[c], sc);
+        dp = mfma_32x32x16(*reinterpret_cast<const bf16x8*>(slot + kKvTileBytes + aoff[c]), vf[c], dp);
       }
-      // LSE / D of the 16 query rows held in this lane's registers: rows 16(i/8) + 8grp + (i%8).
-      const f32x4* l4 = reinterpret_cast<const f32x4*>(lsep + kKvSub * sub);
-      const f32x4* d4 = reinterpret_cast<const f32x4*>(ddp + kKvSub * sub);
-      const f32x4 la = l4[2 * grp], lb = l4[2 * grp + 1], lc = l4[4 + 2 * grp], ld = l4[4 + 2 * grp + 1];
-      const f32x4 da_ = d4[2 * grp], db_ = d4[2 * grp + 1], dc = d4[4 + 2 * grp], dd_ = d4[4 + 2 * grp + 1];
-      const float lse2[16] = {la[0], la[1], la[2], la[3], lb[0], lb[1], lb[2], lb[3],
-                              lc[0], lc[1], lc[2], lc[3], ld[0], ld[1], ld[2], ld[3]};
-      const float dd[16] = {da_[0], da_[1], da_[2], da_[3], db_[0], db_[1], db_[2], db_[3],
-                            dc[0], dc[1], dc[2], dc[3], dd_[0], dd_[1], dd_[2], dd_[3]};
-
-      const bool need_mask = (i0 + kKvSub > len) || (k0 + 32 > len) || (a.causal && k0 + 31 > i0) ||
-                             (a.window > 0 && k0 <= i0 + kKvSub - 1 - a.window);
-      if (need_mask) {  // wave-uniform: only diagonal, window-edge and ragged blocks
-        const int kj = k0 + l32;
+      u32x2 tr[16];
+      tr_all(slot_lds, tr);
+      if (need_mask) {
+        // Row of register i: i0 + 8grp + r_i with r_i = 16(i/8) + i%8. Visible iff the row and
+        // the key exist, the key is not after the row (causal) and the row is less than
+        // `window` rows after the key. (The empty asm keeps the comparisons in this branch.)
+        int kj = k0 + l32;
+        asm volatile("" : "+v"(kj));
+        const int dq = i0 + 8 * grp - kj;     // row - key for r_i = 0
+        const int rlim = len - i0 - 8 * grp;  // row exists iff r_i < rlim
+        const bool key_ok = kj < len;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const int qi = i0 + c_row(i, grp);
-          if (!(qi < len && visible(qi, kj, len, a.causal, a.window))) s[i] = kNegInf;
+          const int r = 16 * (i >> 3) + (i & 7);
+          const int t = dq + r;
+          const bool vis = key_ok & (r < rlim) & ((a.causal == 0) | (t >= 0)) & ((a.window <= 0) | (t < a.window));
+          sc[i] = vis ? sc[i] : kNegInf;
         }
       }
       float pmax = 0.0f;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const float p = fast_exp2(__builtin_fmaf(s[i], a.scale_log2, -lse2[i]));
+        const float p = fast_exp2(sc[i] * a.scale_log2);
         pmax = fmaxf(pmax, p);
-        s[i] = p;
-        dp[i] = p * (dp[i] - dd[i]);
+        sc[i] = p;
+        dp[i] *= p;
       }
-      const bf16x8 pb0 = pack8(s, 0), pb1 = pack8(s, 1);
-      const bf16x8 ds0 = pack8(dp, 0), ds1 = pack8(dp, 1);
-      // Large probabilities: add the products of the bf16 rounding residuals of P and dS.
-      const bool split = wave_any(pmax > kSplitThreshold);
-
-      // dV^T += dO^T P and dK^T += Q^T dS over the block's 32 queries; the transposed operands
-      // come straight from the natural tiles through transposing LDS loads.
+      bf16x8 pb0 = pack8(sc, 0), pb1 = pack8(sc, 1);
+      bf16x8 sb0 = pack8(dp, 0), sb1 = pack8(dp, 1);
+      if (residual) {
+        pb0 = residual8(sc, 0, pb0);
+        pb1 = residual8(sc, 1, pb1);
+        sb0 = residual8(dp, 0, sb0);
+        sb1 = residual8(dp, 1, sb1);
+      }
+      wait_lds_into(tr);
 #pragma unroll
       for (int db = 0; db < 2; ++db) {
-        const bf16x8 doa0 = load_tr8(ds, kLdsStride, 0, 32 * db), doa1 = load_tr8(ds, kLdsStride, 16, 32 * db);
-        const bf16x8 qta0 = load_tr8(qs, kLdsStride, 0, 32 * db), qta1 = load_tr8(qs, kLdsStride, 16, 32 * db);
-        dv[db] = mfma_32x32x16(doa0, pb0, dv[db]);
-        dv[db] = mfma_32x32x16(doa1, pb1, dv[db]);
-        dk[db] = mfma_32x32x16(qta0, ds0, dk[db]);
-        dk[db] = mfma_32x32x16(qta1, ds1, dk[db]);
-        if (split) {
-          // The opaque copies of the packed values keep the residual arithmetic inside this
-          // rarely taken branch (it depends on them), without copying the fp32 tiles.
-          bf16x8 h0 = pb0, h1 = pb1, e0 = ds0, e1 = ds1;
-          opaque(h0);
-          opaque(h1);
-          opaque(e0);
-          opaque(e1);
-          dv[db] = mfma_32x32x16(doa0, residual8(s, 0, h0), dv[db]);
-          dv[db] = mfma_32x32x16(doa1, residual8(s, 1, h1), dv[db]);
-          dk[db] = mfma_32x32x16(qta0, residual8(dp, 0, e0), dk[db]);
-          dk[db] = mfma_32x32x16(qta1, residual8(dp, 1, e1), dk[db]);
-        }
+        const u32x2* t = tr + 8 * db;
+        dv[db] = mfma_32x32x16(join_tr(t[2], t[3]), pb0, dv[db]);
+        dv[db] = mfma_32x32x16(join_tr(t[6], t[7]), pb1, dv[db]);
+        dk[db] = mfma_32x32x16(join_tr(t[0], t[1]), sb0, dk[db]);
+        dk[db] = mfma_32x32x16(join_tr(t[4], t[5]), sb1, dk[db]);
+      }
+      again = !residual && wave_any(pmax > kSplitThreshold);
+      residual = true;
+    } while (again);
+  };
+
+  int ij = 0, it = 0;  // (head, tile) of the next step to issue
+  auto advance = [&](int& j, int& t) {
+    if (++t == n_sub) {
+      t = 0;
+      ++j;
+    }
+  };
+  issue(ij, it, 0);
+  advance(ij, it);
+  int ct = 0;  // tile index of the current step
+  for (int s = 0; s < n_steps; ++s) {
+    wait_own_step();
+    // Both halves of step s have landed, and every wave is done with step s - 1, whose slot
+    // receives step s + 1.
+    __syncthreads();
+    if (s + 1 < n_steps) {
+      issue(ij, it, (s + 1) % kKvRing);
+      advance(ij, it);
+    }
+#pragma unroll
+    for (int sub = 0; sub < kKvRows / kKvSub; ++sub) {
+      const int i0 = i_begin + kKvRows * (n_sub - 1 - ct) + kKvSub * sub;
+      const bool live = (!a.causal || k0 <= i0 + kKvSub - 1) && (a.window <= 0 || i0 <= k0 + 31 + a.window - 1) &&
+                        k0 < len && i0 < len;
+      if (live) {  // wave-uniform: skip blocks in which none of this wave's pairs is visible
+        const bool need_mask = (i0 + kKvSub > len) || (k0 + 32 > len) || (a.causal && k0 + 31 > i0) ||
+                               (a.window > 0 && k0 <= i0 + kKvSub - 1 - a.window);
+        step(s % kKvRing, sub, i0, need_mask);
       }
     }
-
-    if (has_next) commit(cur ^ 1);
-    hj = hj_n;
-    ti = ti_n;
-    __syncthreads();
+    if (++ct == n_sub) ct = 0;
   }
 
   // Add the second stream's partial sums (LDS, [key][d] fp32 per key half), then store rows.
-  float* red = reinterpret_cast<float*>(smem) + kh * 32 * kKvRedStride;
-  if (NS == 2 && st == 1) {
+  float* red = reinterpret_cast<float*>(smem) + kh * 2 * 32 * kKvRedStride;
+  if (NS == 2) {
+    __syncthreads();  // every wave is done with its ring
+    if (st == 1) {
 #pragma unroll
-    for (int db = 0; db < 2; ++db) {
+      for (int db = 0; db < 2; ++db) {
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const int d = 32 * db + 8 * r4 + 4 * grp;
-        *reinterpret_cast<f32x4*>(&red[l32 * kKvRedStride + d]) =
-            (f32x4){dk[db][4 * r4], dk[db][4 * r4 + 1], dk[db][4 * r4 + 2], dk[db][4 * r4 + 3]};
-        *reinterpret_cast<f32x4*>(&red[(64 + l32) * kKvRedStride + d]) =
-            (f32x4){dv[db][4 * r4], dv[db][4 * r4 + 1], dv[db][4 * r4 + 2], dv[db][4 * r4 + 3]};
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int d = 32 * db + 8 * r4 + 4 * grp;
+          *reinterpret_cast<f32x4*>(&red[l32 * kKvRedStride + d]) =
+              (f32x4){dk[db][4 * r4], dk[db][4 * r4 + 1], dk[db][4 * r4 + 2], dk[db][4 * r4 + 3]};
+          *reinterpret_cast<f32x4*>(&red[(32 + l32) * kKvRedStride + d]) =
+              (f32x4){dv[db][4 * r4], dv[db][4 * r4 + 1], dv[db][4 * r4 + 2], dv[db][4 * r4 + 3]};
+        }
       }
     }
+    __syncthreads();
   }
-  if (NS == 2) __syncthreads();
   if (st == 0) {
     const int key = k0 + l32;
     if (key < len) {
@@ -321,7 +366,7 @@ __global__ __launch_bounds__(128 * NS, 2) void attn_sink_bwd_dkdv_kernel(BwdArgs
           f32x4 vv = {dv[db][4 * r4], dv[db][4 * r4 + 1], dv[db][4 * r4 + 2], dv[db][4 * r4 + 3]};
           if (NS == 2) {
             kv += *reinterpret_cast<const f32x4*>(&red[l32 * kKvRedStride + d]);
-            vv += *reinterpret_cast<const f32x4*>(&red[(64 + l32) * kKvRedStride + d]);
+            vv += *reinterpret_cast<const f32x4*>(&red[(32 + l32) * kKvRedStride + d]);
           }
           *reinterpret_cast<f32x4*>(dkrow + d) = kv;
           *reinterpret_cast<f32x4*>(dvrow + d) = vv;
@@ -394,8 +439,8 @@ __global__ __launch_bounds__(64 * HPW, 2) void attn_sink_bwd_dq_kernel(BwdArgs a
     qf[c] = load_bf16x8(a.q + off);
     df[c] = load_bf16x8(a.dout + off);
   }
-  const float lse2 = a.lse[(size_t)h * a.T + cs + qc] * kLog2e;
-  const float dd = a.dws[(size_t)h * a.T + cs + qc];
+  const float lse2 = -a.nlse[(size_t)h * a.T + cs + qc] * a.scale_log2;  // LSE_i * log2(e)
+  const float nd = a.negd[(size_t)h * a.T + cs + qc];  // -D_i
   float dsum = 0.0f;
   f32x16 acc[2];  // dQ^T, [d block]
   acc[0] = acc[1] = zero_f32x16();
@@ -484,7 +529,7 @@ __global__ __launch_bounds__(64 * HPW, 2) void attn_sink_bwd_dq_kernel(BwdArgs a
         pmax = fmaxf(pmax, p);
         const float pdp = p * dp[mb][i];
         part += pdp;
-        dp[mb][i] = __builtin_fmaf(-p, dd, pdp);
+        dp[mb][i] = __builtin_fmaf(p, nd, pdp);
       }
       dsb[mb][0] = pack8(dp[mb], 0);
       dsb[mb][1] = pack8(dp[mb], 1);
@@ -554,10 +599,20 @@ __global__ __launch_bounds__(64) void attn_sink_bwd_dsink_kernel(BwdArgs a) {
 }  // namespace
 
 hipError_t launch_bwd_prep(const BwdArgs& a, hipStream_t stream) {
-  const long long rows = (long long)a.T * a.Hq;
-  long long nblocks = (rows + 15) / 16;
+  long long nblocks = (long long)a.Hq * ((a.T + 15) / 16);
   if (nblocks < 1) nblocks = 1;  // still clears the dSink partials when T = 0
   hipLaunchKernelGGL(attn_sink_bwd_prep_kernel, dim3((unsigned)nblocks), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream) {
+  const long long nblocks = (long long)a.n_kblocks * a.B * a.Hkv * a.n_halves;
+  if (nblocks <= 0) return hipSuccess;
+  if (a.kv_streams == 2) {
+    hipLaunchKernelGGL(attn_sink_bwd_dkdv_kernel<2>, dim3((unsigned)nblocks), dim3(256), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL(attn_sink_bwd_dkdv_kernel<1>, dim3((unsigned)nblocks), dim3(128), 0, stream, a);
+  }
   return hipGetLastError();
 }
 
@@ -567,17 +622,6 @@ hipError_t launch_bwd_dkdv_sum(const BwdArgs& a, hipStream_t stream) {
   long long nblocks = (n4 + 255) / 256;
   if (nblocks > 8192) nblocks = 8192;
   hipLaunchKernelGGL(attn_sink_bwd_dkdv_sum_kernel, dim3((unsigned)nblocks), dim3(256), 0, stream, a);
-  return hipGetLastError();
-}
-
-hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream) {
-  const long long nblocks = (long long)a.n_kblocks * a.B * a.Hkv * a.n_halves;
-  if (nblocks <= 0) return hipSuccess;
-  if (a.kv_waves == 4) {
-    hipLaunchKernelGGL(attn_sink_bwd_dkdv_kernel<2>, dim3((unsigned)nblocks), dim3(256), 0, stream, a);
-  } else {
-    hipLaunchKernelGGL(attn_sink_bwd_dkdv_kernel<1>, dim3((unsigned)nblocks), dim3(128), 0, stream, a);
-  }
   return hipGetLastError();
 }
 

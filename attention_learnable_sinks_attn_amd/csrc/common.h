@@ -137,6 +137,64 @@ __device__ __forceinline__ void opaque(bf16x8& x) {
   x = __builtin_bit_cast(bf16x8, u);
 }
 
+// Direct global -> LDS copies (gfx950): lane l's 16 (or 4) bytes at `src` land at LDS byte
+// offset lds_dst + 16 * l (or 4 * l). `lds_dst` must be wave-uniform. The copy completes
+// asynchronously; it is counted by vmcnt like any other vector memory load.
+typedef __attribute__((address_space(3))) void lds_void;
+__device__ __forceinline__ void dma16(const void* src, void* lds_dst) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void*)lds_dst, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const void* src, void* lds_dst) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void*)lds_dst, 4, 0, 0);
+}
+
+// s_waitcnt vmcnt(N) (expcnt and lgkmcnt left unconstrained).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit counter");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+// LDS byte address of a pointer into __shared__ memory.
+__device__ __forceinline__ unsigned lds_addr(const void* p) {
+  return (unsigned)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// ds_read_b64_tr_b16 (see load_tr8) issued through inline asm. The compiler makes every
+// transposing LDS read it knows about wait for all outstanding direct global->LDS copies
+// (vmcnt(0)), which would serialise a kernel that keeps copies in flight into other LDS slots.
+// The result is not tracked either: wait_lds_into must follow before any use.
+template <int OFF>
+__device__ __forceinline__ u32x2 ds_read_tr16_b64_asm(unsigned addr) {
+  static_assert(OFF >= 0 && OFF < 65536, "16-bit DS offset");
+  u32x2 r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+  return r;
+}
+// lgkmcnt(0), tied to the registers of 16 untracked LDS reads so that no use moves above it.
+__device__ __forceinline__ void wait_lds_into(u32x2 (&t)[16]) {
+  asm volatile("s_waitcnt lgkmcnt(0)"
+               : "+v"(t[0]), "+v"(t[1]), "+v"(t[2]), "+v"(t[3]), "+v"(t[4]), "+v"(t[5]), "+v"(t[6]), "+v"(t[7]),
+                 "+v"(t[8]), "+v"(t[9]), "+v"(t[10]), "+v"(t[11]), "+v"(t[12]), "+v"(t[13]), "+v"(t[14]),
+                 "+v"(t[15]));
+}
+__device__ __forceinline__ bf16x8 join_tr(const u32x2& lo, const u32x2& hi) {
+  return __builtin_bit_cast(bf16x8, (u32x4){lo[0], lo[1], hi[0], hi[1]});
+}
+
+// The 16 fp32 values of rows 16(i/8) + 8g + i%8, i = 0..15 (the rows a C register block of lane
+// group g holds after a swap23 load), from a row vector in LDS.
+__device__ __forceinline__ f32x16 load_rows16(const float* p, int g) {
+  const f32x4 a = *reinterpret_cast<const f32x4*>(p + 8 * g);
+  const f32x4 b = *reinterpret_cast<const f32x4*>(p + 8 * g + 4);
+  const f32x4 c = *reinterpret_cast<const f32x4*>(p + 16 + 8 * g);
+  const f32x4 d = *reinterpret_cast<const f32x4*>(p + 20 + 8 * g);
+  return (f32x16){a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3], c[0], c[1], c[2], c[3], d[0], d[1], d[2], d[3]};
+}
+
 // Work descriptors (filled on the host).
 struct FwdArgs {
   const __bf16* q;
@@ -166,14 +224,15 @@ struct BwdArgs {
   float* dk;
   float* dv;
   float* dsinks;
-  float* dws;        // D_i = rowsum(dO * O), [Hq, T]
+  float* nlse;       // workspace: -LSE_i / scale (score units), [Hq, T]
+  float* negd;       // workspace: -D_i = -rowsum(dO * O), [Hq, T]
   float* dsink_part; // per (head, row-block slot) partial sums of P_sink * D~, [Hq, n_slots]
   float* dkv_part;   // dK / dV partial sums per head half: [2][n_halves][T][Hkv][64] (unscaled)
   int n_slots;
   int n_halves;      // query-head halves of a KV group processed by separate dK/dV workgroups
   int T, B, Hq, Hkv, G;
   int hpw;            // dQ kernel: query heads per workgroup
-  int kv_waves;       // dK/dV kernel: waves per workgroup (2 key halves x head streams)
+  int kv_streams;     // dK/dV kernel: head streams per workgroup (1 or 2; waves = 2 x streams)
   int n_qblocks;      // dQ kernel grid rows
   int n_kblocks;      // dK/dV kernel grid rows
   int causal, window;

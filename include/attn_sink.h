@@ -57,8 +57,8 @@ enum {
   ATTN_SINK_OK = 0,
   ATTN_SINK_ERR_NULL_PTR = -1,    /* a required pointer (or the shape struct) is NULL */
   ATTN_SINK_ERR_BAD_SHAPE = -2,   /* T < 0, B < 1, Hq < 1, Hkv < 1, Hq % Hkv != 0, max_seqlen < 0
-                                     or max_seqlen > T, or max_seqlen * Hq * 64 >= 2^31 (offsets
-                                     inside one sequence are 32-bit) */
+                                     or max_seqlen > T, max_seqlen * Hq * 64 >= 2^31 (offsets
+                                     inside one sequence are 32-bit), or T * Hq > 2^34 (grid size) */
   ATTN_SINK_ERR_UNSUPPORTED = -3, /* head_dim != 64 or out_dtype != ATTN_SINK_F32 */
   ATTN_SINK_ERR_BAD_WINDOW = -4,  /* window > 0 without causal */
   ATTN_SINK_ERR_WORKSPACE = -5,   /* workspace NULL or smaller than attn_sink_bwd_workspace_bytes() */
@@ -90,8 +90,10 @@ int attn_sink_fwd(const void* q, const void* k, const void* v, const float* sink
                   hipStream_t stream);
 
 /*
- * Bytes of device workspace attn_sink_bwd needs for this shape (D_i rows and per-block dSink
- * partial sums, 256-byte aligned). Returns 0 if `shape` is NULL or invalid.
+ * Bytes of device workspace attn_sink_bwd needs for this shape: -LSE_i/scale and -D_i for every
+ * (head, row), one dSink partial sum per (head, 32-row block), and fp32 dK/dV partial sums for
+ * each half of a KV group's query heads (2 * halves * T * Hkv * 64 floats); each region 256-byte
+ * aligned. Returns 0 if `shape` is NULL or invalid.
  */
 size_t attn_sink_bwd_workspace_bytes(const attn_sink_shape* shape);
 

@@ -113,8 +113,9 @@ def test_workspace_size_formula():
     lib = asa.load_library()
     s = shape(T=4096, maxlen=4096, hq=64, hkv=8)
     need = lib.attn_sink_bwd_workspace_bytes(ctypes.byref(s))
-    # D_i for every (head, row) plus one partial dSink per (head, 64-row block slot)
-    assert need >= 64 * 4096 * 4 + 64 * (4096 // 64 + 1 + 1) * 4
+    # -LSE/scale and -D_i for every (head, row), one dSink partial per (head, 32-row block slot), and
+    # fp32 dK/dV partials for the two query-head halves of each KV group; each region 256-byte aligned
+    assert need == 2 * 64 * 4096 * 4 + 64 * (4096 // 32 + 1 + 1) * 4 + 2 * 2 * 4096 * 8 * 64 * 4
     assert need % 256 == 0
     assert lib.attn_sink_bwd_workspace_bytes(None) == 0
     assert lib.attn_sink_bwd_workspace_bytes(ctypes.byref(shape(d=16))) == 0

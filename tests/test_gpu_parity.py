@@ -93,6 +93,8 @@ SMALL_CASES = {
     "sinks_x3": ((300,), 4, 1, True, 0, {"sink_scale": 3.0}),
     "scale_0p07": ((140,), 2, 2, True, 0, {"scale": 0.07}),
     "exact_tiles": ((256, 128), 8, 8, True, 64, {}),
+    "gqa3_causal": ((200, 70), 6, 2, True, 0, {}),
+    "gqa6_window50": ((180,), 6, 1, True, 50, {}),
 }
 
 
