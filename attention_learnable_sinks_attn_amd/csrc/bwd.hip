@@ -26,8 +26,9 @@
 //            (launched longest first) they keep two per CU busy under a causal mask.
 //  2b. dkdv_sum: dK = scale * (sum of the halves), dV = sum of the halves.
 //  3. dq:    row-parallel. A workgroup owns 32 query rows of `hpw` heads of one group (one head
-//            per wave) and streams double-buffered 64-key tiles of K and V through LDS (K^T
-//            operands come from transposing LDS loads of the K tile).
+//            per wave) and streams 64-key tiles of K and V through a 3-slot LDS ring filled by
+//            direct copies two tiles ahead (swizzled like the dkdv tiles; K^T operands come from
+//            transposing LDS loads of the K tile).
 //            Besides dQ it accumulates D~_i = sum_j P_ij dP_ij from the fp32 P and dP it already
 //            holds and writes sum_i P_{i,h} D~_i for its rows. D~ equals D mathematically but
 //            does not carry the bf16 rounding of the forward's P.V product, which matters
@@ -397,15 +398,15 @@ __global__ __launch_bounds__(256) void attn_sink_bwd_dkdv_sum_kernel(BwdArgs a) 
 // 3. dQ and the dSink partials: row-parallel over 32-row query blocks.
 // ------------------------------------------------------------------------------------------
 constexpr int kDqTileKeys = 64;
-constexpr int kDqTileElems = kDqTileKeys * kLdsStride;
+constexpr int kDqTileBytes = kDqTileKeys * kHeadDim * 2;  // one swizzled 64-key tile (K or V)
+constexpr int kDqSlotBytes = 2 * kDqTileBytes;             // K tile, then V tile
+constexpr int kDqRing = 3;                                 // LDS ring slots (two tiles in flight)
 
 template <int HPW>
 __global__ __launch_bounds__(64 * HPW, 2) void attn_sink_bwd_dq_kernel(BwdArgs a) {
-  constexpr int NT = 64 * HPW;
   constexpr int kRows = kDqRowsPerWave;
-  constexpr int KU = kDqTileKeys * 8 / NT;  // 16-byte K (and V) pieces per thread and tile
-  __shared__ __attribute__((aligned(16))) __bf16 k_lds[2 * kDqTileElems];
-  __shared__ __attribute__((aligned(16))) __bf16 v_lds[2 * kDqTileElems];
+  constexpr int CPW = 2 * (kDqTileBytes / 1024) / HPW;  // copies per wave and tile (K and V)
+  __shared__ __attribute__((aligned(1024))) unsigned char ring[kDqRing * kDqSlotBytes];
 
   const int n_hs = a.Hq / HPW;
   const int bid = blockIdx.x;
@@ -420,9 +421,8 @@ __global__ __launch_bounds__(64 * HPW, 2) void attn_sink_bwd_dq_kernel(BwdArgs a
   const int q0 = qb * kRows;
   if (q0 >= len) return;
 
-  const int tid = threadIdx.x;
   const int wave = wave_id();
-  const int lane = tid & 63;
+  const int lane = threadIdx.x & 63;
   const int l32 = lane & 31;
   const int grp = lane >> 5;
   const int h = hs * HPW + wave;
@@ -440,7 +440,7 @@ __global__ __launch_bounds__(64 * HPW, 2) void attn_sink_bwd_dq_kernel(BwdArgs a
     df[c] = load_bf16x8(a.dout + off);
   }
   const float lse2 = -a.nlse[(size_t)h * a.T + cs + qc] * a.scale_log2;  // LSE_i * log2(e)
-  const float nd = a.negd[(size_t)h * a.T + cs + qc];  // -D_i
+  const float nd = a.negd[(size_t)h * a.T + cs + qc];                   // -D_i
   float dsum = 0.0f;
   f32x16 acc[2];  // dQ^T, [d block]
   acc[0] = acc[1] = zero_f32x16();
@@ -449,48 +449,48 @@ __global__ __launch_bounds__(64 * HPW, 2) void attn_sink_bwd_dq_kernel(BwdArgs a
   const int kbeg = a.window > 0 ? max(0, q0 - a.window + 1) : 0;
   const int kt_begin = kbeg / kDqTileKeys;
   const int kt_end = (kend + kDqTileKeys - 1) / kDqTileKeys;
-  const size_t tok_stride = (size_t)a.Hkv * kHeadDim;
-  const __bf16* kbase = a.k + (size_t)cs * tok_stride + (size_t)g * kHeadDim;
-  const __bf16* vbase = a.v + (size_t)cs * tok_stride + (size_t)g * kHeadDim;
+  const int kv_stride = a.Hkv * kHeadDim;
+  const __bf16* kbase = a.k + (size_t)cs * kv_stride + (size_t)g * kHeadDim;
+  const __bf16* vbase = a.v + (size_t)cs * kv_stride + (size_t)g * kHeadDim;
 
-  // K and V tiles in natural [key][d] layout; K^T operands come from transposing LDS loads.
-  // Keys past the sequence end are clamped onto its last key (finite data; they are masked).
-  bf16x8 kpre[KU], vpre[KU];
-  auto prefetch = [&](int kt) {
-    const int kk = kt * kDqTileKeys;
+  // K and V tiles of 64 keys, swizzled (see tile_swz), in a 3-slot ring filled by direct
+  // global->LDS copies issued two tiles ahead; the waves split each tile's 16 copies. Keys past
+  // the sequence end repeat its last key (finite data; they are masked).
+  auto issue = [&](int kt) {
+    unsigned char* slot = ring + (kt % kDqRing) * kDqSlotBytes;
 #pragma unroll
-    for (int u = 0; u < KU; ++u) {
-      const int idx = tid + u * NT;
-      const unsigned off = (unsigned)(min(kk + (idx >> 3), len - 1) * (int)tok_stride + 8 * (idx & 7));
-      kpre[u] = load_bf16x8(kbase + off);
-      vpre[u] = load_bf16x8(vbase + off);
-    }
-  };
-  auto commit = [&](int buf) {
-    __bf16* kl = k_lds + buf * kDqTileElems;
-    __bf16* vl = v_lds + buf * kDqTileElems;
-#pragma unroll
-    for (int u = 0; u < KU; ++u) {
-      const int idx = tid + u * NT;
-      const int off = (idx >> 3) * kLdsStride + 8 * (idx & 7);
-      *reinterpret_cast<bf16x8*>(&kl[off]) = kpre[u];
-      *reinterpret_cast<bf16x8*>(&vl[off]) = vpre[u];
+    for (int i = 0; i < CPW; ++i) {
+      const int u = wave * CPW + i;  // 0..7: K copies, 8..15: V copies
+      if (u < 8) {
+        tile_copy(kbase, kt * kDqTileKeys, len - 1, kv_stride, slot, u, lane);
+      } else {
+        tile_copy(vbase, kt * kDqTileKeys, len - 1, kv_stride, slot + kDqTileBytes, u - 8, lane);
+      }
     }
   };
 
-  // Unconditional (the range is never empty here): every load issued so far is complete on every
-  // path into the loop, so the loop only waits on its prefetch when committing it.
-  prefetch(kt_begin);
-  commit(0);
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): nothing issued before the loop stays in flight
-  __syncthreads();
+  int aoff[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) aoff[c] = tile_frag_off(l32, grp, c);
+  int toff[2][2];
+  tile_tr_offsets(lane, toff);
+  const unsigned ring_lds = lds_addr(ring);
+
+  issue(kt_begin);
+  if (kt_begin + 1 < kt_end) issue(kt_begin + 1);
 
   for (int kt = kt_begin; kt < kt_end; ++kt) {
-    const int cur = (kt - kt_begin) & 1;
-    const bool has_next = kt + 1 < kt_end;
-    if (has_next) prefetch(kt + 1);
-    const __bf16* kl = k_lds + cur * kDqTileElems;
-    const __bf16* vl = v_lds + cur * kDqTileElems;
+    if (kt + 1 < kt_end) {
+      wait_vmcnt<CPW>();  // this wave's copies of tile kt (those of kt + 1 may stay in flight)
+    } else {
+      wait_vmcnt<0>();
+    }
+    // Every wave's copies of tile kt have landed, and every wave is done with tile kt - 1, whose
+    // slot receives tile kt + 2.
+    __syncthreads();
+    if (kt + 2 < kt_end) issue(kt + 2);
+    const unsigned char* slot = ring + (kt % kDqRing) * kDqSlotBytes;
+    const unsigned slot_lds = ring_lds + (kt % kDqRing) * kDqSlotBytes;
     const int k0 = kt * kDqTileKeys;
 
     // S^T = K Q^T and dP^T = V dO^T (rows = keys, loaded with the swap23 permutation).
@@ -501,10 +501,23 @@ __global__ __launch_bounds__(64 * HPW, 2) void attn_sink_bwd_dq_kernel(BwdArgs a
       dp[mb] = zero_f32x16();
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        const int row = (32 * mb + swap23(l32)) * kLdsStride + 16 * c + 8 * grp;
-        s[mb] = mfma_32x32x16(load_bf16x8(&kl[row]), qf[c], s[mb]);
-        dp[mb] = mfma_32x32x16(load_bf16x8(&vl[row]), df[c], dp[mb]);
+        s[mb] = mfma_32x32x16(*reinterpret_cast<const bf16x8*>(slot + 4096 * mb + aoff[c]), qf[c], s[mb]);
+        dp[mb] = mfma_32x32x16(*reinterpret_cast<const bf16x8*>(slot + kDqTileBytes + 4096 * mb + aoff[c]), df[c],
+                               dp[mb]);
       }
+    }
+    // K^T operands for dQ^T (rows d = 32db + l32, k slots = keys 32mb + 16cc + 8grp + 0..7).
+    u32x2 tr[16];  // [d block][key block][half][lo / hi]
+#pragma unroll
+    for (int db = 0; db < 2; ++db) {
+      tr[8 * db + 0] = ds_read_tr16_b64_asm<0>(slot_lds + toff[db][0]);
+      tr[8 * db + 1] = ds_read_tr16_b64_asm<0>(slot_lds + toff[db][1]);
+      tr[8 * db + 2] = ds_read_tr16_b64_asm<2048>(slot_lds + toff[db][0]);
+      tr[8 * db + 3] = ds_read_tr16_b64_asm<2048>(slot_lds + toff[db][1]);
+      tr[8 * db + 4] = ds_read_tr16_b64_asm<4096>(slot_lds + toff[db][0]);
+      tr[8 * db + 5] = ds_read_tr16_b64_asm<4096>(slot_lds + toff[db][1]);
+      tr[8 * db + 6] = ds_read_tr16_b64_asm<6144>(slot_lds + toff[db][0]);
+      tr[8 * db + 7] = ds_read_tr16_b64_asm<6144>(slot_lds + toff[db][1]);
     }
 
     const bool need_mask = (k0 + kDqTileKeys > len) || (a.causal && k0 + kDqTileKeys - 1 > q0) ||
@@ -515,7 +528,7 @@ __global__ __launch_bounds__(64 * HPW, 2) void attn_sink_bwd_dq_kernel(BwdArgs a
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int kj = k0 + 32 * mb + c_row(i, grp);
-          if (!visible(qi, kj, len, a.causal, a.window)) s[mb][i] = kNegInf;
+          s[mb][i] = visible(qi, kj, len, a.causal, a.window) ? s[mb][i] : kNegInf;
         }
       }
     }
@@ -538,14 +551,16 @@ __global__ __launch_bounds__(64 * HPW, 2) void attn_sink_bwd_dq_kernel(BwdArgs a
     // Large probabilities: also multiply the bf16 rounding residual of dS.
     const bool split = wave_any(pmax > kSplitThreshold);
 
-    // dQ^T += K^T dS^T (A = K^T from LDS, contracting over the tile's keys).
+    wait_lds_into(tr);
+    // dQ^T += K^T dS^T (contracting over the tile's keys).
 #pragma unroll
     for (int db = 0; db < 2; ++db) {
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) {
 #pragma unroll
         for (int cc = 0; cc < 2; ++cc) {
-          const bf16x8 kta = load_tr8(kl, kLdsStride, 32 * mb + 16 * cc, 32 * db);  // K^T rows d, keys
+          const u32x2* t = tr + 8 * db + 4 * mb + 2 * cc;
+          const bf16x8 kta = join_tr(t[0], t[1]);
           acc[db] = mfma_32x32x16(kta, dsb[mb][cc], acc[db]);
           if (split) {
             bf16x8 hi = dsb[mb][cc];
@@ -555,9 +570,6 @@ __global__ __launch_bounds__(64 * HPW, 2) void attn_sink_bwd_dq_kernel(BwdArgs a
         }
       }
     }
-
-    if (has_next) commit(cur ^ 1);
-    __syncthreads();
   }
 
   // dQ row, and this wave's share of sum_i P_{i,h} D~_i.

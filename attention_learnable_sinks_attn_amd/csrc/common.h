@@ -195,6 +195,51 @@ __device__ __forceinline__ f32x16 load_rows16(const float* p, int g) {
   return (f32x16){a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3], c[0], c[1], c[2], c[3], d[0], d[1], d[2], d[3]};
 }
 
+// ---- Swizzled tiles of 64-element bf16 rows in LDS ----
+// Rows of 64 bf16 (128 bytes) are stored back to back without padding; logical 16-byte chunk k of
+// tile row r lives in chunk k ^ tile_swz(r). Over any 16 consecutive rows, rows of equal parity
+// get distinct values, so the 16-byte A-operand fragment reads of a 32-row block (rows permuted by
+// swap23, 16 lanes per LDS cycle) hit distinct banks; and rows r and r + 2 (r % 4 == 0) differ in
+// bit 2, so the transposing 8-byte reads of 4 consecutive rows x 32 columns (32 lanes per cycle)
+// do too. tile_swz(r + 16) == tile_swz(r), so 32-row blocks of a tile share one offset table.
+__device__ __forceinline__ int tile_swz(int r) {
+  const int x = (r >> 1) & 7;
+  return ((x & 1) << 2) | (x >> 1);
+}
+
+// Byte offset, within a swizzled 32-row block, of the A-operand fragment of lane (l32, grp) for
+// k slots 16c + 8grp .. +7: row swap23(l32).
+__device__ __forceinline__ int tile_frag_off(int l32, int grp, int c) {
+  const int r = swap23(l32);
+  return r * 128 + (((2 * c + grp) ^ tile_swz(r)) << 4);
+}
+
+// Per-lane byte offsets of the transposing reads (see load_tr8) of a swizzled tile:
+// off[mb][h] addresses rows 8grp + (l%16)/4 + 4h, logical columns 32mb + 16((l>>4)&1) + 4(l%4).
+// Rows k0 + ... (k0 a multiple of 16) add 128 * k0, which fits the instruction's offset field.
+__device__ __forceinline__ void tile_tr_offsets(int lane, int (&off)[2][2]) {
+  const int s16 = lane & 15;
+  const int grp = lane >> 5;
+  const int ch = 2 * ((lane >> 4) & 1) + ((s16 & 3) >> 1);
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int r = 8 * grp + (s16 >> 2) + 4 * h;
+      off[mb][h] = r * 128 + (((4 * mb + ch) ^ tile_swz(r)) << 4) + 8 * (s16 & 1);
+    }
+  }
+}
+
+// Copy u of a swizzled tile: lane l fetches tile row 8u + l/8 (global row min(row0 + 8u + l/8,
+// last), `stride` elements apart), logical chunk (l % 8) ^ tile_swz(row), into LDS tile + 1024u +
+// 16l, i.e. physical chunk l % 8 of that row.
+__device__ __forceinline__ void tile_copy(const __bf16* base, int row0, int last, int stride, unsigned char* tile,
+                                          int u, int lane) {
+  const int r = 8 * u + (lane >> 3);
+  dma16(base + (size_t)min(row0 + r, last) * stride + 8 * ((lane & 7) ^ tile_swz(r)), tile + 1024 * u);
+}
+
 // Work descriptors (filled on the host).
 struct FwdArgs {
   const __bf16* q;

@@ -8,10 +8,11 @@
 // because the sink has no value row. LSE = max + log(denominator) therefore includes the sink.
 //
 // Work split. A workgroup owns one block of 64 query rows of one sequence and HPW query heads
-// that share one KV head (GQA); wave w handles head hs*HPW + w. K and V tiles of 64 keys are
-// double-buffered in LDS and shared by the workgroup's waves; the next tile's global loads are
-// issued before the current tile's math so their latency is hidden, and one barrier per tile
-// suffices. Per tile each wave computes
+// that share one KV head (GQA); wave w handles head hs*HPW + w. K and V tiles of 64 keys pass
+// through a 3-slot LDS ring shared by the workgroup's waves, filled by direct global->LDS copies
+// two tiles ahead (the waves split the copies); one barrier per tile. The tiles are stored with
+// an XOR swizzle of their 16-byte chunks (tile_swz), so that neither the K fragment reads nor the
+// transposing V^T reads have bank conflicts. Per tile each wave computes
 //   S^T = K Q^T   (32x32x16 MFMA; keys on the C rows, the wave's 64 queries on the columns)
 // so that each lane owns one query: the row max and row sum are lane-local plus one exchange
 // with lane ^ 32, and the probabilities, rounded to bf16, are already laid out as the B operand
@@ -31,17 +32,16 @@ namespace attn_sink {
 namespace {
 
 constexpr int kTileKeys = 64;
-constexpr int kLdsStride = 72;            // bf16 elements per staged row (64 + 8 pad: 16-byte aligned rows)
-constexpr int kTileElems = 64 * kLdsStride;
+constexpr int kTileBytes = kTileKeys * kHeadDim * 2;  // one swizzled 64-key tile (K or V)
+constexpr int kSlotBytes = 2 * kTileBytes;             // K tile, then V tile
+constexpr int kRing = 3;                               // LDS ring slots (two tiles in flight)
 
 template <int HPW>
 __global__ __launch_bounds__(64 * HPW, 2) void attn_sink_fwd_kernel(FwdArgs a) {
-  constexpr int NT = 64 * HPW;
-  constexpr int KU = kTileKeys * 8 / NT;        // 16-byte K (and V) pieces per thread and tile
-  constexpr int NB = 2;                         // 32-query column blocks per wave
+  constexpr int NB = 2;                                 // 32-query column blocks per wave
   constexpr int kRows = 32 * NB;
-  __shared__ __attribute__((aligned(16))) __bf16 k_lds[2 * kTileElems];
-  __shared__ __attribute__((aligned(16))) __bf16 v_lds[2 * kTileElems];
+  constexpr int CPW = 2 * (kTileBytes / 1024) / HPW;    // copies per wave and tile (K and V)
+  __shared__ __attribute__((aligned(1024))) unsigned char ring[kRing * kSlotBytes];
 
   const int n_hs = a.Hq / HPW;
   const int bid = blockIdx.x;
@@ -96,52 +96,48 @@ __global__ __launch_bounds__(64 * HPW, 2) void attn_sink_fwd_kernel(FwdArgs a) {
   const int kt_begin = kbeg / kTileKeys;
   const int kt_end = (kend + kTileKeys - 1) / kTileKeys;
 
-  const size_t tok_stride = (size_t)a.Hkv * kHeadDim;
-  const __bf16* kbase = a.k + (size_t)cs * tok_stride + (size_t)g * kHeadDim;
-  const __bf16* vbase = a.v + (size_t)cs * tok_stride + (size_t)g * kHeadDim;
+  const int kv_stride = a.Hkv * kHeadDim;
+  const __bf16* kbase = a.k + (size_t)cs * kv_stride + (size_t)g * kHeadDim;
+  const __bf16* vbase = a.v + (size_t)cs * kv_stride + (size_t)g * kHeadDim;
 
-  // Register staging of one K / V tile (global -> registers -> LDS), both in natural [key][d]
-  // layout; V^T operands are read with transposing LDS loads. Keys past the sequence end are
-  // clamped onto its last key (finite data; they are masked).
-  bf16x8 kpre[KU], vpre[KU];
-  auto prefetch = [&](int kt) {
-    const int k0 = kt * kTileKeys;
+  // K and V tiles of 64 keys, swizzled (see tile_swz), in a 3-slot ring filled by direct
+  // global->LDS copies issued two tiles ahead; the waves split each tile's 16 copies. Keys past
+  // the sequence end repeat its last key (finite data; they are masked). V^T operands come from
+  // transposing LDS loads of the V tile.
+  auto issue = [&](int kt) {
+    unsigned char* slot = ring + (kt % kRing) * kSlotBytes;
 #pragma unroll
-    for (int u = 0; u < KU; ++u) {
-      const int idx = tid + u * NT;
-      const unsigned off = (unsigned)(min(k0 + (idx >> 3), len - 1) * (int)tok_stride + 8 * (idx & 7));
-      kpre[u] = load_bf16x8(kbase + off);
-      vpre[u] = load_bf16x8(vbase + off);
+    for (int i = 0; i < CPW; ++i) {
+      const int u = wave * CPW + i;  // 0..7: K copies, 8..15: V copies
+      if (u < 8) {
+        tile_copy(kbase, kt * kTileKeys, len - 1, kv_stride, slot, u, lane);
+      } else {
+        tile_copy(vbase, kt * kTileKeys, len - 1, kv_stride, slot + kTileBytes, u - 8, lane);
+      }
     }
   };
-  auto commit = [&](int buf) {
-    __bf16* kl = k_lds + buf * kTileElems;
-    __bf16* vl = v_lds + buf * kTileElems;
+  int aoff[4];
 #pragma unroll
-    for (int u = 0; u < KU; ++u) {
-      const int idx = tid + u * NT;
-      const int off = (idx >> 3) * kLdsStride + 8 * (idx & 7);
-      *reinterpret_cast<bf16x8*>(&kl[off]) = kpre[u];
-      *reinterpret_cast<bf16x8*>(&vl[off]) = vpre[u];
-    }
-  };
+  for (int c = 0; c < 4; ++c) aoff[c] = tile_frag_off(l32, grp, c);
+  int toff[2][2];
+  tile_tr_offsets(lane, toff);
+  const unsigned ring_lds = lds_addr(ring);
 
-  // Unconditional (the range is never empty here): every load issued so far, including the Q
-  // operands, is complete on every path into the loop, so the loop only waits on its prefetch
-  // when committing it.
-  prefetch(kt_begin);
-  commit(0);
-  // vmcnt(0): the Q loads may have been scheduled after the tile loads; make sure nothing issued
-  // before the loop is still in flight, or the loop would wait on its own prefetch at the top.
-  __builtin_amdgcn_s_waitcnt(0x0F70);
-  __syncthreads();
+  issue(kt_begin);
+  if (kt_begin + 1 < kt_end) issue(kt_begin + 1);
 
   for (int kt = kt_begin; kt < kt_end; ++kt) {
-    const int cur = (kt - kt_begin) & 1;
-    const bool has_next = kt + 1 < kt_end;
-    if (has_next) prefetch(kt + 1);
-    const __bf16* kl = k_lds + cur * kTileElems;
-    const __bf16* vl = v_lds + cur * kTileElems;
+    if (kt + 1 < kt_end) {
+      wait_vmcnt<CPW>();  // this wave's copies of tile kt (those of kt + 1 may stay in flight)
+    } else {
+      wait_vmcnt<0>();
+    }
+    // Every wave's copies of tile kt have landed, and every wave is done with tile kt - 1, whose
+    // slot receives tile kt + 2.
+    __syncthreads();
+    if (kt + 2 < kt_end) issue(kt + 2);
+    const unsigned char* slot = ring + (kt % kRing) * kSlotBytes;
+    const unsigned vt_lds = ring_lds + (kt % kRing) * kSlotBytes + kTileBytes;
     const int k0 = kt * kTileKeys;
 
     // S^T = K Q^T for two 32-key row blocks.
@@ -152,12 +148,11 @@ __global__ __launch_bounds__(64 * HPW, 2) void attn_sink_fwd_kernel(FwdArgs a) {
       for (int nb = 0; nb < NB; ++nb) s[mb][nb] = zero_f32x16();
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        const bf16x8 ka = load_bf16x8(&kl[(32 * mb + swap23(l32)) * kLdsStride + 16 * c + 8 * grp]);
+        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(slot + 4096 * mb + aoff[c]);
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) s[mb][nb] = mfma_32x32x16(ka, qf[nb][c], s[mb][nb]);
       }
     }
-
     const bool need_mask = (k0 + kTileKeys > len) || (a.causal && k0 + kTileKeys - 1 > q0) ||
                            (a.window > 0 && k0 <= q0 + kRows - 1 - a.window);
     if (need_mask) {
@@ -169,7 +164,7 @@ __global__ __launch_bounds__(64 * HPW, 2) void attn_sink_fwd_kernel(FwdArgs a) {
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int kj = k0 + 32 * mb + c_row(i, grp);
-            if (!visible(qi, kj, len, a.causal, a.window)) s[mb][nb][i] = kNegInf;
+            s[mb][nb][i] = visible(qi, kj, len, a.causal, a.window) ? s[mb][nb][i] : kNegInf;
           }
         }
       }
@@ -201,6 +196,20 @@ __global__ __launch_bounds__(64 * HPW, 2) void attn_sink_fwd_kernel(FwdArgs a) {
       }
     }
 
+    // V^T operands for O^T += V^T P^T (rows d = 32db + l32, k slots = keys 32mb + 16cc + 8grp + 0..7).
+    u32x2 tr[16];  // [d block][key block][half][lo / hi]
+#pragma unroll
+    for (int db = 0; db < 2; ++db) {
+      tr[8 * db + 0] = ds_read_tr16_b64_asm<0>(vt_lds + toff[db][0]);
+      tr[8 * db + 1] = ds_read_tr16_b64_asm<0>(vt_lds + toff[db][1]);
+      tr[8 * db + 2] = ds_read_tr16_b64_asm<2048>(vt_lds + toff[db][0]);
+      tr[8 * db + 3] = ds_read_tr16_b64_asm<2048>(vt_lds + toff[db][1]);
+      tr[8 * db + 4] = ds_read_tr16_b64_asm<4096>(vt_lds + toff[db][0]);
+      tr[8 * db + 5] = ds_read_tr16_b64_asm<4096>(vt_lds + toff[db][1]);
+      tr[8 * db + 6] = ds_read_tr16_b64_asm<6144>(vt_lds + toff[db][0]);
+      tr[8 * db + 7] = ds_read_tr16_b64_asm<6144>(vt_lds + toff[db][1]);
+    }
+
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       const float moff = m[nb] == kNegInf ? 0.0f : m[nb];  // nothing visible yet: exp2(-inf) = 0
@@ -219,21 +228,19 @@ __global__ __launch_bounds__(64 * HPW, 2) void attn_sink_fwd_kernel(FwdArgs a) {
       }
       lsum[nb] += rs;
       // O^T += V^T P^T for this column block, contracting over the tile's 64 keys.
+      if (nb == 0) wait_lds_into(tr);
 #pragma unroll
       for (int db = 0; db < 2; ++db) {
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) {
 #pragma unroll
           for (int cc = 0; cc < 2; ++cc) {
-            const bf16x8 va = load_tr8(vl, kLdsStride, 32 * mb + 16 * cc, 32 * db);  // V^T rows d, keys
-            o[db][nb] = mfma_32x32x16(va, pb[mb][cc], o[db][nb]);
+            const u32x2* t = tr + 8 * db + 4 * mb + 2 * cc;
+            o[db][nb] = mfma_32x32x16(join_tr(t[0], t[1]), pb[mb][cc], o[db][nb]);
           }
         }
       }
     }
-
-    if (has_next) commit(cur ^ 1);
-    __syncthreads();
   }
 
   // Epilogue: combine the two lane halves' partial denominators, normalise, store.
