@@ -91,16 +91,6 @@ constexpr int kKvSlotBytes = 2 * kKvTileBytes + 2 * kKvRows * 4;  // Q, dO, -LSE
 constexpr int kKvStreamBytes = kKvRing * kKvSlotBytes;
 constexpr int kKvRedStride = kHeadDim + 4;                        // fp32 row of the final sum
 
-// Chunk swizzle of a 128-byte LDS row: logical 16-byte chunk k of tile row r is stored in chunk
-// k ^ kv_swz(r). Over any 16 consecutive rows, rows of equal parity get distinct values (so the
-// 16-byte fragment reads of 16 rows, permuted by swap23, hit distinct banks), and rows r and r + 2
-// with r % 4 == 0 differ in bit 2 (so the transposing 8-byte reads of 4 consecutive rows x 32
-// columns do too). kv_swz(r + 16) == kv_swz(r).
-__device__ __forceinline__ int kv_swz(int r) {
-  const int x = (r >> 1) & 7;
-  return ((x & 1) << 2) | (x >> 1);
-}
-
 template <int NS>  // head streams per workgroup: 1 or 2 (waves = 2 key halves x NS)
 __global__ __launch_bounds__(128 * NS, 2) void attn_sink_bwd_dkdv_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(1024))) unsigned char smem[NS * kKvStreamBytes];
@@ -157,15 +147,14 @@ __global__ __launch_bounds__(128 * NS, 2) void attn_sink_bwd_dkdv_kernel(BwdArgs
   const int n_sub = (i_end - i_begin + kKvRows - 1) / kKvRows;
   const int n_steps = hps * n_sub;
 
-  // Each stream owns a ring of 3 slots; step s lives in slot s % 3. The two key halves of a
+  // Each stream owns a ring of 2 slots; step s lives in slot s % 2. The two key halves of a
   // stream split the copies of a step: half 0 copies the Q tile and the -LSE/scale, -D rows,
-  // half 1 the dO tile. Lane l of copy u fetches tile row 8u + l/8, logical chunk
-  // (l % 8) ^ kv_swz(row), which lands at physical chunk l % 8 of that row.
+  // half 1 the dO tile (tile_copy layout; full tiles take a precomputed per-lane offset).
   unsigned char* ring = smem + st * kKvStreamBytes;
   const int qstride = a.Hq * kHeadDim;  // elements per token row of q / dout
   const int crow = lane >> 3;
-  const int coff0 = crow * qstride + 8 * ((lane & 7) ^ kv_swz(crow));      // rows 8u + crow, u even
-  const int coff1 = crow * qstride + 8 * ((lane & 7) ^ kv_swz(8 + crow));  // u odd
+  const int coff0 = crow * qstride + 8 * ((lane & 7) ^ tile_swz(crow));      // rows 8u + crow, u even
+  const int coff1 = crow * qstride + 8 * ((lane & 7) ^ tile_swz(8 + crow));  // u odd
   auto issue = [&](int j, int t, int slot) {
     const int h = h0 + NS * j;
     const int i0 = i_begin + kKvRows * (n_sub - 1 - t);
@@ -178,10 +167,7 @@ __global__ __launch_bounds__(128 * NS, 2) void attn_sink_bwd_dkdv_kernel(BwdArgs
       }
     } else {  // last, partial tile: rows past the end repeat the last row (they are masked)
 #pragma unroll
-      for (int u = 0; u < kKvTileBytes / 1024; ++u) {
-        const int r = 8 * u + crow;
-        dma16(src + (min(i0 + r, len - 1) - i0) * qstride + 8 * ((lane & 7) ^ kv_swz(r)), dst + 1024 * u);
-      }
+      for (int u = 0; u < kKvTileBytes / 1024; ++u) tile_copy(src, 0, len - 1 - i0, qstride, dst, u, lane);
     }
     if (kh == 0) {  // -LSE/scale rows, then -D rows (64 each)
       const float* nl = a.nlse + (size_t)h * a.T + cs;
@@ -192,26 +178,13 @@ __global__ __launch_bounds__(128 * NS, 2) void attn_sink_bwd_dkdv_kernel(BwdArgs
   };
   auto wait_own_step = [&]() { wait_vmcnt<0>(); };  // this wave's copies of the current step
 
-  // Per-lane LDS byte offsets within a tile. Fragment reads (A operands, k = d): row
-  // swap23(l32), logical chunk 2c + grp.
-  const int ar = swap23(l32);
+  // Per-lane LDS byte offsets within a 32-row block of a swizzled tile: A-operand fragments
+  // (k = d) and transposing reads (k = query rows).
   int aoff[4];
 #pragma unroll
-  for (int c = 0; c < 4; ++c) aoff[c] = ar * 128 + (((2 * c + grp) ^ kv_swz(ar)) << 4);
-  // Transposing reads (A operands, k = query): rows 8grp + s/4 (+4), logical columns
-  // m0 + 16*((l>>4)&1) + 4*(s%4), s = l % 16; m0 = 32 * db; rows +16 for the second query half.
-  const int s16 = lane & 15;
-  const int trow = 8 * grp + (s16 >> 2);
-  const int tch = 2 * ((lane >> 4) & 1) + ((s16 & 3) >> 1);
+  for (int c = 0; c < 4; ++c) aoff[c] = tile_frag_off(l32, grp, c);
   int toff[2][2];  // [d block][+0 / +4 rows]
-#pragma unroll
-  for (int db = 0; db < 2; ++db) {
-#pragma unroll
-    for (int hi = 0; hi < 2; ++hi) {
-      const int r = trow + 4 * hi;
-      toff[db][hi] = r * 128 + (((4 * db + tch) ^ kv_swz(r)) << 4) + 8 * (s16 & 1);
-    }
-  }
+  tile_tr_offsets(lane, toff);
   // Transposed operands (see load_tr8): Q^T (tile 0) or dO^T (tile 1) rows d = 32db + l32, k
   // slots = query rows 16*half + 8grp + 0..7 of the slot at LDS address `slot_lds`.
   auto tr8 = [&](unsigned slot_lds, auto tile_tag, int db, auto half_tag, u32x2& lo, u32x2& hi) {

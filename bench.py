@@ -9,13 +9,19 @@ head_dim 64, causal, bf16 inputs (the headline configuration).
 Prints one JSON line. ``value`` is algorithmic TFLOP/s over the timed steps: 4*d FLOPs per visible
 (query, key, head) in the forward (QK^T and PV) plus 10*d in the backward (S, dP, dV, dK, dQ);
 recomputation and masked tile work are not counted. ``roofline`` describes the kernel with the
-largest share of the step time, timed with HIP events recorded on the stream the kernels run on.
+largest share of the step time, timed with HIP events recorded on the stream the kernels run on:
+against the bf16 MFMA peak for the causal workloads, and against HBM bandwidth (algorithmic bytes:
+each tensor the kernel needs read or written once at its ABI dtype) for the banded window ones.
 ``cpu_baseline`` times the fp64 CPU oracle on a bounded sample of the same workload.
+
+``--copy-probe-mib N`` also runs one device-to-device copy of N MiB before the timed steps, the
+known-size kernel that scales the FETCH_SIZE / WRITE_SIZE counters of a ``rocprofv3 --pmc`` run.
 """
 from __future__ import annotations
 
 import argparse
 import ctypes
+import hashlib
 import json
 import math
 import os
@@ -45,6 +51,43 @@ KERNEL_FLOPS_PER_PAIR_D = {
     "attn_sink_bwd_dq_kernel": 2,
     "attn_sink_bwd_dsink_kernel": 0,
 }
+
+
+# HBM traffic of the dominant kernel, per launch, from two rocprofv3 --pmc runs of this script
+# (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch) scaled by what the same counters read for the
+# copy probe; valid only for kernel sources with the recorded digest.
+TRAFFIC = {
+    ("causal4k", "attn_sink_bwd_dkdv_kernel"): {"bytes": 148726365, "digest": "0c3e577ebdf54fde"},
+    ("window4k", "attn_sink_bwd_dkdv_kernel"): {"bytes": 114745761, "digest": "0c3e577ebdf54fde"},
+}
+
+
+def kernel_source_digest() -> str:
+    """sha256 over the HIP sources and headers the library is built from."""
+    h = hashlib.sha256()
+    for d in (os.path.join(ROOT, "attention_learnable_sinks_attn_amd", "csrc"), os.path.join(ROOT, "include")):
+        for name in sorted(os.listdir(d)):
+            if name.endswith((".hip", ".h")):
+                with open(os.path.join(d, name), "rb") as f:
+                    h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def kernel_bytes(name: str, T: int, hq: int, hkv: int, d: int) -> int:
+    """Algorithmic HBM bytes of one launch: every tensor the kernel needs, read or written once."""
+    q = T * hq * d * 2
+    kv = 2 * T * hkv * d * 2
+    rows = hq * T * 4  # one fp32 per (head, row): LSE, D
+    o32 = T * hq * d * 4
+    dkv32 = 2 * T * hkv * d * 4
+    return {
+        "attn_sink_fwd_kernel": q + kv + o32 + rows,
+        "attn_sink_bwd_prep_kernel": o32 + q + rows + 2 * rows,
+        "attn_sink_bwd_dkdv_kernel": 2 * q + kv + 2 * rows + dkv32,
+        "attn_sink_bwd_dkdv_sum_kernel": dkv32,
+        "attn_sink_bwd_dq_kernel": 2 * q + kv + 2 * rows + o32,
+        "attn_sink_bwd_dsink_kernel": 0,
+    }[name]
 
 
 class Hip:
@@ -111,6 +154,7 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-kv-groups", type=int, default=8)
+    ap.add_argument("--copy-probe-mib", type=int, default=0)
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
@@ -148,6 +192,13 @@ def main():
         asa.bwd(q, k, v, sinks, out, lse, dout, cu, inp.max_seqlen, inp.causal, inp.window, dq=dq, dk=dk, dv=dv,
                 dsinks=dsinks, workspace=ws, events=None if evs is None else evs[1:])
 
+    if args.copy_probe_mib > 0:
+        n = args.copy_probe_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -170,11 +221,22 @@ def main():
     flops = pairs * 14 * d
     tflops = flops / (ms_step * 1e-3) / 1e12
     dom = max(per_kernel, key=per_kernel.get)
-    dom_flops = pairs * KERNEL_FLOPS_PER_PAIR_D[dom] * d
-    achieved = dom_flops / (per_kernel[dom] * 1e-3) / 1e12
-    roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
-                "avg_launch_ms": round(per_kernel[dom], 4)}
+    if inp.window > 0:  # banded: far less compute per byte than the ridge point
+        dom_bytes = kernel_bytes(dom, T, Hq, Hkv, d)
+        achieved = dom_bytes / (per_kernel[dom] * 1e-3) / 1e9
+        roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                    "avg_launch_ms": round(per_kernel[dom], 4), "algorithmic_bytes": dom_bytes}
+    else:
+        dom_flops = pairs * KERNEL_FLOPS_PER_PAIR_D[dom] * d
+        achieved = dom_flops / (per_kernel[dom] * 1e-3) / 1e12
+        roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                    "avg_launch_ms": round(per_kernel[dom], 4), "algorithmic_flops": dom_flops}
+    rec = TRAFFIC.get((w.name, dom))
+    if rec is not None and rec["digest"] == kernel_source_digest():
+        roofline["traffic"] = rec["bytes"]
+        roofline["traffic_unit"] = "bytes per launch (HBM fetch + write)"
     res = {
         "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
