@@ -113,8 +113,7 @@ int bwd_impl(const void* q, const void* k, const void* v, const float* sinks, co
   a.scale_log2 = a.scale * kLog2e;
 
   typedef hipError_t (*launcher)(const BwdArgs&, hipStream_t);
-  const launcher steps[kBwdNumKernels] = {launch_bwd_prep, launch_bwd_dkdv, launch_bwd_dkdv_sum, launch_bwd_dq,
-                                           launch_bwd_dsink};
+  const launcher steps[kBwdNumKernels] = {launch_bwd_prep, launch_bwd_dkdv, launch_bwd_dq, launch_bwd_finish};
   for (int i = 0; i < kBwdNumKernels; ++i) {
     if (events && hipEventRecord(static_cast<hipEvent_t>(events[i]), stream) != hipSuccess) return ATTN_SINK_ERR_HIP;
     if (steps[i](a, stream) != hipSuccess) return ATTN_SINK_ERR_HIP;
@@ -186,8 +185,7 @@ int attn_sink_bwd_num_kernels(void) { return kBwdNumKernels; }
 
 const char* attn_sink_bwd_kernel_name(int i) {
   static const char* const names[kBwdNumKernels] = {"attn_sink_bwd_prep_kernel", "attn_sink_bwd_dkdv_kernel",
-                                                    "attn_sink_bwd_dkdv_sum_kernel", "attn_sink_bwd_dq_kernel",
-                                                    "attn_sink_bwd_dsink_kernel"};
+                                                    "attn_sink_bwd_dq_kernel", "attn_sink_bwd_finish_kernel"};
   return (i >= 0 && i < kBwdNumKernels) ? names[i] : nullptr;
 }
 

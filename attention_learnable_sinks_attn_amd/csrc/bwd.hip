@@ -24,7 +24,6 @@
 //            two streams' partial sums are added in LDS at the end, and each head half writes its
 //            own fp32 partial. Splitting the heads doubles the number of workgroups, so that
 //            (launched longest first) they keep two per CU busy under a causal mask.
-//  2b. dkdv_sum: dK = scale * (sum of the halves), dV = sum of the halves.
 //  3. dq:    row-parallel. A workgroup owns 32 query rows of `hpw` heads of one group (one head
 //            per wave) and streams 64-key tiles of K and V through a 3-slot LDS ring filled by
 //            direct copies two tiles ahead (swizzled like the dkdv tiles; K^T operands come from
@@ -33,7 +32,8 @@
 //            holds and writes sum_i P_{i,h} D~_i for its rows. D~ equals D mathematically but
 //            does not carry the bf16 rounding of the forward's P.V product, which matters
 //            because the terms of dL/dS_h cancel heavily.
-//  4. dsink: dL/dS_h = -(sum of the partials of head h), summed in a fixed order.
+//  4. finish: dK = scale * (sum of the halves), dV = sum of the halves; and
+//            dL/dS_h = -(sum of the partials of head h), summed in a fixed order.
 #include <type_traits>
 
 #include "kernels.h"
@@ -46,31 +46,43 @@ constexpr int kLdsStride = 72;  // bf16 per staged 64-element row (16-byte align
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 // ------------------------------------------------------------------------------------------
-// 1. -D_i = -sum_d dO[i,h,d] * O[i,h,d] and -LSE_i / scale. A block handles 16 consecutive rows
-//    of one head (16 lanes per row, 4 elements each), so the [Hq, T] results are written
-//    contiguously.
+// 1. -D_i = -sum_d dO[i,h,d] * O[i,h,d] and -LSE_i / scale. A block handles 64 consecutive rows
+//    of one head: 16 lanes per row (4 elements each), each 16-lane group 4 rows 16 apart, so the
+//    [Hq, T] results are written contiguously and each lane keeps 4 row loads in flight.
 // ------------------------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void attn_sink_bwd_prep_kernel(BwdArgs a) {
-  const int tblocks = (a.T + 15) / 16;
-  const int h = blockIdx.x / tblocks;
-  const int t = (blockIdx.x - h * tblocks) * 16 + (threadIdx.x >> 4);
-  const int part = threadIdx.x & 15;
-  float acc = 0.0f;
-  if (h < a.Hq && t < a.T) {
-    const size_t row = (size_t)t * a.Hq + h;
-    const f32x4 o = *reinterpret_cast<const f32x4*>(a.out + row * kHeadDim + 4 * part);
+  constexpr int kRowsPerBlock = 64;
+  const int tblocks = (a.T + kRowsPerBlock - 1) / kRowsPerBlock;
+  // With T = 0 there are no rows (tblocks = 0, and the single launched block only clears below).
+  if (tblocks > 0 && (int)blockIdx.x < a.Hq * tblocks) {
+    const int h = blockIdx.x / tblocks;
+    const int t0 = (blockIdx.x - h * tblocks) * kRowsPerBlock + (threadIdx.x >> 4);
+    const int part = threadIdx.x & 15;
     typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-    const bf16x4 d = *reinterpret_cast<const bf16x4*>(a.dout + row * kHeadDim + 4 * part);
-    acc = o[0] * (float)d[0] + o[1] * (float)d[1] + o[2] * (float)d[2] + o[3] * (float)d[3];
-  }
-  acc += __shfl_xor(acc, 8, 16);
-  acc += __shfl_xor(acc, 4, 16);
-  acc += __shfl_xor(acc, 2, 16);
-  acc += __shfl_xor(acc, 1, 16);
-  if (h < a.Hq && t < a.T && part == 0) {
-    const size_t o = (size_t)h * a.T + t;
-    a.negd[o] = -acc;
-    a.nlse[o] = -a.lse[o] / a.scale;
+    f32x4 o[4];
+    bf16x4 d[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int t = min(t0 + 16 * k, a.T - 1);  // in [0, T): rows past the end repeat the last (not stored)
+      const size_t row = (size_t)t * a.Hq + h;
+      o[k] = *reinterpret_cast<const f32x4*>(a.out + row * kHeadDim + 4 * part);
+      d[k] = *reinterpret_cast<const bf16x4*>(a.dout + row * kHeadDim + 4 * part);
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      float acc = o[k][0] * (float)d[k][0] + o[k][1] * (float)d[k][1] + o[k][2] * (float)d[k][2] +
+                  o[k][3] * (float)d[k][3];
+      acc += __shfl_xor(acc, 8, 16);
+      acc += __shfl_xor(acc, 4, 16);
+      acc += __shfl_xor(acc, 2, 16);
+      acc += __shfl_xor(acc, 1, 16);
+      const int t = t0 + 16 * k;
+      if (t < a.T && part == 0) {
+        const size_t r = (size_t)h * a.T + t;
+        a.negd[r] = -acc;
+        a.nlse[r] = -a.lse[r] / a.scale;
+      }
+    }
   }
   // Clear the dSink partials (rows of the dq pass that exit early never write theirs).
   const long long nparts = (long long)a.Hq * a.n_slots;
@@ -327,7 +339,7 @@ __global__ __launch_bounds__(128 * NS, 2) void attn_sink_bwd_dkdv_kernel(BwdArgs
   if (st == 0) {
     const int key = k0 + l32;
     if (key < len) {
-      // This head half's partial sums (unscaled); attn_sink_bwd_dkdv_sum_kernel adds the halves.
+      // This head half's partial sums (unscaled); attn_sink_bwd_finish_kernel adds the halves.
       const size_t plane = (size_t)a.T * a.Hkv * kHeadDim;
       float* dkrow = a.dkv_part + hh * plane + ((size_t)(cs + key) * a.Hkv + g) * kHeadDim;
       float* dvrow = a.dkv_part + (a.n_halves + hh) * plane + ((size_t)(cs + key) * a.Hkv + g) * kHeadDim;
@@ -347,23 +359,6 @@ __global__ __launch_bounds__(128 * NS, 2) void attn_sink_bwd_dkdv_kernel(BwdArgs
         }
       }
     }
-  }
-}
-
-// ------------------------------------------------------------------------------------------
-// 2b. dK = scale * (sum of the head halves' partials), dV = sum of the partials.
-// ------------------------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void attn_sink_bwd_dkdv_sum_kernel(BwdArgs a) {
-  const size_t plane4 = (size_t)a.T * a.Hkv * (kHeadDim / 4);  // float4 per partial plane
-  const f32x4* p = reinterpret_cast<const f32x4*>(a.dkv_part);
-  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < plane4; i += (size_t)gridDim.x * blockDim.x) {
-    f32x4 k4 = p[i], v4 = p[a.n_halves * plane4 + i];
-    for (int hh = 1; hh < a.n_halves; ++hh) {
-      k4 += p[hh * plane4 + i];
-      v4 += p[(a.n_halves + hh) * plane4 + i];
-    }
-    reinterpret_cast<f32x4*>(a.dk)[i] = k4 * a.scale;
-    reinterpret_cast<f32x4*>(a.dv)[i] = v4;
   }
 }
 
@@ -462,86 +457,83 @@ __global__ __launch_bounds__(64 * HPW, 2) void attn_sink_bwd_dq_kernel(BwdArgs a
     // slot receives tile kt + 2.
     __syncthreads();
     if (kt + 2 < kt_end) issue(kt + 2);
-    const unsigned char* slot = ring + (kt % kDqRing) * kDqSlotBytes;
-    const unsigned slot_lds = ring_lds + (kt % kDqRing) * kDqSlotBytes;
     const int k0 = kt * kDqTileKeys;
-
-    // S^T = K Q^T and dP^T = V dO^T (rows = keys, loaded with the swap23 permutation).
-    f32x16 s[2], dp[2];
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      s[mb] = zero_f32x16();
-      dp[mb] = zero_f32x16();
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        s[mb] = mfma_32x32x16(*reinterpret_cast<const bf16x8*>(slot + 4096 * mb + aoff[c]), qf[c], s[mb]);
-        dp[mb] = mfma_32x32x16(*reinterpret_cast<const bf16x8*>(slot + kDqTileBytes + 4096 * mb + aoff[c]), df[c],
-                               dp[mb]);
-      }
-    }
-    // K^T operands for dQ^T (rows d = 32db + l32, k slots = keys 32mb + 16cc + 8grp + 0..7).
-    u32x2 tr[16];  // [d block][key block][half][lo / hi]
-#pragma unroll
-    for (int db = 0; db < 2; ++db) {
-      tr[8 * db + 0] = ds_read_tr16_b64_asm<0>(slot_lds + toff[db][0]);
-      tr[8 * db + 1] = ds_read_tr16_b64_asm<0>(slot_lds + toff[db][1]);
-      tr[8 * db + 2] = ds_read_tr16_b64_asm<2048>(slot_lds + toff[db][0]);
-      tr[8 * db + 3] = ds_read_tr16_b64_asm<2048>(slot_lds + toff[db][1]);
-      tr[8 * db + 4] = ds_read_tr16_b64_asm<4096>(slot_lds + toff[db][0]);
-      tr[8 * db + 5] = ds_read_tr16_b64_asm<4096>(slot_lds + toff[db][1]);
-      tr[8 * db + 6] = ds_read_tr16_b64_asm<6144>(slot_lds + toff[db][0]);
-      tr[8 * db + 7] = ds_read_tr16_b64_asm<6144>(slot_lds + toff[db][1]);
-    }
 
     const bool need_mask = (k0 + kDqTileKeys > len) || (a.causal && k0 + kDqTileKeys - 1 > q0) ||
                            (a.window > 0 && k0 <= q0 + kRows - 1 - a.window);
-    if (need_mask) {  // uniform: only diagonal, window-edge and ragged tiles
+    // One tile: S^T = K Q^T and dP^T = V dO^T (rows = keys, loaded with the swap23 permutation),
+    // P = exp2(S*scale*log2e - LSE*log2e), dS = P (dP - D), dQ^T += K^T dS^T, one 32-key block
+    // after the other so that block 1's softmax overlaps block 0's dQ products. Returns the
+    // tile's largest probability. When it exceeds kSplitThreshold, the tile runs a second time in
+    // residual mode, multiplying the bf16 rounding residual of dS instead (its LDS offset goes
+    // through an empty asm, so that none of the first pass's loads are kept for it).
+    auto tile = [&](bool residual, unsigned lds_off) -> float {
+      const unsigned char* slot = ring + lds_off;
+      const unsigned slot_lds = ring_lds + lds_off;
+      f32x16 s[2], dp[2];
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) {
+        s[mb] = zero_f32x16();
+        dp[mb] = zero_f32x16();
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int kj = k0 + 32 * mb + c_row(i, grp);
-          s[mb][i] = visible(qi, kj, len, a.causal, a.window) ? s[mb][i] : kNegInf;
+        for (int c = 0; c < 4; ++c) {
+          s[mb] = mfma_32x32x16(*reinterpret_cast<const bf16x8*>(slot + 4096 * mb + aoff[c]), qf[c], s[mb]);
+          dp[mb] = mfma_32x32x16(*reinterpret_cast<const bf16x8*>(slot + kDqTileBytes + 4096 * mb + aoff[c]), df[c],
+                                 dp[mb]);
         }
       }
-    }
-    bf16x8 dsb[2][2];
-    float pmax = 0.0f, part = 0.0f;
+      // K^T operands for dQ^T (rows d = 32db + l32, k slots = keys 32mb + 16cc + 8grp + 0..7).
+      u32x2 tr[16];  // [d block][key block][half][lo / hi]
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float p = fast_exp2(__builtin_fmaf(s[mb][i], a.scale_log2, -lse2));
-        pmax = fmaxf(pmax, p);
-        const float pdp = p * dp[mb][i];
-        part += pdp;
-        dp[mb][i] = __builtin_fmaf(p, nd, pdp);
+      for (int db = 0; db < 2; ++db) {
+        tr[8 * db + 0] = ds_read_tr16_b64_asm<0>(slot_lds + toff[db][0]);
+        tr[8 * db + 1] = ds_read_tr16_b64_asm<0>(slot_lds + toff[db][1]);
+        tr[8 * db + 2] = ds_read_tr16_b64_asm<2048>(slot_lds + toff[db][0]);
+        tr[8 * db + 3] = ds_read_tr16_b64_asm<2048>(slot_lds + toff[db][1]);
+        tr[8 * db + 4] = ds_read_tr16_b64_asm<4096>(slot_lds + toff[db][0]);
+        tr[8 * db + 5] = ds_read_tr16_b64_asm<4096>(slot_lds + toff[db][1]);
+        tr[8 * db + 6] = ds_read_tr16_b64_asm<6144>(slot_lds + toff[db][0]);
+        tr[8 * db + 7] = ds_read_tr16_b64_asm<6144>(slot_lds + toff[db][1]);
       }
-      dsb[mb][0] = pack8(dp[mb], 0);
-      dsb[mb][1] = pack8(dp[mb], 1);
-    }
-    dsum += part;
-    // Large probabilities: also multiply the bf16 rounding residual of dS.
-    const bool split = wave_any(pmax > kSplitThreshold);
-
-    wait_lds_into(tr);
-    // dQ^T += K^T dS^T (contracting over the tile's keys).
-#pragma unroll
-    for (int db = 0; db < 2; ++db) {
+      float pmax = 0.0f, part = 0.0f;
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) {
+        if (need_mask) {  // uniform: only diagonal, window-edge and ragged tiles
 #pragma unroll
-        for (int cc = 0; cc < 2; ++cc) {
-          const u32x2* t = tr + 8 * db + 4 * mb + 2 * cc;
-          const bf16x8 kta = join_tr(t[0], t[1]);
-          acc[db] = mfma_32x32x16(kta, dsb[mb][cc], acc[db]);
-          if (split) {
-            bf16x8 hi = dsb[mb][cc];
-            opaque(hi);  // keeps the residual arithmetic inside this rarely taken branch
-            acc[db] = mfma_32x32x16(kta, residual8(dp[mb], cc, hi), acc[db]);
+          for (int i = 0; i < 16; ++i) {
+            const int kj = k0 + 32 * mb + c_row(i, grp);
+            s[mb][i] = visible(qi, kj, len, a.causal, a.window) ? s[mb][i] : kNegInf;
           }
         }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float p = fast_exp2(__builtin_fmaf(s[mb][i], a.scale_log2, -lse2));
+          pmax = fmaxf(pmax, p);
+          const float pdp = p * dp[mb][i];
+          part += pdp;
+          dp[mb][i] = __builtin_fmaf(p, nd, pdp);
+        }
+        bf16x8 d0 = pack8(dp[mb], 0), d1 = pack8(dp[mb], 1);
+        if (residual) {
+          d0 = residual8(dp[mb], 0, d0);
+          d1 = residual8(dp[mb], 1, d1);
+        }
+        if (mb == 0) wait_lds_into(tr);
+#pragma unroll
+        for (int db = 0; db < 2; ++db) {
+          const u32x2* t = tr + 8 * db + 4 * mb;
+          acc[db] = mfma_32x32x16(join_tr(t[0], t[1]), d0, acc[db]);
+          acc[db] = mfma_32x32x16(join_tr(t[2], t[3]), d1, acc[db]);
+        }
       }
+      if (!residual) dsum += part;
+      return pmax;
+    };
+    const unsigned off = (kt % kDqRing) * kDqSlotBytes;
+    if (wave_any(tile(false, off) > kSplitThreshold)) {
+      unsigned off2 = off;
+      asm volatile("" : "+v"(off2));
+      tile(true, off2);
     }
   }
 
@@ -570,21 +562,40 @@ __global__ __launch_bounds__(64 * HPW, 2) void attn_sink_bwd_dq_kernel(BwdArgs a
 }
 
 // ------------------------------------------------------------------------------------------
-// 4. dL/dS_h = -sum of the head's partials (one wave per head, fixed summation order).
+// 4. Finish: dK = scale * (sum of the head halves' partials), dV = sum of the partials (blocks
+//    below n_sum_blocks, grid-stride), and dL/dS_h = -(sum of the partials of head h) (one block
+//    per head after those, fixed summation order).
 // ------------------------------------------------------------------------------------------
-__global__ __launch_bounds__(64) void attn_sink_bwd_dsink_kernel(BwdArgs a) {
-  const int h = blockIdx.x;
-  float acc = 0.0f;
-  for (int i = threadIdx.x; i < a.n_slots; i += 64) acc += a.dsink_part[(size_t)h * a.n_slots + i];
+__global__ __launch_bounds__(256) void attn_sink_bwd_finish_kernel(BwdArgs a, int n_sum_blocks) {
+  if ((int)blockIdx.x >= n_sum_blocks) {
+    const int h = blockIdx.x - n_sum_blocks;
+    __shared__ float part[4];
+    float acc = 0.0f;
+    for (int i = threadIdx.x; i < a.n_slots; i += 256) acc += a.dsink_part[(size_t)h * a.n_slots + i];
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
-  if (threadIdx.x == 0) a.dsinks[h] = -acc;
+    for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = acc;
+    __syncthreads();
+    if (threadIdx.x == 0) a.dsinks[h] = -(part[0] + part[1] + part[2] + part[3]);
+    return;
+  }
+  const size_t plane4 = (size_t)a.T * a.Hkv * (kHeadDim / 4);  // float4 per partial plane
+  const f32x4* p = reinterpret_cast<const f32x4*>(a.dkv_part);
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < plane4; i += (size_t)n_sum_blocks * blockDim.x) {
+    f32x4 k4 = p[i], v4 = p[a.n_halves * plane4 + i];
+    for (int hh = 1; hh < a.n_halves; ++hh) {
+      k4 += p[hh * plane4 + i];
+      v4 += p[(a.n_halves + hh) * plane4 + i];
+    }
+    reinterpret_cast<f32x4*>(a.dk)[i] = k4 * a.scale;
+    reinterpret_cast<f32x4*>(a.dv)[i] = v4;
+  }
 }
 
 }  // namespace
 
 hipError_t launch_bwd_prep(const BwdArgs& a, hipStream_t stream) {
-  long long nblocks = (long long)a.Hq * ((a.T + 15) / 16);
+  long long nblocks = (long long)a.Hq * ((a.T + 63) / 64);
   if (nblocks < 1) nblocks = 1;  // still clears the dSink partials when T = 0
   hipLaunchKernelGGL(attn_sink_bwd_prep_kernel, dim3((unsigned)nblocks), dim3(256), 0, stream, a);
   return hipGetLastError();
@@ -601,15 +612,6 @@ hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_dkdv_sum(const BwdArgs& a, hipStream_t stream) {
-  const long long n4 = (long long)a.T * a.Hkv * (kHeadDim / 4);
-  if (n4 <= 0) return hipSuccess;
-  long long nblocks = (n4 + 255) / 256;
-  if (nblocks > 8192) nblocks = 8192;
-  hipLaunchKernelGGL(attn_sink_bwd_dkdv_sum_kernel, dim3((unsigned)nblocks), dim3(256), 0, stream, a);
-  return hipGetLastError();
-}
-
 hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream) {
   const long long nblocks = (long long)a.n_qblocks * (a.Hq / a.hpw) * a.B;
   if (nblocks <= 0) return hipSuccess;
@@ -622,8 +624,11 @@ hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_dsink(const BwdArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL(attn_sink_bwd_dsink_kernel, dim3((unsigned)a.Hq), dim3(64), 0, stream, a);
+hipError_t launch_bwd_finish(const BwdArgs& a, hipStream_t stream) {
+  const long long n4 = (long long)a.T * a.Hkv * (kHeadDim / 4);
+  long long nsum = (n4 + 255) / 256;
+  if (nsum > 4096) nsum = 4096;
+  hipLaunchKernelGGL(attn_sink_bwd_finish_kernel, dim3((unsigned)(nsum + a.Hq)), dim3(256), 0, stream, a, (int)nsum);
   return hipGetLastError();
 }
 

@@ -12,11 +12,10 @@ constexpr int kKvKeysPerBlock = 64;   // keys per workgroup in the column-parall
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
 
 // Backward passes, in enqueue order.
-constexpr int kBwdNumKernels = 5;
-hipError_t launch_bwd_prep(const BwdArgs& a, hipStream_t stream);      // -LSE/scale, -D_i, zero dSink partials
-hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream);      // dK, dV partials per head half
-hipError_t launch_bwd_dkdv_sum(const BwdArgs& a, hipStream_t stream);  // dK, dV = sum of the halves
-hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream);        // dQ, dSink partials
-hipError_t launch_bwd_dsink(const BwdArgs& a, hipStream_t stream);     // dSink = -sum partials
+constexpr int kBwdNumKernels = 4;
+hipError_t launch_bwd_prep(const BwdArgs& a, hipStream_t stream);    // -LSE/scale, -D_i, zero dSink partials
+hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream);    // dK, dV partials per head half
+hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream);      // dQ, dSink partials
+hipError_t launch_bwd_finish(const BwdArgs& a, hipStream_t stream);  // dK, dV = sum of halves; dSink
 
 }  // namespace attn_sink

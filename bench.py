@@ -47,9 +47,8 @@ KERNEL_FLOPS_PER_PAIR_D = {
     "attn_sink_fwd_kernel": 4,
     "attn_sink_bwd_prep_kernel": 0,
     "attn_sink_bwd_dkdv_kernel": 8,
-    "attn_sink_bwd_dkdv_sum_kernel": 0,
     "attn_sink_bwd_dq_kernel": 2,
-    "attn_sink_bwd_dsink_kernel": 0,
+    "attn_sink_bwd_finish_kernel": 0,
 }
 
 
@@ -84,9 +83,8 @@ def kernel_bytes(name: str, T: int, hq: int, hkv: int, d: int) -> int:
         "attn_sink_fwd_kernel": q + kv + o32 + rows,
         "attn_sink_bwd_prep_kernel": o32 + q + rows + 2 * rows,
         "attn_sink_bwd_dkdv_kernel": 2 * q + kv + 2 * rows + dkv32,
-        "attn_sink_bwd_dkdv_sum_kernel": dkv32,
         "attn_sink_bwd_dq_kernel": 2 * q + kv + 2 * rows + o32,
-        "attn_sink_bwd_dsink_kernel": 0,
+        "attn_sink_bwd_finish_kernel": dkv32,
     }[name]
 
 
