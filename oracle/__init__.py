@@ -14,3 +14,4 @@ from .sink_attention import (  # noqa: F401
     dsink_heads,
     visible,
 )
+from .decode import decode_forward  # noqa: F401,E402
