@@ -16,8 +16,8 @@ from typing import Optional, Sequence
 
 import torch
 
-__all__ = ["fwd", "bwd", "bwd_workspace_bytes", "bwd_kernel_names", "library_path", "load_library",
-           "AttnSinkError", "ERROR_CODES", "HEAD_DIM"]
+__all__ = ["fwd", "bwd", "decode_fwd", "bwd_workspace_bytes", "decode_workspace_bytes", "bwd_kernel_names",
+           "library_path", "load_library", "AttnSinkError", "ERROR_CODES", "HEAD_DIM"]
 
 HEAD_DIM = 64
 _PKG_DIR = os.path.dirname(os.path.abspath(__file__))
@@ -42,6 +42,14 @@ class Shape(ctypes.Structure):
     _fields_ = [("total_tokens", ctypes.c_int32), ("num_seqs", ctypes.c_int32), ("max_seqlen", ctypes.c_int32),
                 ("num_heads_q", ctypes.c_int32), ("num_heads_kv", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("softmax_scale", ctypes.c_float), ("out_dtype", ctypes.c_int32)]
+
+
+class DecodeShape(ctypes.Structure):
+    """Mirror of ``attn_sink_decode_shape`` in include/attn_sink.h."""
+    _fields_ = [("total_q", ctypes.c_int32), ("total_k", ctypes.c_int32), ("num_seqs", ctypes.c_int32),
+                ("max_q", ctypes.c_int32), ("max_k", ctypes.c_int32), ("num_heads_q", ctypes.c_int32),
+                ("num_heads_kv", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
+                ("out_dtype", ctypes.c_int32)]
 
 
 def library_path() -> str:
@@ -71,6 +79,11 @@ def load_library() -> ctypes.CDLL:
     lib.attn_sink_bwd_num_kernels.restype = i32
     lib.attn_sink_bwd_kernel_name.argtypes = [i32]
     lib.attn_sink_bwd_kernel_name.restype = ctypes.c_char_p
+    dshp = ctypes.POINTER(DecodeShape)
+    lib.attn_sink_decode_workspace_bytes.argtypes = [dshp]
+    lib.attn_sink_decode_workspace_bytes.restype = sz
+    lib.attn_sink_decode_fwd.argtypes = [vp, vp, vp, vp, i32, vp, vp, dshp, vp, sz, vp, vp, vp]
+    lib.attn_sink_decode_fwd.restype = i32
     lib.attn_sink_strerror.argtypes = [i32]
     lib.attn_sink_strerror.restype = ctypes.c_char_p
     _lib = lib
@@ -179,3 +192,55 @@ def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, sinks: torch.Tensor, 
     if rc != 0:
         raise AttnSinkError(rc, "attn_sink_bwd")
     return dq, dk, dv, dsinks
+
+
+_OUT_DTYPES = {torch.float32: 0, torch.bfloat16: 1}
+
+
+def make_decode_shape(q: torch.Tensor, k: torch.Tensor, cu_seqlens_q: torch.Tensor, max_q: int, max_k: int,
+                      softmax_scale: Optional[float], out_dtype: torch.dtype) -> DecodeShape:
+    if out_dtype not in _OUT_DTYPES:
+        raise TypeError(f"out_dtype must be float32 or bfloat16, got {out_dtype}")
+    return DecodeShape(int(q.shape[0]), int(k.shape[0]), int(cu_seqlens_q.numel()) - 1, int(max_q), int(max_k),
+                       int(q.shape[1]), int(k.shape[1]), int(q.shape[2]),
+                       float(softmax_scale) if softmax_scale else 0.0, _OUT_DTYPES[out_dtype])
+
+
+def decode_workspace_bytes(q: torch.Tensor, k: torch.Tensor, cu_seqlens_q: torch.Tensor, max_q: int,
+                           max_k: int) -> int:
+    shape = make_decode_shape(q, k, cu_seqlens_q, max_q, max_k, None, torch.float32)
+    return int(load_library().attn_sink_decode_workspace_bytes(ctypes.byref(shape)))
+
+
+def decode_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, sinks: torch.Tensor, cu_seqlens_q: torch.Tensor,
+               cu_seqlens_k: torch.Tensor, max_q: int, max_k: int, window: int = 0,
+               softmax_scale: Optional[float] = None, out_dtype: torch.dtype = torch.float32,
+               out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+               workspace: Optional[torch.Tensor] = None):
+    """Decode forward: q [Tq,Hq,64] (each sequence's last Nq_b tokens), k/v [Tk,Hkv,64] caches, bf16;
+    sinks [Hq] fp32; cu_seqlens_q / cu_seqlens_k [B+1] int32 (device). Returns (out [Tq,Hq,64] in
+    ``out_dtype``, lse [Hq,Tq] fp32)."""
+    lib = load_library()
+    dev = q.device
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _check(t, n, torch.bfloat16, dev)
+    _check(sinks, "sinks", torch.float32, dev)
+    _check(cu_seqlens_q, "cu_seqlens_q", torch.int32, dev)
+    _check(cu_seqlens_k, "cu_seqlens_k", torch.int32, dev)
+    Tq, Hq, d = q.shape
+    if out is None:
+        out = torch.empty((Tq, Hq, d), dtype=out_dtype, device=dev)
+    if lse is None:
+        lse = torch.empty((Hq, Tq), dtype=torch.float32, device=dev)
+    _check(out, "out", out_dtype, dev)
+    _check(lse, "lse", torch.float32, dev)
+    shape = make_decode_shape(q, k, cu_seqlens_q, max_q, max_k, softmax_scale, out_dtype)
+    need = int(lib.attn_sink_decode_workspace_bytes(ctypes.byref(shape)))
+    if workspace is None:
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
+    rc = lib.attn_sink_decode_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(sinks), int(window), _ptr(cu_seqlens_q),
+                                  _ptr(cu_seqlens_k), ctypes.byref(shape), _ptr(workspace),
+                                  workspace.numel() * workspace.element_size(), _ptr(out), _ptr(lse), _stream(dev))
+    if rc != 0:
+        raise AttnSinkError(rc, "attn_sink_decode_fwd")
+    return out, lse

@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG_DIR, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG_DIR, "libattn_sink.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
-SOURCES = ("fwd.hip", "bwd.hip", "api.hip")
+SOURCES = ("fwd.hip", "bwd.hip", "decode.hip", "api.hip")
 ARCH = "gfx950"
 
 

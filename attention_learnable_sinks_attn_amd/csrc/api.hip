@@ -124,6 +124,48 @@ int bwd_impl(const void* q, const void* k, const void* v, const float* sinks, co
   return ATTN_SINK_OK;
 }
 
+// ---- decode ----
+int check_decode_shape(const attn_sink_decode_shape* s) {
+  if (s == nullptr) return ATTN_SINK_ERR_NULL_PTR;
+  if (s->total_q < 0 || s->total_k < 0 || s->num_seqs < 1 || s->max_q < 0 || s->max_k < 0 ||
+      s->num_heads_q < 1 || s->num_heads_kv < 1 || s->num_heads_q % s->num_heads_kv != 0 ||
+      s->max_q > s->total_q || s->max_k > s->total_k) {
+    return ATTN_SINK_ERR_BAD_SHAPE;
+  }
+  if (s->head_dim != kHeadDim || (s->out_dtype != ATTN_SINK_F32 && s->out_dtype != ATTN_SINK_BF16)) {
+    return ATTN_SINK_ERR_UNSUPPORTED;
+  }
+  if ((long long)s->max_q * (s->num_heads_q / s->num_heads_kv) > 32) return ATTN_SINK_ERR_UNSUPPORTED;
+  if ((long long)s->total_k * s->num_heads_kv * kHeadDim >= (1LL << 40) ||
+      (long long)s->total_q * s->num_heads_q >= (1LL << 31)) {
+    return ATTN_SINK_ERR_BAD_SHAPE;
+  }
+  return ATTN_SINK_OK;
+}
+
+// Key chunks: enough (sequence, KV head, chunk) waves to fill the GPU several times over, each
+// chunk a multiple of 64 keys.
+void decode_chunks(const attn_sink_decode_shape* s, int* n_chunks, int* chunk_keys) {
+  const long long pairs = (long long)s->num_seqs * s->num_heads_kv;
+  const long long target = pairs >= 8192 ? 1 : (8192 + pairs - 1) / pairs;
+  const long long tiles = ((long long)s->max_k + 63) / 64;
+  long long per = tiles <= 0 ? 1 : (tiles + target - 1) / target;
+  if (per < 1) per = 1;
+  *chunk_keys = (int)(64 * per);
+  const long long n = tiles <= 0 ? 1 : (tiles + per - 1) / per;
+  *n_chunks = (int)n;
+}
+
+size_t decode_part_o_bytes(const attn_sink_decode_shape* s, int n_chunks) {
+  return round256((size_t)s->num_seqs * s->num_heads_kv * n_chunks * kHeadDim * 32 * sizeof(float));
+}
+
+size_t decode_workspace_bytes(const attn_sink_decode_shape* s) {
+  int n, ck;
+  decode_chunks(s, &n, &ck);
+  return decode_part_o_bytes(s, n) + round256((size_t)s->num_seqs * s->num_heads_kv * n * 2 * 32 * sizeof(float));
+}
+
 }  // namespace
 
 extern "C" {
@@ -179,6 +221,49 @@ int attn_sink_bwd_timed(const void* q, const void* k, const void* v, const float
                         float* dv, float* dsinks, hipStream_t stream, void* const* events, int num_events) {
   return bwd_impl(q, k, v, sinks, out, lse, dout, causal, window, cu_seqlens, shape, workspace, workspace_bytes, dq,
                   dk, dv, dsinks, stream, events, num_events);
+}
+
+size_t attn_sink_decode_workspace_bytes(const attn_sink_decode_shape* shape) {
+  if (check_decode_shape(shape) != ATTN_SINK_OK) return 0;
+  return decode_workspace_bytes(shape);
+}
+
+int attn_sink_decode_fwd(const void* q, const void* k, const void* v, const float* sinks, int window,
+                         const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, const attn_sink_decode_shape* shape,
+                         void* workspace, size_t workspace_bytes, void* out, float* lse, hipStream_t stream) {
+  int rc = check_decode_shape(shape);
+  if (rc) return rc;
+  if (window < 0) return ATTN_SINK_ERR_BAD_WINDOW;
+  if (sinks == nullptr || cu_seqlens_q == nullptr || cu_seqlens_k == nullptr) return ATTN_SINK_ERR_NULL_PTR;
+  if (shape->total_q > 0 && (!q || !out || !lse)) return ATTN_SINK_ERR_NULL_PTR;
+  if (shape->total_k > 0 && (!k || !v)) return ATTN_SINK_ERR_NULL_PTR;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return ATTN_SINK_ERR_ALIGN;
+  const size_t need = decode_workspace_bytes(shape);
+  if (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)) return ATTN_SINK_ERR_WORKSPACE;
+  if (shape->total_q == 0) return ATTN_SINK_OK;
+
+  DecodeArgs a;
+  a.q = static_cast<const __bf16*>(q);
+  a.k = static_cast<const __bf16*>(k);
+  a.v = static_cast<const __bf16*>(v);
+  a.sinks = sinks;
+  a.cu_q = cu_seqlens_q;
+  a.cu_k = cu_seqlens_k;
+  a.out = out;
+  a.lse = lse;
+  decode_chunks(shape, &a.n_chunks, &a.chunk_keys);
+  a.part_o = static_cast<float*>(workspace);
+  a.part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + decode_part_o_bytes(shape, a.n_chunks));
+  a.Tq = shape->total_q;
+  a.B = shape->num_seqs;
+  a.Hq = shape->num_heads_q;
+  a.Hkv = shape->num_heads_kv;
+  a.G = a.Hq / a.Hkv;
+  a.window = window;
+  a.out_bf16 = shape->out_dtype == ATTN_SINK_BF16 ? 1 : 0;
+  const float scale = shape->softmax_scale > 0.0f ? shape->softmax_scale : 1.0f / sqrtf((float)shape->head_dim);
+  a.scale_log2 = scale * kLog2e;
+  return launch_decode(a, stream) == hipSuccess ? ATTN_SINK_OK : ATTN_SINK_ERR_HIP;
 }
 
 int attn_sink_bwd_num_kernels(void) { return kBwdNumKernels; }

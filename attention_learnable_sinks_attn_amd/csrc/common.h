@@ -285,4 +285,23 @@ struct BwdArgs {
   float scale_log2;   // softmax scale * log2(e)
 };
 
+struct DecodeArgs {
+  const __bf16* q;     // [Tq, Hq, 64]: the new queries, packed by cu_q
+  const __bf16* k;     // [Tk, Hkv, 64]: the caches, packed by cu_k
+  const __bf16* v;
+  const float* sinks;
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  void* out;           // [Tq, Hq, 64], fp32 or bf16 (out_bf16)
+  float* lse;          // [Hq, Tq]
+  float* part_o;       // per (sequence, KV head, chunk): [64][32] unnormalised outputs per column
+  float* part_ml;      // per (sequence, KV head, chunk): [2][32] running max (log2), denominator
+  int Tq, B, Hq, Hkv, G;
+  int n_chunks;        // key chunks per sequence
+  int chunk_keys;      // keys per chunk (multiple of 64)
+  int window;
+  int out_bf16;
+  float scale_log2;
+};
+
 }  // namespace attn_sink

@@ -18,4 +18,7 @@ hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream);    // dK, dV p
 hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream);      // dQ, dSink partials
 hipError_t launch_bwd_finish(const BwdArgs& a, hipStream_t stream);  // dK, dV = sum of halves; dSink
 
+// Inference-shaped forward: per-chunk partials, then the combine with the sink.
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+
 }  // namespace attn_sink

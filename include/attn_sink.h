@@ -122,6 +122,45 @@ int attn_sink_bwd_timed(const void* q, const void* k, const void* v, const float
                         float* dk, float* dv, float* dsinks, hipStream_t stream, void* const* events,
                         int num_events);
 
+/*
+ * Inference-shaped (decode) forward: a few new query tokens per sequence against that sequence's
+ * cached keys and values. Sequence b has Lk_b = cu_seqlens_k[b+1] - cu_seqlens_k[b] cached tokens
+ * (k, v rows, including the new tokens' own keys) and Nq_b = cu_seqlens_q[b+1] - cu_seqlens_q[b]
+ * new queries (q rows), which are the sequence's last Nq_b tokens: new query j sits at position
+ * Lk_b - Nq_b + j and, as in the causal forward, sees the keys at positions <= its own (and, with
+ * window = W > 0, only the last W of them), plus the sink. Same operation as attn_sink_fwd with
+ * causal = 1 restricted to those rows (nmedialink.com "惊爆！GPT-OSS-20B强化学习…", section
+ * "GPT-OSS中的带注意力槽的注意力机制"); results agree with attn_sink_fwd's rows to rounding, not
+ * bitwise (the keys are summed in another order).
+ *
+ *   q      [Tq, Hq, 64] bf16;  k, v [Tk, Hkv, 64] bf16;  sinks [Hq] fp32
+ *   out    [Tq, Hq, 64] fp32 (out_dtype ATTN_SINK_F32) or bf16 (ATTN_SINK_BF16)
+ *   lse    [Hq, Tq] fp32, natural log, sink included
+ *   cu_seqlens_q / cu_seqlens_k  [B+1] int32 on the device, non-decreasing, Nq_b <= Lk_b (trusted)
+ * Requires max_q * (Hq / Hkv) <= 32 (the new queries of one KV head's query heads fill one
+ * 32-column MFMA block), else ATTN_SINK_ERR_UNSUPPORTED. workspace: caller-owned device memory
+ * of at least attn_sink_decode_workspace_bytes(shape) bytes (per-chunk partial results); its
+ * contents on entry do not matter. Same ownership, asynchrony and error conventions as above.
+ */
+typedef struct attn_sink_decode_shape {
+  int32_t total_q;      /* Tq = cu_seqlens_q[B] */
+  int32_t total_k;      /* Tk = cu_seqlens_k[B] */
+  int32_t num_seqs;     /* B >= 1 */
+  int32_t max_q;        /* >= every Nq_b, >= 0 */
+  int32_t max_k;        /* >= every Lk_b, >= 0 (sizes the key chunks) */
+  int32_t num_heads_q;  /* Hq */
+  int32_t num_heads_kv; /* Hkv, divides Hq */
+  int32_t head_dim;     /* must be 64 */
+  float softmax_scale;  /* <= 0 selects 1/sqrt(head_dim) */
+  int32_t out_dtype;    /* ATTN_SINK_F32 or ATTN_SINK_BF16 */
+} attn_sink_decode_shape;
+
+size_t attn_sink_decode_workspace_bytes(const attn_sink_decode_shape* shape);
+
+int attn_sink_decode_fwd(const void* q, const void* k, const void* v, const float* sinks, int window,
+                         const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, const attn_sink_decode_shape* shape,
+                         void* workspace, size_t workspace_bytes, void* out, float* lse, hipStream_t stream);
+
 /* Number of kernels attn_sink_bwd enqueues, and the name of kernel i (static string, or NULL). */
 int attn_sink_bwd_num_kernels(void);
 const char* attn_sink_bwd_kernel_name(int i);

@@ -137,3 +137,61 @@ def test_binding_raises_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(asa, "_lib", None)
     with pytest.raises(ImportError):
         asa.load_library()
+
+
+def dshape(tq=8, tk=300, B=2, max_q=4, max_k=200, hq=8, hkv=1, d=64, scale=0.0, dtype=0):
+    return asa.DecodeShape(tq, tk, B, max_q, max_k, hq, hkv, d, scale, dtype)
+
+
+def decode(lib, s, ws=P, ws_bytes=None, window=0, **ptrs):
+    p = dict(q=P, k=P, v=P, sinks=P, cuq=P, cuk=P, out=P, lse=P)
+    p.update(ptrs)
+    if ws_bytes is None:
+        ws_bytes = lib.attn_sink_decode_workspace_bytes(ctypes.byref(s)) if s is not None else 0
+    return lib.attn_sink_decode_fwd(p["q"], p["k"], p["v"], p["sinks"], window, p["cuq"], p["cuk"],
+                                    ctypes.byref(s) if s is not None else None, ws, ws_bytes, p["out"], p["lse"], None)
+
+
+@needs_lib
+def test_decode_argument_errors():
+    lib = asa.load_library()
+    assert decode(lib, None) == -1
+    assert decode(lib, dshape(), q=None) == -1
+    assert decode(lib, dshape(), k=None) == -1
+    assert decode(lib, dshape(), sinks=None) == -1
+    assert decode(lib, dshape(), cuk=None) == -1
+    assert decode(lib, dshape(), lse=None) == -1
+    assert decode(lib, dshape(tq=-1)) == -2
+    assert decode(lib, dshape(B=0)) == -2
+    assert decode(lib, dshape(hq=6, hkv=4)) == -2
+    assert decode(lib, dshape(max_q=9)) == -2    # above total_q
+    assert decode(lib, dshape(max_k=301)) == -2  # above total_k
+    assert decode(lib, dshape(d=128)) == -3
+    assert decode(lib, dshape(dtype=2)) == -3
+    # the new queries of one KV head's query heads must fit 32 MFMA columns
+    assert decode(lib, dshape(max_q=5, hq=8, hkv=1)) == -3
+    assert decode(lib, dshape(max_q=8, hq=64, hkv=8)) == -3
+    assert decode(lib, dshape(max_q=2, hq=32, hkv=1)) == -3
+    assert decode(lib, dshape(), window=-1) == -4
+    s = dshape()
+    need = lib.attn_sink_decode_workspace_bytes(ctypes.byref(s))
+    assert decode(lib, s, ws=None) == -5
+    assert decode(lib, s, ws_bytes=need - 1) == -5
+    assert decode(lib, s, ws=PM) == -5
+    assert decode(lib, s, k=PM) == -7
+    assert decode(lib, s, out=PM) == -7
+    # nothing to compute: succeeds without touching memory (no HIP call is made)
+    assert decode(lib, dshape(tq=0, max_q=0), q=None, out=None, lse=None) == 0
+
+
+@needs_lib
+def test_decode_workspace_formula():
+    lib = asa.load_library()
+    # 8 sequences x 8 KV heads = 64 (sequence, KV head) pairs; the key axis is split so that about
+    # 8192 waves run: 32768 keys = 512 tiles of 64 -> chunks of 4 tiles -> 128 chunks per pair. Each
+    # chunk keeps a 64 x 32 fp32 partial output and a running max and sum per column.
+    s = dshape(tq=8, tk=200000, B=8, max_q=1, max_k=32768, hq=64, hkv=8)
+    need = lib.attn_sink_decode_workspace_bytes(ctypes.byref(s))
+    assert need == 64 * 128 * 64 * 32 * 4 + 64 * 128 * 2 * 32 * 4
+    assert lib.attn_sink_decode_workspace_bytes(None) == 0
+    assert lib.attn_sink_decode_workspace_bytes(ctypes.byref(dshape(max_q=5))) == 0

@@ -1,0 +1,134 @@
+"""Parity of the HIP decode (inference-shaped) forward, through the C ABI, against the fp64 oracle,
+and its consistency with the training forward.
+
+Tolerances against the oracle are those of the training forward: max-abs 1e-2 on O (fp32 or bf16
+output) and 1e-3 on the fp32 LSE. Small cases compare every element and cover several key chunks
+with ragged tails, GQA groups of 1 to 8, per-sequence numbers of new tokens (0 included), a
+sliding window, sinks at -inf, sequences made only of new tokens and an empty batch. The
+full-size cases run the 8-sequence, 16k-32k-key GPT-OSS-shaped caches in the launch
+configuration the bench times and compare every output.
+
+Train/inference consistency: the decode forward and the training forward compute the same rows
+with the same bf16 rounding of P but sum the keys in another order and against another running
+maximum, so they agree to rounding, not bitwise; the test bounds the difference well inside the
+parity tolerance (CONSIST_TOL).
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import attention_learnable_sinks_attn_amd as asa
+import oracle
+from workloads import last_rows, make_decode_inputs, make_decode_workload_inputs, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+TOL_OUT, TOL_LSE = 1e-2, 1e-3
+CONSIST_TOL = {"out": 4e-3, "lse": 1e-4}
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def run_decode(d, out_dtype=torch.float32, scale=None):
+    dev = torch.device("cuda:0")
+    q, k, v = (t.to(dev).contiguous() for t in (d.q, d.k, d.v))
+    out, lse = asa.decode_fwd(q, k, v, d.sinks.to(dev), d.cu_q.to(dev), d.cu_k.to(dev), d.max_q, d.max_k,
+                              window=d.window, softmax_scale=scale, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+def check_against_oracle(d, out, lse, scale=None):
+    ro, rl = oracle.decode_forward(d.q, d.k, d.v, d.sinks, d.cu_q, d.cu_k, d.window, scale)
+    o = out.double().cpu().numpy()
+    l = lse.double().cpu().numpy()
+    assert np.isfinite(o).all(), "out has non-finite values"
+    eo = float(np.max(np.abs(o - ro))) if o.size else 0.0
+    fin = np.isfinite(rl)
+    assert (np.isfinite(l) == fin).all(), "LSE -inf pattern differs"
+    el = float(np.max(np.abs(l[fin] - rl[fin]))) if fin.any() else 0.0
+    say(f"  out: max-abs err {eo:.3e}   lse: max-abs err {el:.3e}")
+    assert eo <= TOL_OUT, f"out: max-abs err {eo:.3e} > {TOL_OUT}"
+    assert el <= TOL_LSE, f"lse: max-abs err {el:.3e} > {TOL_LSE}"
+
+
+# name: (cache lengths, new tokens per sequence, Hq, Hkv, window, kwargs)
+SMALL = {
+    "g8_nq1": ((100, 37, 260, 1), 1, 8, 1, 0, {}),
+    "g8_nq4_bf16": ((300, 64, 129), 4, 16, 2, 0, {"out_dtype": torch.bfloat16}),
+    "g4_mixed_nq": ((200, 70, 5, 333), (2, 0, 5, 8), 8, 2, 0, {}),
+    "g2_window50": ((400, 90, 33), 3, 4, 2, 50, {}),
+    "g1_nq32": ((300, 40), (32, 17), 2, 2, 0, {}),
+    "g8_window1": ((129, 64), 2, 8, 1, 1, {"out_dtype": torch.bfloat16}),
+    "all_new_tokens": ((5, 8, 3), (5, 8, 3), 8, 2, 0, {}),
+    "neg_inf_sinks": ((150, 77), 2, 8, 1, 0, {"sinks": float("-inf")}),
+    "big_sinks": ((257, 31), 1, 16, 2, 0, {"sink_scale": 3.0}),
+    "scale_0p3": ((190,), 4, 8, 1, 0, {"scale": 0.3}),
+    "window_ge_len": ((70, 20), 3, 8, 2, 500, {}),
+}
+
+
+@pytest.mark.parametrize("name", sorted(SMALL))
+def test_decode_small(name):
+    lengths, nq, hq, hkv, window, kw = SMALL[name]
+    kw = dict(kw)
+    out_dtype = kw.pop("out_dtype", torch.float32)
+    scale = kw.pop("scale", None)
+    sink_value = kw.pop("sinks", None)
+    d = make_decode_inputs(lengths, nq, hq, hkv, window=window, seed=11, **kw)
+    if sink_value is not None:
+        d.sinks.fill_(sink_value)
+    say(f"decode {name}: Lk={lengths} nq={nq} heads {hq}/{hkv} window={window} out={out_dtype}")
+    out, lse = run_decode(d, out_dtype, scale)
+    assert out.dtype == out_dtype
+    check_against_oracle(d, out, lse, scale)
+
+
+def test_decode_empty_batch():
+    d = make_decode_inputs((10, 20), 0, 8, 1, seed=1)
+    say("decode: no new tokens")
+    out, lse = run_decode(d)
+    assert out.shape == (0, 8, 64) and lse.shape == (8, 0)
+
+
+def test_decode_rejects_too_many_columns():
+    d = make_decode_inputs((40, 50), 5, 8, 1, seed=1)  # 5 new tokens x 8 heads > 32 columns
+    say("decode: unsupported max_q * group")
+    with pytest.raises(asa.AttnSinkError) as e:
+        run_decode(d)
+    assert e.value.code == -3
+
+
+@pytest.mark.parametrize("name", ["decode32k", "decode32k_nq4", "decode32k_window"])
+def test_decode_full_size(name):
+    d = make_decode_workload_inputs(name, seed=0)
+    say(f"decode {name}: Lk={[int(x) for x in (d.cu_k[1:] - d.cu_k[:-1])]} max_q={d.max_q}")
+    out, lse = run_decode(d, torch.bfloat16)
+    check_against_oracle(d, out, lse)
+
+
+@pytest.mark.parametrize("window", [0, 128])
+def test_train_inference_consistency(window):
+    """Training forward over whole packed sequences vs the decode forward over their last tokens."""
+    lengths = (1000, 3000, 517, 64, 2049)
+    nq = (1, 4, 3, 2, 4)
+    inp = make_inputs(lengths, 64, 8, causal=True, window=window, seed=5)
+    dev = torch.device("cuda:0")
+    q, k, v = (t.to(dev).contiguous() for t in (inp.q, inp.k, inp.v))
+    sinks, cu = inp.sinks.to(dev), inp.cu_seqlens.to(dev)
+    say(f"consistency: lengths {lengths} new tokens {nq} window {window}")
+    out_t, lse_t = asa.fwd(q, k, v, sinks, cu, inp.max_seqlen, True, window)
+    rows, cu_q = last_rows(inp.cu_seqlens, nq)
+    rows_t = torch.tensor(rows, device=dev)
+    out_d, lse_d = asa.decode_fwd(q[rows_t].contiguous(), k, v, sinks, cu_q.to(dev), cu, max(nq), inp.max_seqlen,
+                                  window=window)
+    torch.cuda.synchronize()
+    do = (out_d - out_t[rows_t]).abs().max().item()
+    dl = (lse_d - lse_t[:, rows_t]).abs().max().item()
+    say(f"  training vs decode: out max-abs diff {do:.3e}, lse max-abs diff {dl:.3e}")
+    assert do <= CONSIST_TOL["out"] and dl <= CONSIST_TOL["lse"]

@@ -147,3 +147,63 @@ def visible_pairs(lengths, causal: bool, window: int) -> int:
         else:
             total += L * (L + 1) // 2
     return total
+
+
+# ---- inference-shaped (decode) inputs ----------------------------------------------------------
+# Recipe: cache lengths Lk_b drawn first with numpy.default_rng(seed).integers(lo, hi, B,
+# endpoint=True); then a torch.Generator(seed) draws fp32 N(0,1) in the order k, v (all Tk cached
+# tokens), q (the Nq new tokens of every sequence, which are its last Nq tokens), sinks; q, k, v
+# are rounded to bf16, the sinks stay fp32. These GPT-OSS-shaped tensors stand in for a serving
+# engine's KV cache during RL rollouts; no dataset or weight is used.
+
+DECODE_WORKLOADS = {
+    # name: (B, Lk range, Nq, Hq, Hkv, window)
+    "decode32k": (8, (16384, 32768), 1, 64, 8, 0),
+    "decode32k_nq4": (8, (16384, 32768), 4, 64, 8, 0),
+    "decode32k_window": (8, (16384, 32768), 1, 64, 8, 128),
+}
+
+
+@dataclass
+class DecodeInputs:
+    q: torch.Tensor            # [Tq, Hq, d] bf16 (CPU): the new tokens' queries
+    k: torch.Tensor            # [Tk, Hkv, d] bf16: the caches (new tokens included)
+    v: torch.Tensor
+    sinks: torch.Tensor        # [Hq] fp32
+    cu_q: torch.Tensor         # [B+1] int32
+    cu_k: torch.Tensor         # [B+1] int32
+    max_q: int
+    max_k: int
+    window: int
+
+
+def make_decode_inputs(lengths_k, nq, hq: int, hkv: int, d: int = 64, window: int = 0, seed: int = 0,
+                       sink_scale: float = 1.0) -> DecodeInputs:
+    lengths_k = tuple(int(x) for x in lengths_k)
+    nqs = [int(nq)] * len(lengths_k) if isinstance(nq, int) else [int(x) for x in nq]
+    nqs = tuple(min(a, b) for a, b in zip(nqs, lengths_k))  # a sequence has at most Lk new tokens
+    Tk, Tq = sum(lengths_k), sum(nqs)
+    gen = torch.Generator().manual_seed(seed)
+    k = torch.randn((Tk, hkv, d), generator=gen, dtype=torch.float32).to(torch.bfloat16)
+    v = torch.randn((Tk, hkv, d), generator=gen, dtype=torch.float32).to(torch.bfloat16)
+    q = torch.randn((Tq, hq, d), generator=gen, dtype=torch.float32).to(torch.bfloat16)
+    sinks = torch.randn((hq,), generator=gen, dtype=torch.float32) * sink_scale
+    return DecodeInputs(q, k, v, sinks, cu_from_lengths(nqs), cu_from_lengths(lengths_k), max(nqs, default=0),
+                        max(lengths_k, default=0), int(window))
+
+
+def make_decode_workload_inputs(name: str, seed: int = 0) -> DecodeInputs:
+    B, (lo, hi), nq, hq, hkv, window = DECODE_WORKLOADS[name]
+    lengths = np.random.default_rng(seed).integers(lo, hi, B, endpoint=True)
+    return make_decode_inputs(lengths, nq, hq, hkv, 64, window, seed)
+
+
+def last_rows(cu_seqlens, nq):
+    """Row indices of the last nq[b] tokens of every packed sequence, and their offsets [B+1]."""
+    cu = [int(x) for x in cu_seqlens]
+    rows, cu_q = [], [0]
+    for b in range(len(cu) - 1):
+        n = min(int(nq[b]), cu[b + 1] - cu[b])
+        rows += list(range(cu[b + 1] - n, cu[b + 1]))
+        cu_q.append(cu_q[-1] + n)
+    return rows, torch.tensor(cu_q, dtype=torch.int32)
