@@ -17,7 +17,7 @@ from typing import Optional, Sequence
 import torch
 
 __all__ = ["fwd", "bwd", "decode_fwd", "bwd_workspace_bytes", "decode_workspace_bytes", "bwd_kernel_names",
-           "library_path", "load_library", "AttnSinkError", "ERROR_CODES", "HEAD_DIM"]
+           "decode_kernel_names", "library_path", "load_library", "AttnSinkError", "ERROR_CODES", "HEAD_DIM"]
 
 HEAD_DIM = 64
 _PKG_DIR = os.path.dirname(os.path.abspath(__file__))
@@ -84,6 +84,12 @@ def load_library() -> ctypes.CDLL:
     lib.attn_sink_decode_workspace_bytes.restype = sz
     lib.attn_sink_decode_fwd.argtypes = [vp, vp, vp, vp, i32, vp, vp, dshp, vp, sz, vp, vp, vp]
     lib.attn_sink_decode_fwd.restype = i32
+    lib.attn_sink_decode_fwd_timed.argtypes = [vp, vp, vp, vp, i32, vp, vp, dshp, vp, sz, vp, vp, vp,
+                                               ctypes.POINTER(ctypes.c_void_p), i32]
+    lib.attn_sink_decode_fwd_timed.restype = i32
+    lib.attn_sink_decode_num_kernels.restype = i32
+    lib.attn_sink_decode_kernel_name.argtypes = [i32]
+    lib.attn_sink_decode_kernel_name.restype = ctypes.c_char_p
     lib.attn_sink_strerror.argtypes = [i32]
     lib.attn_sink_strerror.restype = ctypes.c_char_p
     _lib = lib
@@ -206,6 +212,11 @@ def make_decode_shape(q: torch.Tensor, k: torch.Tensor, cu_seqlens_q: torch.Tens
                        float(softmax_scale) if softmax_scale else 0.0, _OUT_DTYPES[out_dtype])
 
 
+def decode_kernel_names():
+    lib = load_library()
+    return [lib.attn_sink_decode_kernel_name(i).decode() for i in range(lib.attn_sink_decode_num_kernels())]
+
+
 def decode_workspace_bytes(q: torch.Tensor, k: torch.Tensor, cu_seqlens_q: torch.Tensor, max_q: int,
                            max_k: int) -> int:
     shape = make_decode_shape(q, k, cu_seqlens_q, max_q, max_k, None, torch.float32)
@@ -216,10 +227,11 @@ def decode_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, sinks: torch.T
                cu_seqlens_k: torch.Tensor, max_q: int, max_k: int, window: int = 0,
                softmax_scale: Optional[float] = None, out_dtype: torch.dtype = torch.float32,
                out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-               workspace: Optional[torch.Tensor] = None):
+               workspace: Optional[torch.Tensor] = None, events: Optional[Sequence[int]] = None):
     """Decode forward: q [Tq,Hq,64] (each sequence's last Nq_b tokens), k/v [Tk,Hkv,64] caches, bf16;
     sinks [Hq] fp32; cu_seqlens_q / cu_seqlens_k [B+1] int32 (device). Returns (out [Tq,Hq,64] in
-    ``out_dtype``, lse [Hq,Tq] fp32)."""
+    ``out_dtype``, lse [Hq,Tq] fp32). ``events``: optional raw hipEvent_t handles (num kernels + 1)
+    recorded around each kernel."""
     lib = load_library()
     dev = q.device
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
@@ -238,9 +250,14 @@ def decode_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, sinks: torch.T
     need = int(lib.attn_sink_decode_workspace_bytes(ctypes.byref(shape)))
     if workspace is None:
         workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
-    rc = lib.attn_sink_decode_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(sinks), int(window), _ptr(cu_seqlens_q),
-                                  _ptr(cu_seqlens_k), ctypes.byref(shape), _ptr(workspace),
-                                  workspace.numel() * workspace.element_size(), _ptr(out), _ptr(lse), _stream(dev))
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(sinks), int(window), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k),
+            ctypes.byref(shape), _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(out), _ptr(lse),
+            _stream(dev))
+    if events is None:
+        rc = lib.attn_sink_decode_fwd(*args)
+    else:
+        arr = (ctypes.c_void_p * len(events))(*events)
+        rc = lib.attn_sink_decode_fwd_timed(*args, arr, len(events))
     if rc != 0:
         raise AttnSinkError(rc, "attn_sink_decode_fwd")
     return out, lse

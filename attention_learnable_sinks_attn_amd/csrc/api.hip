@@ -4,6 +4,8 @@
 #include <stdint.h>
 
 #include "attn_sink.h"
+#include <algorithm>
+
 #include "kernels.h"
 
 using namespace attn_sink;
@@ -137,22 +139,44 @@ int check_decode_shape(const attn_sink_decode_shape* s) {
   }
   if ((long long)s->max_q * (s->num_heads_q / s->num_heads_kv) > 32) return ATTN_SINK_ERR_UNSUPPORTED;
   if ((long long)s->total_k * s->num_heads_kv * kHeadDim >= (1LL << 40) ||
-      (long long)s->total_q * s->num_heads_q >= (1LL << 31)) {
+      (long long)s->total_q * s->num_heads_q >= (1LL << 31) ||
+      (long long)s->num_seqs * s->num_heads_kv * 32 >= (1LL << 31) ||  // workgroups of one launch
+      (s->total_q > 0 && s->max_q < 1)) {
     return ATTN_SINK_ERR_BAD_SHAPE;
   }
   return ATTN_SINK_OK;
 }
 
-// Key chunks: enough (sequence, KV head, chunk) waves to fill the GPU several times over, each
-// chunk a multiple of 64 keys.
-void decode_chunks(const attn_sink_decode_shape* s, int* n_chunks, int* chunk_keys) {
+// Key chunks: about 4096 (sequence, KV head, chunk) waves, five rounds of the 768 that fit the
+// GPU at once (three 48 KB rings per CU), each chunk a whole number of 64-key tiles. `tiles` is
+// the most tiles any sequence's new tokens see. Fewer, longer chunks leave the last round's CUs
+// idle; more, shorter ones spend more time filling each wave's ring and merging partials.
+void split_keys(long long pairs, long long tiles, long long* per, long long* n) {
+  const long long target = pairs >= 4096 ? 1 : (4096 + pairs - 1) / pairs;
+  *per = tiles <= 0 ? 1 : (tiles + target - 1) / target;
+  *n = tiles <= 0 ? 1 : (tiles + *per - 1) / *per;
+}
+
+// Chunks for a call with the given window. The workspace is sized for window 0; a window only
+// shortens the span to chunk (the keys from the 64-aligned start of the first visible one), and the
+// chunk count never exceeds the workspace's.
+void decode_chunks(const attn_sink_decode_shape* s, int window, int* n_chunks, int* chunk_keys) {
   const long long pairs = (long long)s->num_seqs * s->num_heads_kv;
-  const long long target = pairs >= 8192 ? 1 : (8192 + pairs - 1) / pairs;
-  const long long tiles = ((long long)s->max_k + 63) / 64;
-  long long per = tiles <= 0 ? 1 : (tiles + target - 1) / target;
-  if (per < 1) per = 1;
+  long long per, n;
+  split_keys(pairs, ((long long)s->max_k + 63) / 64, &per, &n);
+  if (window > 0) {
+    const long long span = std::min<long long>(s->max_k, (long long)window + s->max_q - 1 + 63);
+    const long long tiles = (span + 63) / 64;
+    long long per_w, n_w;
+    split_keys(pairs, tiles, &per_w, &n_w);
+    if (n_w > n) {
+      per_w = (tiles + n - 1) / n;
+      n_w = (tiles + per_w - 1) / per_w;
+    }
+    per = per_w;
+    n = n_w;
+  }
   *chunk_keys = (int)(64 * per);
-  const long long n = tiles <= 0 ? 1 : (tiles + per - 1) / per;
   *n_chunks = (int)n;
 }
 
@@ -162,7 +186,7 @@ size_t decode_part_o_bytes(const attn_sink_decode_shape* s, int n_chunks) {
 
 size_t decode_workspace_bytes(const attn_sink_decode_shape* s) {
   int n, ck;
-  decode_chunks(s, &n, &ck);
+  decode_chunks(s, 0, &n, &ck);
   return decode_part_o_bytes(s, n) + round256((size_t)s->num_seqs * s->num_heads_kv * n * 2 * 32 * sizeof(float));
 }
 
@@ -228,11 +252,13 @@ size_t attn_sink_decode_workspace_bytes(const attn_sink_decode_shape* shape) {
   return decode_workspace_bytes(shape);
 }
 
-int attn_sink_decode_fwd(const void* q, const void* k, const void* v, const float* sinks, int window,
-                         const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, const attn_sink_decode_shape* shape,
-                         void* workspace, size_t workspace_bytes, void* out, float* lse, hipStream_t stream) {
+int attn_sink_decode_fwd_timed(const void* q, const void* k, const void* v, const float* sinks, int window,
+                               const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                               const attn_sink_decode_shape* shape, void* workspace, size_t workspace_bytes, void* out,
+                               float* lse, hipStream_t stream, void* const* events, int num_events) {
   int rc = check_decode_shape(shape);
   if (rc) return rc;
+  if (events != nullptr && num_events != kDecodeNumKernels + 1) return ATTN_SINK_ERR_BAD_SHAPE;
   if (window < 0) return ATTN_SINK_ERR_BAD_WINDOW;
   if (sinks == nullptr || cu_seqlens_q == nullptr || cu_seqlens_k == nullptr) return ATTN_SINK_ERR_NULL_PTR;
   if (shape->total_q > 0 && (!q || !out || !lse)) return ATTN_SINK_ERR_NULL_PTR;
@@ -240,7 +266,13 @@ int attn_sink_decode_fwd(const void* q, const void* k, const void* v, const floa
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return ATTN_SINK_ERR_ALIGN;
   const size_t need = decode_workspace_bytes(shape);
   if (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)) return ATTN_SINK_ERR_WORKSPACE;
-  if (shape->total_q == 0) return ATTN_SINK_OK;
+  hipEvent_t const* ev = reinterpret_cast<hipEvent_t const*>(events);
+  if (shape->total_q == 0) {  // nothing to compute; the events still mark the (empty) interval
+    for (int i = 0; ev && i <= kDecodeNumKernels; ++i) {
+      if (hipEventRecord(ev[i], stream) != hipSuccess) return ATTN_SINK_ERR_HIP;
+    }
+    return ATTN_SINK_OK;
+  }
 
   DecodeArgs a;
   a.q = static_cast<const __bf16*>(q);
@@ -251,7 +283,7 @@ int attn_sink_decode_fwd(const void* q, const void* k, const void* v, const floa
   a.cu_k = cu_seqlens_k;
   a.out = out;
   a.lse = lse;
-  decode_chunks(shape, &a.n_chunks, &a.chunk_keys);
+  decode_chunks(shape, window, &a.n_chunks, &a.chunk_keys);
   a.part_o = static_cast<float*>(workspace);
   a.part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + decode_part_o_bytes(shape, a.n_chunks));
   a.Tq = shape->total_q;
@@ -259,11 +291,27 @@ int attn_sink_decode_fwd(const void* q, const void* k, const void* v, const floa
   a.Hq = shape->num_heads_q;
   a.Hkv = shape->num_heads_kv;
   a.G = a.Hq / a.Hkv;
+  a.n_cols = shape->max_q * a.G;
   a.window = window;
   a.out_bf16 = shape->out_dtype == ATTN_SINK_BF16 ? 1 : 0;
   const float scale = shape->softmax_scale > 0.0f ? shape->softmax_scale : 1.0f / sqrtf((float)shape->head_dim);
   a.scale_log2 = scale * kLog2e;
-  return launch_decode(a, stream) == hipSuccess ? ATTN_SINK_OK : ATTN_SINK_ERR_HIP;
+  return launch_decode(a, stream, ev) == hipSuccess ? ATTN_SINK_OK : ATTN_SINK_ERR_HIP;
+}
+
+int attn_sink_decode_fwd(const void* q, const void* k, const void* v, const float* sinks, int window,
+                         const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, const attn_sink_decode_shape* shape,
+                         void* workspace, size_t workspace_bytes, void* out, float* lse, hipStream_t stream) {
+  return attn_sink_decode_fwd_timed(q, k, v, sinks, window, cu_seqlens_q, cu_seqlens_k, shape, workspace,
+                                    workspace_bytes, out, lse, stream, nullptr, 0);
+}
+
+int attn_sink_decode_num_kernels(void) { return kDecodeNumKernels; }
+
+const char* attn_sink_decode_kernel_name(int i) {
+  static const char* const names[kDecodeNumKernels] = {"attn_sink_decode_partial_kernel",
+                                                        "attn_sink_decode_combine_kernel"};
+  return (i >= 0 && i < kDecodeNumKernels) ? names[i] : nullptr;
 }
 
 int attn_sink_bwd_num_kernels(void) { return kBwdNumKernels; }

@@ -13,7 +13,7 @@
 // keys streamed through a 3-slot LDS ring of swizzled tiles (direct global->LDS copies two tiles
 // ahead, transposing reads for V^T; see common.h). It writes the chunk's running max (log2
 // units), denominator and unnormalised output per column. attn_sink_decode_combine_kernel merges
-// the chunks of a (sequence, KV head) and adds the sink once: with M = max(S_h log2e, m_c),
+// the chunks of a (sequence, KV head, column) and adds the sink once: with M = max(S_h log2e, m_c),
 // l = 2^(S_h log2e - M) + sum_c 2^(m_c - M) l_c and O = sum_c 2^(m_c - M) o_c / l; LSE = (M +
 // log2 l) ln 2. O is stored in fp32 or bf16.
 #include "kernels.h"
@@ -30,11 +30,13 @@ constexpr int kDecRing = 3;
 __global__ __launch_bounds__(64) void attn_sink_decode_partial_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(1024))) unsigned char ring[kDecRing * kDecSlotBytes];
 
-  const int bid = blockIdx.x;  // = (b * Hkv + g) * n_chunks + chunk: the partial's index
-  const int chunk = bid % a.n_chunks;
-  const int rest = bid / a.n_chunks;
-  const int g = rest % a.Hkv;
-  const int b = rest / a.Hkv;
+  // The KV heads of one chunk of keys are neighbours in the launch, so that the rows they share
+  // are read from HBM at about the same time.
+  const int g = blockIdx.x % a.Hkv;
+  const int rest = blockIdx.x / a.Hkv;  // = b * n_chunks + chunk
+  const int chunk = rest % a.n_chunks;
+  const int b = rest / a.n_chunks;
+  const int pidx = (b * a.Hkv + g) * a.n_chunks + chunk;  // the partial's index
   const int cq = a.cu_q[b];
   const int nq = a.cu_q[b + 1] - cq;
   const int ck = a.cu_k[b];
@@ -48,10 +50,12 @@ __global__ __launch_bounds__(64) void attn_sink_decode_partial_kernel(DecodeArgs
   const bool col_ok = j < nq;              // nq * G <= 32 (checked on the host)
   const int pos = lk - nq + min(j, nq - 1);  // the column's query position (< 0: sees no key)
 
-  // Keys of this chunk that some column can see.
-  int k_lo = chunk * a.chunk_keys;
-  const int k_hi = min(lk, (chunk + 1) * a.chunk_keys);
-  if (a.window > 0) k_lo = max(k_lo, lk - nq - a.window + 1);
+  // Keys of this chunk that some column can see. Chunks tile the keys from the 64-aligned start of
+  // the first one any new query sees (key 0 without a window).
+  const int k_vis = a.window > 0 ? max(0, lk - nq - a.window + 1) : 0;
+  const int k_base = k_vis & ~(kDecTileKeys - 1);
+  const int k_lo = max(k_vis, k_base + chunk * a.chunk_keys);
+  const int k_hi = min(lk, k_base + (chunk + 1) * a.chunk_keys);
 
   float m = kNegInf, lsum = 0.0f;  // running max (log2 units) and denominator, without the sink
   f32x16 o[2];
@@ -108,16 +112,16 @@ __global__ __launch_bounds__(64) void attn_sink_decode_partial_kernel(DecodeArgs
         }
       }
       // Per element: the key must lie in the chunk's range, exist, and be visible from the column.
-      const bool need_mask = k0 < k_lo || k0 + kDecTileKeys > k_hi || k0 + kDecTileKeys - 1 > lk - nq ||
-                             a.window > 0 || nq * a.G < 32;
+      // Columns past the last (query, head) pair repeat the last query and are never stored.
+      const bool need_mask =
+          k0 < k_lo || k0 + kDecTileKeys > k_hi || k0 + kDecTileKeys - 1 > lk - nq || a.window > 0;
       if (need_mask) {
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) {
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int kj = k0 + 32 * mb + c_row(i, grp);
-            const bool vis = col_ok & (kj >= k_lo) & (kj < k_hi) & (kj <= pos) &
-                             ((a.window <= 0) | (kj > pos - a.window));
+            const bool vis = (kj >= k_lo) & (kj < k_hi) & (kj <= pos) & ((a.window <= 0) | (kj > pos - a.window));
             s[mb][i] = vis ? s[mb][i] : kNegInf;
           }
         }
@@ -177,16 +181,19 @@ __global__ __launch_bounds__(64) void attn_sink_decode_partial_kernel(DecodeArgs
     }
   }
 
-  // This chunk's partial: running max, denominator, unnormalised output per column.
+  // This chunk's partial: running max, denominator, unnormalised output per column. Only the
+  // columns of real (query, head) pairs are stored; the combine reads no other.
   const float ltot = sum_xor32(lsum);
-  float* po = a.part_o + (size_t)bid * kHeadDim * 32;  // [64 d][32 columns]
-  float* pml = a.part_ml + (size_t)bid * 2 * 32;        // [max, denominator][32 columns]
+  float* po = a.part_o + (size_t)pidx * 32 * kHeadDim + l32 * kHeadDim;  // [32 columns][64 d]
+  float* pml = a.part_ml + (size_t)pidx * 2 * 32;                        // [max, denominator][32 columns]
+  if (col_ok) {
 #pragma unroll
-  for (int db = 0; db < 2; ++db) {
+    for (int db = 0; db < 2; ++db) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int d = 32 * db + 8 * (i >> 2) + 4 * grp + (i & 3);
-      po[d * 32 + l32] = o[db][i];
+      for (int r4 = 0; r4 < 4; ++r4) {
+        *reinterpret_cast<f32x4*>(po + 32 * db + 8 * r4 + 4 * grp) =
+            (f32x4){o[db][4 * r4], o[db][4 * r4 + 1], o[db][4 * r4 + 2], o[db][4 * r4 + 3]};
+      }
     }
   }
   if (grp == 0) {
@@ -195,59 +202,82 @@ __global__ __launch_bounds__(64) void attn_sink_decode_partial_kernel(DecodeArgs
   }
 }
 
-// One workgroup per (sequence, KV head): thread t merges column t % 32 for d = 8(t/32) .. +7.
-__global__ __launch_bounds__(256) void attn_sink_decode_combine_kernel(DecodeArgs a) {
-  const int g = blockIdx.x % a.Hkv;
-  const int b = blockIdx.x / a.Hkv;
+// One workgroup per (sequence, KV head, column): lane d of each of the four waves accumulates
+// output element d over every fourth chunk; the waves' sums meet in LDS.
+constexpr int kCombineWaves = 4;
+
+__global__ __launch_bounds__(64 * kCombineWaves) void attn_sink_decode_combine_kernel(DecodeArgs a) {
+  __shared__ float red[kCombineWaves][kHeadDim + 1];
+  const int c = blockIdx.x % a.n_cols;
+  const int rest = blockIdx.x / a.n_cols;
+  const int g = rest % a.Hkv;
+  const int b = rest / a.Hkv;
   const int cq = a.cu_q[b];
   const int nq = a.cu_q[b + 1] - cq;
-  const int c = threadIdx.x & 31;
-  const int dg = threadIdx.x >> 5;
   const int j = c / a.G;
-  if (j >= nq) return;
+  if (j >= nq) return;  // uniform over the workgroup
   const int hq = g * a.G + c % a.G;
-  const size_t p0 = (size_t)blockIdx.x * a.n_chunks;  // first partial of this (sequence, KV head)
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const size_t p0 = (size_t)rest * a.n_chunks;  // first partial of this (sequence, KV head)
+  const float* ml = a.part_ml + p0 * 64 + c;    // chunk ch: max at ml[64 ch], denominator at ml[64 ch + 32]
 
+  // Largest running max over the chunks and the sink (log2 units).
   const float sink2 = a.sinks[hq] * kLog2e;
   float M = sink2;
-  for (int ch = 0; ch < a.n_chunks; ++ch) M = fmaxf(M, a.part_ml[(p0 + ch) * 64 + c]);
+  for (int ch = threadIdx.x; ch < a.n_chunks; ch += 64 * kCombineWaves) M = fmaxf(M, ml[(size_t)ch * 64]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+  if (lane == 0) red[w][kHeadDim] = M;
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < kCombineWaves; ++i) M = fmaxf(M, red[i][kHeadDim]);
   const float Ms = M == kNegInf ? 0.0f : M;
-  float L = fast_exp2(sink2 - Ms);
-  float acc[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
-  for (int ch = 0; ch < a.n_chunks; ++ch) {
-    const float w = fast_exp2(a.part_ml[(p0 + ch) * 64 + c] - Ms);  // 0 for an empty chunk (max -inf)
-    L += w * a.part_ml[(p0 + ch) * 64 + 32 + c];
-    const float* po = a.part_o + (p0 + ch) * kHeadDim * 32;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] += w * po[(8 * dg + i) * 32 + c];
+  __syncthreads();  // red[.][kHeadDim] is reused below
+
+  float acc = 0.0f, L = 0.0f;
+  const float* po = a.part_o + p0 * 32 * kHeadDim + c * kHeadDim + lane;
+#pragma unroll 4
+  for (int ch = w; ch < a.n_chunks; ch += kCombineWaves) {
+    const float wt = fast_exp2(ml[(size_t)ch * 64] - Ms);  // 0 for an empty chunk (max -inf)
+    L += wt * ml[(size_t)ch * 64 + 32];
+    acc += wt * po[(size_t)ch * 32 * kHeadDim];
   }
+  red[w][lane] = acc;
+  if (lane == 0) red[w][kHeadDim] = L;
+  __syncthreads();
+  if (w != 0) return;
+  L = fast_exp2(sink2 - Ms);
+#pragma unroll
+  for (int i = 0; i < kCombineWaves; ++i) L += red[i][kHeadDim];
+  acc = 0.0f;
+#pragma unroll
+  for (int i = 0; i < kCombineWaves; ++i) acc += red[i][lane];
   const float inv = L > 0.0f ? 1.0f / L : 0.0f;
   const size_t row = (size_t)(cq + j) * a.Hq + hq;
   if (a.out_bf16) {
-    bf16x8 v;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = (__bf16)(acc[i] * inv);
-    *reinterpret_cast<bf16x8*>(static_cast<__bf16*>(a.out) + row * kHeadDim + 8 * dg) = v;
+    static_cast<__bf16*>(a.out)[row * kHeadDim + lane] = (__bf16)(acc * inv);
   } else {
-    float* dst = static_cast<float*>(a.out) + row * kHeadDim + 8 * dg;
-    *reinterpret_cast<f32x4*>(dst) = (f32x4){acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv};
-    *reinterpret_cast<f32x4*>(dst + 4) = (f32x4){acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv};
+    static_cast<float*>(a.out)[row * kHeadDim + lane] = acc * inv;
   }
-  if (dg == 0) a.lse[(size_t)hq * a.Tq + cq + j] = L > 0.0f ? (Ms + fast_log2(L)) * kLn2 : kNegInf;
+  if (lane == 0) a.lse[(size_t)hq * a.Tq + cq + j] = L > 0.0f ? (Ms + fast_log2(L)) * kLn2 : kNegInf;
 }
 
 }  // namespace
 
-hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream, hipEvent_t const* events) {
   const long long parts = (long long)a.B * a.Hkv * a.n_chunks;
   if (parts <= 0) return hipSuccess;
+  hipError_t e;
+  if (events && (e = hipEventRecord(events[0], stream)) != hipSuccess) return e;
   hipLaunchKernelGGL(attn_sink_decode_partial_kernel, dim3((unsigned)parts), dim3(64), 0, stream, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(attn_sink_decode_combine_kernel, dim3((unsigned)(a.B * a.Hkv)), dim3(256), 0, stream, a);
-  return hipGetLastError();
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (events && (e = hipEventRecord(events[1], stream)) != hipSuccess) return e;
+  hipLaunchKernelGGL(attn_sink_decode_combine_kernel, dim3((unsigned)(a.B * a.Hkv * a.n_cols)),
+                     dim3(64 * kCombineWaves), 0, stream, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (events && (e = hipEventRecord(events[2], stream)) != hipSuccess) return e;
+  return hipSuccess;
 }
 
 }  // namespace attn_sink

@@ -6,6 +6,10 @@ head_dim 64, causal, bf16 inputs (the headline configuration).
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload causal4k] [--no-cpu-baseline]
 
+``--workload decode32k`` (or decode32k_nq4, decode32k_window) times the inference-shaped decode
+forward instead: a few new tokens per sequence against 16k-32k-token KV caches, reported as
+algorithmic HBM GB/s (q, every cached K/V row a new token sees, out and LSE, each once).
+
 Prints one JSON line. ``value`` is algorithmic TFLOP/s over the timed steps: 4*d FLOPs per visible
 (query, key, head) in the forward (QK^T and PV) plus 10*d in the backward (S, dP, dV, dK, dQ);
 recomputation and masked tile work are not counted. ``roofline`` describes the kernel with the
@@ -35,7 +39,8 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 import attention_learnable_sinks_attn_amd as asa  # noqa: E402
-from workloads import WORKLOAD_NAMES, make_workload_inputs, visible_pairs, workload  # noqa: E402
+from workloads import (DECODE_WORKLOADS, WORKLOAD_NAMES, make_decode_workload_inputs, make_workload_inputs,  # noqa: E402
+                       visible_pairs, workload)
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 HBM_PEAK_GBS = 8000.0
@@ -58,6 +63,7 @@ KERNEL_FLOPS_PER_PAIR_D = {
 TRAFFIC = {
     ("causal4k", "attn_sink_bwd_dkdv_kernel"): {"bytes": 148726365, "digest": "0c3e577ebdf54fde"},
     ("window4k", "attn_sink_bwd_dkdv_kernel"): {"bytes": 114745761, "digest": "0c3e577ebdf54fde"},
+    ("decode32k", "attn_sink_decode_partial_kernel"): {"bytes": 368479642, "digest": "8d5bcbc09448eca7"},
 }
 
 
@@ -118,15 +124,20 @@ class Hip:
         return out.value
 
 
+def _oracle_threads() -> int:
+    """Threads numpy's BLAS may use for the oracle's matrix products."""
+    try:
+        from threadpoolctl import threadpool_info
+        return int(max([p.get("num_threads", 1) for p in threadpool_info()] or [1]))
+    except Exception:  # pragma: no cover
+        return len(os.sched_getaffinity(0))
+
+
 def cpu_baseline(inp, w, max_heads_kv: int):
     """Time the fp64 oracle (forward + backward) on the first `max_heads_kv` KV groups."""
     import numpy as np  # noqa: F401
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = len(os.sched_getaffinity(0))
+    threads = _oracle_threads()
     G = w.hq // w.hkv
     hq_s = G * max_heads_kv
     q = inp.q[:, :hq_s]
@@ -143,12 +154,98 @@ def cpu_baseline(inp, w, max_heads_kv: int):
                       f"fwd+bwd in fp64 numpy, {dt:.2f} s"}
 
 
+def decode_bytes(d, hq: int, hkv: int, out_bytes: int):
+    """Algorithmic HBM bytes of one decode call: (q + every K/V row some new query sees) for the
+    partial kernel, (out + lse) for the combine kernel."""
+    cu_q, cu_k = d.cu_q.tolist(), d.cu_k.tolist()
+    keys = 0
+    for b in range(len(cu_q) - 1):
+        nq, lk = cu_q[b + 1] - cu_q[b], cu_k[b + 1] - cu_k[b]
+        if nq:
+            keys += min(lk, d.window + nq - 1) if d.window > 0 else lk
+    tq = cu_q[-1]
+    return {"attn_sink_decode_partial_kernel": tq * hq * 64 * 2 + 2 * keys * hkv * 64 * 2,
+            "attn_sink_decode_combine_kernel": tq * hq * 64 * out_bytes + hq * tq * 4}
+
+
+def bench_decode(args):
+    """Decode forward (attn_sink_decode_fwd, bf16 output) over resident KV caches."""
+    d = make_decode_workload_inputs(args.workload, args.seed)
+    B = len(d.cu_k) - 1
+    _, _, nq, hq, hkv, window = DECODE_WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    q, k, v = (t.to(dev).contiguous() for t in (d.q, d.k, d.v))
+    sinks, cu_q, cu_k = d.sinks.to(dev), d.cu_q.to(dev), d.cu_k.to(dev)
+    Tq = q.shape[0]
+    out = torch.empty((Tq, hq, 64), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((hq, Tq), dtype=torch.float32, device=dev)
+    ws = torch.empty((asa.decode_workspace_bytes(q, k, cu_q, d.max_q, d.max_k),), dtype=torch.uint8, device=dev)
+    names = asa.decode_kernel_names()
+    hip = Hip()
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    events = [[hip.event() for _ in range(len(names) + 1)] for _ in range(args.steps)]
+
+    def step(evs=None):
+        asa.decode_fwd(q, k, v, sinks, cu_q, cu_k, d.max_q, d.max_k, window=window, out_dtype=torch.bfloat16,
+                       out=out, lse=lse, workspace=ws, events=evs)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record()
+    for s in range(args.steps):
+        step(events[s])
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = start.elapsed_time(end) / args.steps
+    per_kernel = {n: 0.0 for n in names}
+    for s in range(args.steps):
+        for i, n in enumerate(names):
+            per_kernel[n] += hip.elapsed_ms(events[s][i], events[s][i + 1]) / args.steps
+    kb = decode_bytes(d, hq, hkv, 2)
+    total = sum(kb.values())
+    gbs = total / (ms_step * 1e-3) / 1e9
+    dom = max(per_kernel, key=per_kernel.get)
+    achieved = kb[dom] / (per_kernel[dom] * 1e-3) / 1e9
+    roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "avg_launch_ms": round(per_kernel[dom], 4), "algorithmic_bytes": kb[dom]}
+    rec = TRAFFIC.get((args.workload, dom))
+    if rec is not None and rec["digest"] == kernel_source_digest():
+        roofline["traffic"] = rec["bytes"]
+        roofline["traffic_unit"] = "bytes per launch (HBM fetch + write)"
+    res = {
+        "metric": "sink-attention decode forward HBM GB/s (GQA 64/8, d=64, bf16 KV cache)", "value": round(gbs, 1),
+        "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": args.workload, "seqs": B, "new_tokens": int(Tq), "cached_tokens": int(k.shape[0]),
+                   "heads_q": hq, "heads_kv": hkv, "head_dim": 64, "window": window, "out_dtype": "bf16",
+                   "seed": args.seed, "parallelism": "none (1 GPU)"},
+        "tokens_per_s": round(Tq / (ms_step * 1e-3), 1),
+        "kernel_ms": {n: round(t, 4) for n, t in per_kernel.items()},
+        "wall_s_timed": round(wall, 4),
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        t0 = time.perf_counter()
+        oracle.decode_forward(d.q, d.k, d.v, d.sinks, d.cu_q, d.cu_k, window)
+        dt = time.perf_counter() - t0
+        res["cpu_baseline"] = {"value": round(total / dt / 1e9, 3), "unit": "GB/s", "cores": _oracle_threads(),
+                               "kind": "oracle", "sample": f"{args.workload}: the whole batch ({B} sequences, "
+                                                           f"{Tq} new tokens) in fp64 numpy, {dt:.2f} s"}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="causal4k", choices=WORKLOAD_NAMES)
+    ap.add_argument("--workload", default="causal4k", choices=list(WORKLOAD_NAMES) + list(DECODE_WORKLOADS))
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-kv-groups", type=int, default=8)
@@ -161,6 +258,16 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
 
+    if args.copy_probe_mib > 0:
+        n = args.copy_probe_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    if args.workload in DECODE_WORKLOADS:
+        bench_decode(args)
+        return
     w = workload(args.workload, args.seed)
     inp = make_workload_inputs(args.workload, args.seed)
     dev = torch.device("cuda:0")
@@ -190,13 +297,6 @@ def main():
         asa.bwd(q, k, v, sinks, out, lse, dout, cu, inp.max_seqlen, inp.causal, inp.window, dq=dq, dk=dk, dv=dv,
                 dsinks=dsinks, workspace=ws, events=None if evs is None else evs[1:])
 
-    if args.copy_probe_mib > 0:
-        n = args.copy_probe_mib * (1 << 20) // 4
-        src = torch.ones(n, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()

@@ -161,6 +161,19 @@ int attn_sink_decode_fwd(const void* q, const void* k, const void* v, const floa
                          const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, const attn_sink_decode_shape* shape,
                          void* workspace, size_t workspace_bytes, void* out, float* lse, hipStream_t stream);
 
+/*
+ * attn_sink_decode_fwd with timing: events (hipEvent_t handles owned by the caller) are recorded on
+ * `stream` before the first kernel, between the kernels and after the last; num_events must equal
+ * attn_sink_decode_num_kernels() + 1, else ATTN_SINK_ERR_BAD_SHAPE. events == NULL behaves like
+ * attn_sink_decode_fwd. attn_sink_decode_kernel_name(i) names kernel i (static string, or NULL).
+ */
+int attn_sink_decode_fwd_timed(const void* q, const void* k, const void* v, const float* sinks, int window,
+                               const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                               const attn_sink_decode_shape* shape, void* workspace, size_t workspace_bytes, void* out,
+                               float* lse, hipStream_t stream, void* const* events, int num_events);
+int attn_sink_decode_num_kernels(void);
+const char* attn_sink_decode_kernel_name(int i);
+
 /* Number of kernels attn_sink_bwd enqueues, and the name of kernel i (static string, or NULL). */
 int attn_sink_bwd_num_kernels(void);
 const char* attn_sink_bwd_kernel_name(int i);

@@ -166,6 +166,7 @@ def test_decode_argument_errors():
     assert decode(lib, dshape(hq=6, hkv=4)) == -2
     assert decode(lib, dshape(max_q=9)) == -2    # above total_q
     assert decode(lib, dshape(max_k=301)) == -2  # above total_k
+    assert decode(lib, dshape(max_q=0)) == -2    # new tokens but max_q = 0
     assert decode(lib, dshape(d=128)) == -3
     assert decode(lib, dshape(dtype=2)) == -3
     # the new queries of one KV head's query heads must fit 32 MFMA columns
@@ -188,10 +189,24 @@ def test_decode_argument_errors():
 def test_decode_workspace_formula():
     lib = asa.load_library()
     # 8 sequences x 8 KV heads = 64 (sequence, KV head) pairs; the key axis is split so that about
-    # 8192 waves run: 32768 keys = 512 tiles of 64 -> chunks of 4 tiles -> 128 chunks per pair. Each
-    # chunk keeps a 64 x 32 fp32 partial output and a running max and sum per column.
+    # 4096 waves run: 32768 keys = 512 tiles of 64 -> chunks of 8 tiles -> 64 chunks per pair. Each
+    # chunk keeps a 32 x 64 fp32 partial output and a running max and sum per column.
     s = dshape(tq=8, tk=200000, B=8, max_q=1, max_k=32768, hq=64, hkv=8)
     need = lib.attn_sink_decode_workspace_bytes(ctypes.byref(s))
-    assert need == 64 * 128 * 64 * 32 * 4 + 64 * 128 * 2 * 32 * 4
+    assert need == 64 * 64 * 32 * 64 * 4 + 64 * 64 * 2 * 32 * 4
     assert lib.attn_sink_decode_workspace_bytes(None) == 0
     assert lib.attn_sink_decode_workspace_bytes(ctypes.byref(dshape(max_q=5))) == 0
+
+
+@needs_lib
+def test_decode_timed_entry_point_checks_event_count():
+    lib = asa.load_library()
+    s = dshape()
+    need = lib.attn_sink_decode_workspace_bytes(ctypes.byref(s))
+    n = lib.attn_sink_decode_num_kernels()
+    assert [lib.attn_sink_decode_kernel_name(i) for i in range(n)] == [b"attn_sink_decode_partial_kernel",
+                                                                      b"attn_sink_decode_combine_kernel"]
+    assert lib.attn_sink_decode_kernel_name(n) is None
+    evs = (ctypes.c_void_p * n)(*([P] * n))  # one too few
+    rc = lib.attn_sink_decode_fwd_timed(P, P, P, P, 0, P, P, ctypes.byref(s), P, need, P, P, None, evs, n)
+    assert rc == -2
