@@ -4,7 +4,10 @@ One step = attn_sink_fwd + attn_sink_bwd over one batch of synthetic GPT-OSS-sha
 already resident in HBM. Default workload: 4096 tokens, 64 query heads sharing 8 KV heads,
 head_dim 64, causal, bf16 inputs (the headline configuration).
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload causal4k] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps 50] [--warmup 50] [--workload causal4k] [--no-cpu-baseline]
+
+The default 50 warm-up steps let the GPU's clocks settle: from idle, the first 20-40 steps of the
+4k workload run up to 8% slower than the rest.
 
 ``--workload decode32k`` (or decode32k_nq4, decode32k_window) times the inference-shaped decode
 forward instead: a few new tokens per sequence against 16k-32k-token KV caches, reported as
@@ -243,8 +246,8 @@ def bench_decode(args):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="causal4k", choices=list(WORKLOAD_NAMES) + list(DECODE_WORKLOADS))
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
