@@ -64,8 +64,11 @@ KERNEL_FLOPS_PER_PAIR_D = {
 # (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch) scaled by what the same counters read for the
 # copy probe; valid only for kernel sources with the recorded digest.
 TRAFFIC = {
-    ("causal4k", "attn_sink_bwd_dkdv_kernel"): {"bytes": 148726365, "digest": "0c3e577ebdf54fde"},
-    ("window4k", "attn_sink_bwd_dkdv_kernel"): {"bytes": 114745761, "digest": "0c3e577ebdf54fde"},
+    ("causal4k", "attn_sink_bwd_dkdv_kernel"): {"bytes": 148910635, "digest": "8d5bcbc09448eca7"},
+    ("window4k", "attn_sink_bwd_dkdv_kernel"): {"bytes": 114759329, "digest": "8d5bcbc09448eca7"},
+    ("window4k", "attn_sink_bwd_dq_kernel"): {"bytes": 144921750, "digest": "8d5bcbc09448eca7"},
+    ("varlen_window", "attn_sink_bwd_dkdv_kernel"): {"bytes": 3881858128, "digest": "8d5bcbc09448eca7"},
+    ("varlen_window", "attn_sink_bwd_dq_kernel"): {"bytes": 2517019340, "digest": "8d5bcbc09448eca7"},
     ("decode32k", "attn_sink_decode_partial_kernel"): {"bytes": 368479642, "digest": "8d5bcbc09448eca7"},
 }
 
