@@ -39,6 +39,8 @@ Readings where the pages are silent (each listed in the design notes):
   masked by causality or the window; it does not count toward the window.
 * Sliding window W > 0: query i sees keys j with i - W < j <= i (exactly W keys including
   itself). Causal: j <= i. The sink is visible from every row.
+* Non-causal with a window W > 0 (the pages only train with causal windows; this is the plain
+  symmetric reading): query i sees keys j with |i - j| < W, i.e. i - W < j < i + W.
 * GQA: query head h reads KV head h // (Hq / Hkv). Sinks are per query head.
 * Varlen: sequences are packed back to back; cu_seqlens[b] .. cu_seqlens[b+1] are the rows of
   sequence b, and attention never crosses a sequence boundary ([nmedialink] section
@@ -84,6 +86,8 @@ def visible(i, j, causal: bool, window: int) -> np.ndarray:
         ok &= j <= i
     if window is not None and window > 0:
         ok &= j > i - window
+        if not causal:
+            ok &= j < i + window
     return ok
 
 
@@ -95,7 +99,10 @@ def _key_range(r_lo: int, r_hi: int, L: int, causal: bool, window: int):
     """Smallest key interval [c0, c1) containing every key visible from rows r_lo..r_hi.
     Keys outside it are masked for all these rows, so they contribute exactly zero."""
     c0 = max(0, r_lo - window + 1) if window and window > 0 else 0
-    c1 = min(L, r_hi + 1) if causal else L
+    if causal:
+        c1 = min(L, r_hi + 1)
+    else:
+        c1 = min(L, r_hi + window) if window and window > 0 else L
     return c0, max(c0, c1)
 
 

@@ -93,6 +93,8 @@ def _sdpa_reference(inp, scale=None):
             mask &= j <= i
         if inp.window > 0:
             mask &= j > i - inp.window
+            if not inp.causal:
+                mask &= j < i + inp.window
         qs = q[a:e].transpose(0, 1)                                   # [H, L, d]
         ks = k[a:e].repeat_interleave(G, dim=1).transpose(0, 1)
         vs = v[a:e].repeat_interleave(G, dim=1).transpose(0, 1)
@@ -105,7 +107,7 @@ def _sdpa_reference(inp, scale=None):
     return out.detach().numpy(), torch.cat(lses, 1).detach().numpy(), q.grad.numpy(), k.grad.numpy(), v.grad.numpy()
 
 
-@pytest.mark.parametrize("causal,window", [(True, 0), (True, 5), (False, 0)])
+@pytest.mark.parametrize("causal,window", [(True, 0), (True, 5), (False, 0), (False, 5)])
 @pytest.mark.parametrize("hkv", [1, 2, 4])
 def test_neg_inf_sink_is_plain_attention(causal, window, hkv):
     inp = _small(lengths=(23, 1, 40), hq=4, hkv=hkv, causal=causal, window=window,
@@ -133,7 +135,7 @@ def test_neg_inf_sink_non_default_scale():
 # Normalisation invariant: sum_j P_ij + P_sink = 1
 # ---------------------------------------------------------------------------------------------
 
-@pytest.mark.parametrize("causal,window", [(True, 0), (True, 7), (False, 0)])
+@pytest.mark.parametrize("causal,window", [(True, 0), (True, 7), (False, 0), (False, 7)])
 def test_probabilities_sum_to_one(causal, window):
     inp = _small(lengths=(50,), hq=3, hkv=1, causal=causal, window=window, sink_scale=3.0)
     P, Ps = oracle.probabilities(inp.q, inp.k, inp.sinks, inp.cu_seqlens, causal, window)
@@ -151,11 +153,13 @@ def test_probabilities_sum_to_one(causal, window):
 def _n_visible(L, causal, window):
     i = np.arange(L)
     if not causal:
+        if window > 0:  # keys i - W < j < i + W inside [0, L)
+            return np.minimum(i + window, L) - np.maximum(i - window + 1, 0)
         return np.full(L, L)
     return np.minimum(i + 1, window) if window > 0 else i + 1
 
 
-@pytest.mark.parametrize("causal,window", [(True, 0), (True, 4), (False, 0)])
+@pytest.mark.parametrize("causal,window", [(True, 0), (True, 4), (False, 0), (False, 4)])
 def test_uniform_scores_closed_form(causal, window):
     L = 29
     inp = _small(lengths=(L,), hq=2, hkv=1, causal=causal, window=window, zero_q=True)
@@ -221,7 +225,7 @@ def _loss(q, k, v, s, cu, dout, causal, window):
 
 
 @pytest.mark.parametrize("lengths,causal,window", [((3, 5), True, 0), ((3, 5), True, 2), ((4, 0, 4), False, 0),
-                                                    ((1, 6), True, 3)])
+                                                    ((1, 6), True, 3), ((4, 6), False, 2)])
 def test_finite_differences(lengths, causal, window):
     inp = _small(lengths=lengths, hq=2, hkv=1, d=4, causal=causal, window=window, seed=11)
     q, k, v, s, dout = f64(inp.q), f64(inp.k), f64(inp.v), f64(inp.sinks), f64(inp.dout)
@@ -273,6 +277,8 @@ def _pseudocode_autograd(inp):
             keep &= j <= i
         if inp.window > 0:
             keep &= j > i - inp.window
+            if not inp.causal:
+                keep &= j < i + inp.window
         scores = scores.masked_fill(~keep, -math.inf)
         combined = torch.cat([scores, sink[:, None, None].expand(hq, L, 1)], dim=-1)
         probs = torch.softmax(combined, dim=-1)
@@ -283,7 +289,7 @@ def _pseudocode_autograd(inp):
     return out.detach().numpy(), q.grad.numpy(), k.grad.numpy(), v.grad.numpy(), sink.grad.numpy()
 
 
-@pytest.mark.parametrize("causal,window", [(True, 0), (True, 16), (False, 0)])
+@pytest.mark.parametrize("causal,window", [(True, 0), (True, 16), (False, 0), (False, 16)])
 def test_matches_autograd_of_pseudocode(causal, window):
     inp = make_inputs((256,), 4, 2, 64, causal=causal, window=window, seed=5)
     out, _ = oracle.forward(inp.q, inp.k, inp.v, inp.sinks, inp.cu_seqlens, causal, window, row_block=100)
@@ -349,7 +355,7 @@ def test_gqa_equals_repeated_mha():
     np.testing.assert_allclose(g1[3], g2[3], atol=1e-13)
 
 
-@pytest.mark.parametrize("causal,window", [(True, 0), (True, 6), (False, 0)])
+@pytest.mark.parametrize("causal,window", [(True, 0), (True, 6), (False, 0), (False, 6)])
 def test_varlen_equals_concatenated_runs(causal, window):
     lengths = (17, 0, 1, 40, 9)
     inp = _small(lengths=lengths, hq=4, hkv=2, d=8, causal=causal, window=window)
@@ -390,6 +396,28 @@ def test_window_boundary_pair():
         assert (P[0, i] > 0).sum() == W
 
 
+def test_symmetric_window_boundary_pairs():
+    """Non-causal window W: keys i-W and i+W are excluded, keys i-W+1 and i+W-1 included."""
+    W, L = 3, 12
+    inp = _small(lengths=(L,), hq=1, hkv=1, d=8, causal=False, window=W)
+    P, _ = oracle.probabilities(inp.q, inp.k, inp.sinks, inp.cu_seqlens, False, W)
+    for i in range(L):
+        if i - W >= 0:
+            assert P[0, i, i - W] == 0.0
+        if i + W < L:
+            assert P[0, i, i + W] == 0.0
+        assert P[0, i, max(i - W + 1, 0)] > 0.0 and P[0, i, min(i + W - 1, L - 1)] > 0.0
+        assert (P[0, i] > 0).sum() == min(i + W, L) - max(i - W + 1, 0)
+
+
+def test_symmetric_window_at_least_length_is_full():
+    inp = _small(lengths=(30, 12), hq=2, hkv=1, d=8, causal=False)
+    a = oracle.backward(inp.q, inp.k, inp.v, inp.sinks, inp.dout, inp.cu_seqlens, False, 0, return_forward=True)
+    b = oracle.backward(inp.q, inp.k, inp.v, inp.sinks, inp.dout, inp.cu_seqlens, False, 30, return_forward=True)
+    for x, y in zip(a, b):
+        np.testing.assert_array_equal(x, y)
+
+
 def test_row_block_does_not_change_results():
     inp = _small(lengths=(70,), hq=2, hkv=1, d=16, window=9)
     a = oracle.backward(inp.q, inp.k, inp.v, inp.sinks, inp.dout, inp.cu_seqlens, True, 9, return_forward=True)
@@ -403,7 +431,7 @@ def test_row_block_does_not_change_results():
 # Row-sampled helpers (used for full-size checks) agree with the full oracle
 # ---------------------------------------------------------------------------------------------
 
-@pytest.mark.parametrize("causal,window", [(True, 0), (True, 5), (False, 0)])
+@pytest.mark.parametrize("causal,window", [(True, 0), (True, 5), (False, 0), (False, 5)])
 def test_sampled_helpers_agree_with_full(causal, window):
     inp = _small(lengths=(26, 1, 31), hq=4, hkv=2, d=16, causal=causal, window=window)
     args = (inp.q, inp.k, inp.v, inp.sinks)
@@ -457,6 +485,11 @@ def _off_by_one_window(q_rows, Kg, rows, L, sink, causal, window, scale):
     return _ORIG_SOFTMAX(q_rows, Kg, rows, L, sink, causal, window + 1 if window else 0, scale)
 
 
+def _one_sided_window(q_rows, Kg, rows, L, sink, causal, window, scale):
+    # treats a non-causal window like a causal one on the right-hand side (keys j <= i only)
+    return _ORIG_SOFTMAX(q_rows, Kg, rows, L, sink, causal or window > 0, window, scale)
+
+
 def _flipped_sink_grad(probs, dout_rows, Vcols):
     dS, dsink, D = _ORIG_GRADS(probs, dout_rows, Vcols)
     return dS, -dsink, D
@@ -480,7 +513,8 @@ def _pins_pass():
               lambda: test_uniform_scores_closed_form(True, 4),
               lambda: test_probabilities_sum_to_one(True, 7),
               lambda: test_finite_differences((3, 5), True, 2),
-              lambda: test_window_boundary_pair()]
+              lambda: test_window_boundary_pair(),
+              lambda: test_symmetric_window_boundary_pairs()]
     for c in checks:
         try:
             c()
@@ -489,8 +523,8 @@ def _pins_pass():
     return True
 
 
-@pytest.mark.parametrize("mutant", ["scaled_sink", "no_sink", "window_off_by_one", "flipped_sink_grad",
-                                     "dropped_D"])
+@pytest.mark.parametrize("mutant", ["scaled_sink", "no_sink", "window_off_by_one", "one_sided_window",
+                                     "flipped_sink_grad", "dropped_D"])
 def test_planted_mistakes_are_caught(monkeypatch, mutant):
     assert _pins_pass(), "pins must pass on the unmodified oracle"
     if mutant == "scaled_sink":
@@ -499,6 +533,8 @@ def test_planted_mistakes_are_caught(monkeypatch, mutant):
         monkeypatch.setattr(sa, "_combined_softmax", _no_sink_softmax)
     elif mutant == "window_off_by_one":
         monkeypatch.setattr(sa, "_combined_softmax", _off_by_one_window)
+    elif mutant == "one_sided_window":
+        monkeypatch.setattr(sa, "_combined_softmax", _one_sided_window)
     elif mutant == "flipped_sink_grad":
         monkeypatch.setattr(sa, "_prob_grads", _flipped_sink_grad)
     elif mutant == "dropped_D":
