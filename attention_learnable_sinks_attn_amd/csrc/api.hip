@@ -68,7 +68,6 @@ int bwd_impl(const void* q, const void* k, const void* v, const float* sinks, co
              void* const* events, int num_events) {
   int rc = check_shape(shape);
   if (rc) return rc;
-  if (window > 0 && !causal) return ATTN_SINK_ERR_BAD_WINDOW;
   if (sinks == nullptr || cu_seqlens == nullptr || dsinks == nullptr) return ATTN_SINK_ERR_NULL_PTR;
   const int T = shape->total_tokens;
   if (T > 0 && (!q || !k || !v || !out || !lse || !dout || !dq || !dk || !dv)) return ATTN_SINK_ERR_NULL_PTR;
@@ -199,7 +198,6 @@ int attn_sink_fwd(const void* q, const void* k, const void* v, const float* sink
                   hipStream_t stream) {
   int rc = check_shape(shape);
   if (rc) return rc;
-  if (window > 0 && !causal) return ATTN_SINK_ERR_BAD_WINDOW;
   if (sinks == nullptr || cu_seqlens == nullptr) return ATTN_SINK_ERR_NULL_PTR;
   const int T = shape->total_tokens;
   if (T > 0 && (!q || !k || !v || !out || !lse)) return ATTN_SINK_ERR_NULL_PTR;
@@ -328,7 +326,7 @@ const char* attn_sink_strerror(int code) {
     case ATTN_SINK_ERR_NULL_PTR: return "a required pointer is NULL";
     case ATTN_SINK_ERR_BAD_SHAPE: return "invalid shape (sizes, head counts or max_seqlen)";
     case ATTN_SINK_ERR_UNSUPPORTED: return "unsupported head_dim or output dtype (head_dim 64, float32 outputs)";
-    case ATTN_SINK_ERR_BAD_WINDOW: return "a sliding window requires causal attention";
+    case ATTN_SINK_ERR_BAD_WINDOW: return "negative window";
     case ATTN_SINK_ERR_WORKSPACE: return "workspace missing or smaller than attn_sink_bwd_workspace_bytes()";
     case ATTN_SINK_ERR_HIP: return "a HIP launch failed";
     case ATTN_SINK_ERR_ALIGN: return "a tensor base pointer is not 16-byte aligned";

@@ -154,7 +154,7 @@ __global__ __launch_bounds__(128 * NS, 2) void attn_sink_bwd_dkdv_kernel(BwdArgs
   // stream the same rows at about the same time and mostly hit in L2). Both key halves and both
   // streams run the same number of steps, so one barrier per step serves the whole workgroup.
   const int kmax = min(len, kblk + kKvKeysPerBlock) - 1;
-  const int i_begin = a.causal ? kblk : 0;
+  const int i_begin = a.causal ? kblk : (a.window > 0 ? max(0, kblk - a.window + 1) : 0);
   const int i_end = a.window > 0 ? min(len, kmax + a.window) : len;  // exclusive
   const int n_sub = (i_end - i_begin + kKvRows - 1) / kKvRows;
   const int n_steps = hps * n_sub;
@@ -239,8 +239,9 @@ __global__ __launch_bounds__(128 * NS, 2) void attn_sink_bwd_dkdv_kernel(BwdArgs
       tr_all(slot_lds, tr);
       if (need_mask) {
         // Row of register i: i0 + 8grp + r_i with r_i = 16(i/8) + i%8. Visible iff the row and
-        // the key exist, the key is not after the row (causal) and the row is less than
-        // `window` rows after the key. (The empty asm keeps the comparisons in this branch.)
+        // the key exist, the key is not after the row (causal), the row is less than `window`
+        // rows after the key and, without causality, the key less than `window` keys after the
+        // row. (The empty asm keeps the comparisons in this branch.)
         int kj = k0 + l32;
         asm volatile("" : "+v"(kj));
         const int dq = i0 + 8 * grp - kj;     // row - key for r_i = 0
@@ -250,7 +251,8 @@ __global__ __launch_bounds__(128 * NS, 2) void attn_sink_bwd_dkdv_kernel(BwdArgs
         for (int i = 0; i < 16; ++i) {
           const int r = 16 * (i >> 3) + (i & 7);
           const int t = dq + r;
-          const bool vis = key_ok & (r < rlim) & ((a.causal == 0) | (t >= 0)) & ((a.window <= 0) | (t < a.window));
+          const bool vis = key_ok & (r < rlim) & ((a.causal == 0) | (t >= 0)) & ((a.window <= 0) | (t < a.window)) &
+                           ((a.causal != 0) | (a.window <= 0) | (t > -a.window));
           sc[i] = vis ? sc[i] : kNegInf;
         }
       }
@@ -307,10 +309,11 @@ __global__ __launch_bounds__(128 * NS, 2) void attn_sink_bwd_dkdv_kernel(BwdArgs
     for (int sub = 0; sub < kKvRows / kKvSub; ++sub) {
       const int i0 = i_begin + kKvRows * (n_sub - 1 - ct) + kKvSub * sub;
       const bool live = (!a.causal || k0 <= i0 + kKvSub - 1) && (a.window <= 0 || i0 <= k0 + 31 + a.window - 1) &&
-                        k0 < len && i0 < len;
+                        (a.causal || a.window <= 0 || k0 <= i0 + kKvSub - 1 + a.window - 1) && k0 < len && i0 < len;
       if (live) {  // wave-uniform: skip blocks in which none of this wave's pairs is visible
         const bool need_mask = (i0 + kKvSub > len) || (k0 + 32 > len) || (a.causal && k0 + 31 > i0) ||
-                               (a.window > 0 && k0 <= i0 + kKvSub - 1 - a.window);
+                               (a.window > 0 && k0 <= i0 + kKvSub - 1 - a.window) ||
+                               (!a.causal && a.window > 0 && k0 + 31 >= i0 + a.window);
         step(s % kKvRing, sub, i0, need_mask);
       }
     }
@@ -413,7 +416,7 @@ __global__ __launch_bounds__(64 * HPW, 2) void attn_sink_bwd_dq_kernel(BwdArgs a
   f32x16 acc[2];  // dQ^T, [d block]
   acc[0] = acc[1] = zero_f32x16();
 
-  const int kend = a.causal ? min(len, q0 + kRows) : len;
+  const int kend = a.causal ? min(len, q0 + kRows) : (a.window > 0 ? min(len, q0 + kRows - 1 + a.window) : len);
   const int kbeg = a.window > 0 ? max(0, q0 - a.window + 1) : 0;
   const int kt_begin = kbeg / kDqTileKeys;
   const int kt_end = (kend + kDqTileKeys - 1) / kDqTileKeys;
@@ -460,7 +463,8 @@ __global__ __launch_bounds__(64 * HPW, 2) void attn_sink_bwd_dq_kernel(BwdArgs a
     const int k0 = kt * kDqTileKeys;
 
     const bool need_mask = (k0 + kDqTileKeys > len) || (a.causal && k0 + kDqTileKeys - 1 > q0) ||
-                           (a.window > 0 && k0 <= q0 + kRows - 1 - a.window);
+                           (a.window > 0 && k0 <= q0 + kRows - 1 - a.window) ||
+                           (!a.causal && a.window > 0 && k0 + kDqTileKeys - 1 >= q0 + a.window);
     // One tile: S^T = K Q^T and dP^T = V dO^T (rows = keys, loaded with the swap23 permutation),
     // P = exp2(S*scale*log2e - LSE*log2e), dS = P (dP - D), dQ^T += K^T dS^T, one 32-key block
     // after the other so that block 1's softmax overlaps block 0's dQ products. Returns the
@@ -499,10 +503,11 @@ __global__ __launch_bounds__(64 * HPW, 2) void attn_sink_bwd_dq_kernel(BwdArgs a
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) {
         if (need_mask) {  // uniform: only diagonal, window-edge and ragged tiles
+          const KeyBounds kb = key_bounds(qi, len, a.causal, a.window);
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int kj = k0 + 32 * mb + c_row(i, grp);
-            s[mb][i] = visible(qi, kj, len, a.causal, a.window) ? s[mb][i] : kNegInf;
+            s[mb][i] = ((kj > kb.lo) & (kj <= kb.hi)) ? s[mb][i] : kNegInf;
           }
         }
 #pragma unroll

@@ -117,10 +117,21 @@ __device__ __forceinline__ float sum_xor32(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Visibility of key j from query i inside one sequence (the sink is always visible). Bitwise
-// operators keep it branch-free.
-__device__ __forceinline__ bool visible(int i, int j, int len, int causal, int window) {
-  return (j < len) & ((causal == 0) | (j <= i)) & ((window <= 0) | (j > i - window));
+// Keys visible from query i of a sequence of `len` tokens (the sink is always visible): the
+// interval lo < j <= hi. Causal attention sees j <= i and, with a window W, j > i - W;
+// non-causal attention with a window sees the band i - W < j < i + W. A mask then tests each
+// key with two comparisons.
+struct KeyBounds {
+  int lo, hi;
+};
+__device__ __forceinline__ KeyBounds key_bounds(int i, int len, int causal, int window) {
+  int hi = len - 1;
+  if (causal) {
+    hi = min(hi, i);
+  } else if (window > 0) {
+    hi = min(hi, i + window - 1);
+  }
+  return {window > 0 ? i - window : -(1 << 30), hi};
 }
 
 // Makes a register value opaque to the optimiser (no instruction is emitted). Used at the top of

@@ -91,7 +91,9 @@ __global__ __launch_bounds__(64 * HPW, 2) void attn_sink_fwd_kernel(FwdArgs a) {
     o[1][nb] = zero_f32x16();
   }
 
-  const int kend = a.causal ? min(len, q0 + kRows) : len;
+  // Keys some row of the block can see: up to the last row (causal), or up to W - 1 past it (a
+  // non-causal window), and from W - 1 before the first row (any window).
+  const int kend = a.causal ? min(len, q0 + kRows) : (a.window > 0 ? min(len, q0 + kRows - 1 + a.window) : len);
   const int kbeg = a.window > 0 ? max(0, q0 - a.window + 1) : 0;
   const int kt_begin = kbeg / kTileKeys;
   const int kt_end = (kend + kTileKeys - 1) / kTileKeys;
@@ -154,17 +156,18 @@ __global__ __launch_bounds__(64 * HPW, 2) void attn_sink_fwd_kernel(FwdArgs a) {
       }
     }
     const bool need_mask = (k0 + kTileKeys > len) || (a.causal && k0 + kTileKeys - 1 > q0) ||
-                           (a.window > 0 && k0 <= q0 + kRows - 1 - a.window);
+                           (a.window > 0 && k0 <= q0 + kRows - 1 - a.window) ||
+                           (!a.causal && a.window > 0 && k0 + kTileKeys - 1 >= q0 + a.window);
     if (need_mask) {
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
-        const int qi = q0 + 32 * nb + l32;
+        const KeyBounds kb = key_bounds(q0 + 32 * nb + l32, len, a.causal, a.window);
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) {
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int kj = k0 + 32 * mb + c_row(i, grp);
-            s[mb][nb][i] = visible(qi, kj, len, a.causal, a.window) ? s[mb][nb][i] : kNegInf;
+            s[mb][nb][i] = ((kj > kb.lo) & (kj <= kb.hi)) ? s[mb][nb][i] : kNegInf;
           }
         }
       }

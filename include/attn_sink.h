@@ -28,10 +28,12 @@
  *      dq        [T, Hq, 64]  float32;  dk, dv [T, Hkv, 64] float32;  dsinks [Hq] float32
  *      cu_seqlens [B+1] int32 on the device, cu[0] = 0, non-decreasing, cu[B] = T
  *  - GQA: query head h reads KV head h / (Hq / Hkv); Hq must be a multiple of Hkv.
- *  - Masks: causal != 0 lets query i see keys j <= i of its own sequence. window = W > 0
- *    (requires causal) further restricts to j > i - W, i.e. exactly the last W keys including
- *    itself. window <= 0 means no window. The sink is visible from every row, is never masked and
- *    does not count toward W. The sink is added after scaling: it is never multiplied by scale.
+ *  - Masks: causal != 0 lets query i see keys j <= i of its own sequence. window = W > 0 with
+ *    causal further restricts to j > i - W, i.e. exactly the last W keys including itself; with
+ *    causal = 0 it is the symmetric band i - W < j < i + W (the pages only use causal windows;
+ *    the band is the plain non-causal reading). window <= 0 means no window. The sink is visible
+ *    from every row, is never masked and does not count toward W. The sink is added after
+ *    scaling: it is never multiplied by scale.
  *  - Outputs are overwritten, never accumulated into. The caller owns every buffer; the library
  *    allocates nothing, keeps no global state, and only enqueues work on `stream` (NULL = the
  *    default stream). Calls return before the GPU work finishes; errors raised by the device
@@ -60,7 +62,7 @@ enum {
                                      or max_seqlen > T, max_seqlen * Hq * 64 >= 2^31 (offsets
                                      inside one sequence are 32-bit), or T * Hq > 2^34 (grid size) */
   ATTN_SINK_ERR_UNSUPPORTED = -3, /* head_dim != 64 or out_dtype != ATTN_SINK_F32 */
-  ATTN_SINK_ERR_BAD_WINDOW = -4,  /* window > 0 without causal */
+  ATTN_SINK_ERR_BAD_WINDOW = -4,  /* window < 0 (attn_sink_decode_fwd only) */
   ATTN_SINK_ERR_WORKSPACE = -5,   /* workspace NULL or smaller than attn_sink_bwd_workspace_bytes() */
   ATTN_SINK_ERR_HIP = -6,         /* a HIP launch failed (hipGetLastError after the launch) */
   ATTN_SINK_ERR_ALIGN = -7        /* a tensor base pointer is not 16-byte aligned */

@@ -95,6 +95,13 @@ SMALL_CASES = {
     "exact_tiles": ((256, 128), 8, 8, True, 64, {}),
     "gqa3_causal": ((200, 70), 6, 2, True, 0, {}),
     "gqa6_window50": ((180,), 6, 1, True, 50, {}),
+    # non-causal attention with a window: the symmetric band |i - j| < W
+    "band_gqa4_w40": ((150, 70, 1), 8, 2, False, 40, {}),
+    "band_gqa8_w128": ((513, 129), 8, 1, False, 128, {}),
+    "band_w1": ((97, 33), 2, 1, False, 1, {}),
+    "band_w_ge_len": ((150, 40), 4, 1, False, 1000, {}),
+    "band_neg_inf_sinks": ((200, 63), 4, 2, False, 20, {"sinks": [-math.inf] * 4}),
+    "band_exact_tiles": ((256, 128), 8, 8, False, 64, {}),
 }
 
 
@@ -162,7 +169,7 @@ def _sample_keys(cu, causal, window, rng, n):
     return keys
 
 
-@pytest.mark.parametrize("name", ["causal4k", "window4k", "varlen_causal", "varlen_window", "long32k"])
+@pytest.mark.parametrize("name", ["causal4k", "window4k", "varlen_causal", "varlen_window", "long32k", "band4k"])
 def test_full_size_sampled(name):
     inp = make_workload_inputs(name)
     say(f"[gpu] full-size workload {name}: T={inp.total_tokens} B={len(inp.lengths)} window={inp.window}")

@@ -65,13 +65,16 @@ def workload(name: str, seed: int = 0) -> Workload:
     if name == "varlen_window":
         return Workload(name, _varlen_lengths(seed), 64, 8, window=128,
                         description="16 packed sequences, lengths U[512,8192], GQA 64/8, window 128")
+    if name == "band4k":
+        return Workload(name, (4096,), 64, 8, causal=False, window=128,
+                        description="4096 tokens, GQA 64/8, d=64, non-causal band |i - j| < 128")
     if name == "long32k":
         return Workload(name, (32768,), 64, 8, sink_scale=3.0,
                         description="32768 tokens, GQA 64/8, causal, sinks x3")
     raise KeyError(name)
 
 
-WORKLOAD_NAMES = ("tiny", "causal4k", "window4k", "varlen_causal", "varlen_window", "long32k")
+WORKLOAD_NAMES = ("tiny", "causal4k", "window4k", "varlen_causal", "varlen_window", "long32k", "band4k")
 
 
 @dataclass
@@ -138,7 +141,11 @@ def visible_pairs(lengths, causal: bool, window: int) -> int:
     for L in lengths:
         L = int(L)
         if not causal:
-            total += L * L
+            if window and window > 0:  # band i - W < j < i + W inside [0, L)
+                i = np.arange(L, dtype=np.int64)
+                total += int((np.minimum(i + int(window), L) - np.maximum(i - int(window) + 1, 0)).sum())
+            else:
+                total += L * L
         elif window and window > 0:
             W = int(window)
             m = min(L, W)
