@@ -110,16 +110,18 @@ __global__ __launch_bounds__(128 * NS, 2) void attn_sink_bwd_dkdv_kernel(BwdArgs
   static_assert(kKvRing == 2, "the waits below assume one step in flight");
 
   // Block order: KV group fastest (consecutive ids go to different XCDs, so each XCD works on
-  // few groups and their query rows stay in its L2), then head half, sequence, and key blocks
-  // ascending: under a causal mask the first key blocks see the most query rows, so the longest
-  // workgroups start first and the short ones fill in.
+  // few groups and their query rows stay in its L2), then head half. Then, with a window, the key
+  // blocks of one sequence back to back: neighbouring blocks share most of their query rows,
+  // which stay in L2 between them. Otherwise sequences, then key blocks ascending: under a
+  // causal mask the first key blocks see the most query rows, so the longest workgroups start
+  // first and the short ones fill in.
   const int bid = blockIdx.x;
   const int g = bid % a.Hkv;
   int rest = bid / a.Hkv;
   const int hh = rest % a.n_halves;
   rest /= a.n_halves;
-  const int b = rest % a.B;
-  const int kblk = (rest / a.B) * kKvKeysPerBlock;
+  const int b = a.window > 0 ? rest / a.n_kblocks : rest % a.B;
+  const int kblk = (a.window > 0 ? rest % a.n_kblocks : rest / a.B) * kKvKeysPerBlock;
   const int cs = a.cu[b];
   const int len = a.cu[b + 1] - cs;
   if (kblk >= len) return;  // uniform over the workgroup
