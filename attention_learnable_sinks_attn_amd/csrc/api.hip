@@ -42,10 +42,18 @@ int dsink_slots(const attn_sink_shape* s) { return s->total_tokens / kDqRowsPerW
 
 size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-int kv_halves(const attn_sink_shape* s) { return (s->num_heads_q / s->num_heads_kv) % 2 == 0 ? 2 : 1; }
+// The dK/dV pass splits each KV group's query heads over two workgroups only when its key blocks
+// alone would not fill the GPU several times over (about 2048 workgroups); the halves' fp32
+// partials are then added by the finish kernel. With one half the pass writes dK and dV itself.
+int kv_halves(const attn_sink_shape* s) {
+  const long long blocks = (long long)s->num_seqs * ((s->max_seqlen + kKvKeysPerBlock - 1) / kKvKeysPerBlock) *
+                           s->num_heads_kv;
+  return ((s->num_heads_q / s->num_heads_kv) % 2 == 0 && blocks < 2048) ? 2 : 1;
+}
 
 size_t dkv_part_bytes(const attn_sink_shape* s) {
-  return (size_t)2 * kv_halves(s) * s->total_tokens * s->num_heads_kv * s->head_dim * sizeof(float);
+  const int n = kv_halves(s);
+  return n == 1 ? 0 : (size_t)2 * n * s->total_tokens * s->num_heads_kv * s->head_dim * sizeof(float);
 }
 
 // Workspace: -LSE/scale [Hq, T], -D [Hq, T], dSink partials [Hq, n_slots], dK/dV partials per head

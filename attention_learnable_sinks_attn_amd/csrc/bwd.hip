@@ -13,17 +13,18 @@
 // Passes (all on the caller's stream, no atomics, bitwise reproducible):
 //  1. prep:  -LSE_i / scale and -D_i = -rowsum(dO * O) for every (head, row), in the workspace;
 //            clear the dSink partial sums.
-//  2. dkdv:  column-parallel. A workgroup owns 64 keys of one KV head and one half of the
-//            group's query heads: two key halves of 32 (one per wave) times one or two "head
-//            streams". Each stream streams its query rows 32 at a time through a 3-slot LDS ring
-//            filled by direct global->LDS copies issued two steps ahead (the two key halves of a
+//  2. dkdv:  column-parallel. A workgroup owns 64 keys of one KV head and all, or one half, of
+//            the group's query heads: two key halves of 32 (one per wave) times one or two "head
+//            streams". Each stream walks its query rows 64 at a time through a 2-slot LDS ring
+//            filled by direct global->LDS copies issued one step ahead (the two key halves of a
 //            stream split the copies and share the tiles); one barrier per step. The row tiles
 //            are stored with an XOR swizzle of their 16-byte chunks, which keeps both the
 //            fragment reads (rows permuted by swap23) and the transposing reads of Q^T / dO^T
 //            free of bank conflicts. dK^T and dV^T of each wave's 32 keys stay in registers; the
-//            two streams' partial sums are added in LDS at the end, and each head half writes its
-//            own fp32 partial. Splitting the heads doubles the number of workgroups, so that
-//            (launched longest first) they keep two per CU busy under a causal mask.
+//            two streams' partial sums are added in LDS at the end. With all heads in one
+//            workgroup it writes dK and dV; with head halves each half writes its own fp32
+//            partial. Halves double the number of workgroups, so that (launched longest first)
+//            short sequences still keep two per CU busy under a causal mask.
 //  3. dq:    row-parallel. A workgroup owns 32 query rows of `hpw` heads of one group (one head
 //            per wave) and streams 64-key tiles of K and V through a 3-slot LDS ring filled by
 //            direct copies two tiles ahead (swizzled like the dkdv tiles; K^T operands come from
@@ -32,7 +33,7 @@
 //            holds and writes sum_i P_{i,h} D~_i for its rows. D~ equals D mathematically but
 //            does not carry the bf16 rounding of the forward's P.V product, which matters
 //            because the terms of dL/dS_h cancel heavily.
-//  4. finish: dK = scale * (sum of the halves), dV = sum of the halves; and
+//  4. finish: with head halves, dK = scale * (sum of the halves), dV = sum of the halves; and
 //            dL/dS_h = -(sum of the partials of head h), summed in a fixed order.
 #include <type_traits>
 
@@ -344,10 +345,14 @@ __global__ __launch_bounds__(128 * NS, 2) void attn_sink_bwd_dkdv_kernel(BwdArgs
   if (st == 0) {
     const int key = k0 + l32;
     if (key < len) {
-      // This head half's partial sums (unscaled); attn_sink_bwd_finish_kernel adds the halves.
+      // With one head half these are dK (scaled here) and dV; otherwise this half's unscaled
+      // partial sums, which attn_sink_bwd_finish_kernel adds and scales.
       const size_t plane = (size_t)a.T * a.Hkv * kHeadDim;
-      float* dkrow = a.dkv_part + hh * plane + ((size_t)(cs + key) * a.Hkv + g) * kHeadDim;
-      float* dvrow = a.dkv_part + (a.n_halves + hh) * plane + ((size_t)(cs + key) * a.Hkv + g) * kHeadDim;
+      const size_t row = ((size_t)(cs + key) * a.Hkv + g) * kHeadDim;
+      const bool direct = a.n_halves == 1;
+      float* dkrow = direct ? a.dk + row : a.dkv_part + hh * plane + row;
+      float* dvrow = direct ? a.dv + row : a.dkv_part + (a.n_halves + hh) * plane + row;
+      const float kscale = direct ? a.scale : 1.0f;
 #pragma unroll
       for (int db = 0; db < 2; ++db) {
 #pragma unroll
@@ -359,7 +364,7 @@ __global__ __launch_bounds__(128 * NS, 2) void attn_sink_bwd_dkdv_kernel(BwdArgs
             kv += *reinterpret_cast<const f32x4*>(&red[l32 * kKvRedStride + d]);
             vv += *reinterpret_cast<const f32x4*>(&red[(32 + l32) * kKvRedStride + d]);
           }
-          *reinterpret_cast<f32x4*>(dkrow + d) = kv;
+          *reinterpret_cast<f32x4*>(dkrow + d) = kv * kscale;
           *reinterpret_cast<f32x4*>(dvrow + d) = vv;
         }
       }
@@ -569,9 +574,10 @@ __global__ __launch_bounds__(64 * HPW, 2) void attn_sink_bwd_dq_kernel(BwdArgs a
 }
 
 // ------------------------------------------------------------------------------------------
-// 4. Finish: dK = scale * (sum of the head halves' partials), dV = sum of the partials (blocks
-//    below n_sum_blocks, grid-stride), and dL/dS_h = -(sum of the partials of head h) (one block
-//    per head after those, fixed summation order).
+// 4. Finish: with head halves, dK = scale * (sum of the halves' partials), dV = sum of the
+//    partials (blocks below n_sum_blocks, grid-stride; none with a single half, whose dK/dV pass
+//    wrote dK and dV), and dL/dS_h = -(sum of the partials of head h) (one block per head after
+//    those, fixed summation order).
 // ------------------------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void attn_sink_bwd_finish_kernel(BwdArgs a, int n_sum_blocks) {
   if ((int)blockIdx.x >= n_sum_blocks) {
@@ -635,6 +641,7 @@ hipError_t launch_bwd_finish(const BwdArgs& a, hipStream_t stream) {
   const long long n4 = (long long)a.T * a.Hkv * (kHeadDim / 4);
   long long nsum = (n4 + 255) / 256;
   if (nsum > 4096) nsum = 4096;
+  if (a.n_halves == 1) nsum = 0;  // the dK/dV pass wrote dK and dV itself
   hipLaunchKernelGGL(attn_sink_bwd_finish_kernel, dim3((unsigned)(nsum + a.Hq)), dim3(256), 0, stream, a, (int)nsum);
   return hipGetLastError();
 }

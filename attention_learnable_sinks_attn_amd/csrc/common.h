@@ -283,7 +283,7 @@ struct BwdArgs {
   float* nlse;       // workspace: -LSE_i / scale (score units), [Hq, T]
   float* negd;       // workspace: -D_i = -rowsum(dO * O), [Hq, T]
   float* dsink_part; // per (head, row-block slot) partial sums of P_sink * D~, [Hq, n_slots]
-  float* dkv_part;   // dK / dV partial sums per head half: [2][n_halves][T][Hkv][64] (unscaled)
+  float* dkv_part;   // dK / dV partial sums per head half: [2][n_halves][T][Hkv][64] (unscaled; unused with one half)
   int n_slots;
   int n_halves;      // query-head halves of a KV group processed by separate dK/dV workgroups
   int T, B, Hq, Hkv, G;

@@ -93,9 +93,11 @@ int attn_sink_fwd(const void* q, const void* k, const void* v, const float* sink
 
 /*
  * Bytes of device workspace attn_sink_bwd needs for this shape: -LSE_i/scale and -D_i for every
- * (head, row), one dSink partial sum per (head, 32-row block), and fp32 dK/dV partial sums for
- * each half of a KV group's query heads (2 * halves * T * Hkv * 64 floats); each region 256-byte
- * aligned. Returns 0 if `shape` is NULL or invalid.
+ * (head, row), one dSink partial sum per (head, 32-row block), and, when the dK/dV pass splits a
+ * KV group's query heads over two workgroups (even Hq/Hkv and fewer than 2048 key blocks of 64
+ * over all sequences and KV heads, counted as num_seqs * ceil(max_seqlen / 64) * Hkv), fp32
+ * dK/dV partial sums for each half (2 * 2 * T * Hkv * 64 floats); each region 256-byte aligned.
+ * Returns 0 if `shape` is NULL or invalid.
  */
 size_t attn_sink_bwd_workspace_bytes(const attn_sink_shape* shape);
 

@@ -208,3 +208,17 @@ def test_decode_timed_entry_point_checks_event_count():
     evs = (ctypes.c_void_p * n)(*([P] * n))  # one too few
     rc = lib.attn_sink_decode_fwd_timed(P, P, P, P, 0, P, P, ctypes.byref(s), P, need, P, P, None, evs, n)
     assert rc == -2
+
+
+@needs_lib
+def test_workspace_without_head_halves():
+    lib = asa.load_library()
+    # 32768 tokens: 512 key blocks x 8 KV heads = 4096 dK/dV workgroups without splitting the query
+    # heads, so the pass writes dK/dV itself and needs no partial sums
+    s = shape(T=32768, maxlen=32768, hq=64, hkv=8)
+    need = lib.attn_sink_bwd_workspace_bytes(ctypes.byref(s))
+    assert need == 2 * 64 * 32768 * 4 + 64 * (32768 // 32 + 1 + 1) * 4
+    # an odd group never splits
+    s = shape(T=4096, maxlen=4096, hq=24, hkv=8)
+    dsink = 24 * (4096 // 32 + 2) * 4
+    assert lib.attn_sink_bwd_workspace_bytes(ctypes.byref(s)) == 2 * 24 * 4096 * 4 + (dsink + 255) // 256 * 256
