@@ -103,10 +103,15 @@ def _strerror(code: int) -> str:
         return "?"
 
 
+_OUT_DTYPES = {torch.float32: 0, torch.bfloat16: 1}
+
+
 def make_shape(q: torch.Tensor, k: torch.Tensor, cu_seqlens: torch.Tensor, max_seqlen: int,
-               softmax_scale: Optional[float]) -> Shape:
+               softmax_scale: Optional[float], out_dtype: torch.dtype = torch.float32) -> Shape:
+    if out_dtype not in _OUT_DTYPES:
+        raise TypeError(f"out_dtype must be float32 or bfloat16, got {out_dtype}")
     return Shape(int(q.shape[0]), int(cu_seqlens.numel()) - 1, int(max_seqlen), int(q.shape[1]), int(k.shape[1]),
-                 int(q.shape[2]), float(softmax_scale) if softmax_scale else 0.0, 0)
+                 int(q.shape[2]), float(softmax_scale) if softmax_scale else 0.0, _OUT_DTYPES[out_dtype])
 
 
 def _ptr(t: Optional[torch.Tensor]):
@@ -128,9 +133,11 @@ def _stream(device: torch.device) -> int:
 
 def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, sinks: torch.Tensor, cu_seqlens: torch.Tensor,
         max_seqlen: int, causal: bool = True, window: int = 0, softmax_scale: Optional[float] = None,
-        out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None):
+        out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+        out_dtype: torch.dtype = torch.float32):
     """Forward. q [T,Hq,64], k/v [T,Hkv,64] bf16; sinks [Hq] fp32; cu_seqlens [B+1] int32 (device).
-    Returns (out [T,Hq,64] fp32, lse [Hq,T] fp32)."""
+    Returns (out [T,Hq,64] in ``out_dtype`` (fp32, or bf16 for inference; the backward needs fp32),
+    lse [Hq,T] fp32)."""
     lib = load_library()
     dev = q.device
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
@@ -139,12 +146,12 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, sinks: torch.Tensor, 
     _check(cu_seqlens, "cu_seqlens", torch.int32, dev)
     T, Hq, d = q.shape
     if out is None:
-        out = torch.empty((T, Hq, d), dtype=torch.float32, device=dev)
+        out = torch.empty((T, Hq, d), dtype=out_dtype, device=dev)
     if lse is None:
         lse = torch.empty((Hq, T), dtype=torch.float32, device=dev)
-    _check(out, "out", torch.float32, dev)
+    _check(out, "out", out_dtype, dev)
     _check(lse, "lse", torch.float32, dev)
-    shape = make_shape(q, k, cu_seqlens, max_seqlen, softmax_scale)
+    shape = make_shape(q, k, cu_seqlens, max_seqlen, softmax_scale, out_dtype)
     rc = lib.attn_sink_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(sinks), int(bool(causal)), int(window), _ptr(cu_seqlens),
                            ctypes.byref(shape), _ptr(out), _ptr(lse), _stream(dev))
     if rc != 0:
@@ -199,8 +206,6 @@ def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, sinks: torch.Tensor, 
         raise AttnSinkError(rc, "attn_sink_bwd")
     return dq, dk, dv, dsinks
 
-
-_OUT_DTYPES = {torch.float32: 0, torch.bfloat16: 1}
 
 
 def make_decode_shape(q: torch.Tensor, k: torch.Tensor, cu_seqlens_q: torch.Tensor, max_q: int, max_k: int,

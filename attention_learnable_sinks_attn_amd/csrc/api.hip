@@ -14,13 +14,17 @@ namespace {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-int check_shape(const attn_sink_shape* s) {
+// bf16_out: whether the call can store its output in bf16 (the forward can; the backward reads
+// the forward's fp32 output).
+int check_shape(const attn_sink_shape* s, bool bf16_out = false) {
   if (s == nullptr) return ATTN_SINK_ERR_NULL_PTR;
   if (s->total_tokens < 0 || s->num_seqs < 1 || s->num_heads_q < 1 || s->num_heads_kv < 1 ||
       s->max_seqlen < 0 || s->max_seqlen > s->total_tokens || s->num_heads_q % s->num_heads_kv != 0) {
     return ATTN_SINK_ERR_BAD_SHAPE;
   }
-  if (s->head_dim != kHeadDim || s->out_dtype != ATTN_SINK_F32) return ATTN_SINK_ERR_UNSUPPORTED;
+  if (s->head_dim != kHeadDim || (s->out_dtype != ATTN_SINK_F32 && !(bf16_out && s->out_dtype == ATTN_SINK_BF16))) {
+    return ATTN_SINK_ERR_UNSUPPORTED;
+  }
   // Element offsets are 64-bit in the kernels, but grid sizes (the prep pass launches T * Hq / 16
   // workgroups) and per-head row indices are 32-bit.
   const long long rows_q = (long long)s->total_tokens * s->num_heads_q;
@@ -204,7 +208,7 @@ extern "C" {
 int attn_sink_fwd(const void* q, const void* k, const void* v, const float* sinks, int causal, int window,
                   const int32_t* cu_seqlens, const attn_sink_shape* shape, void* out, float* lse,
                   hipStream_t stream) {
-  int rc = check_shape(shape);
+  int rc = check_shape(shape, true);
   if (rc) return rc;
   if (sinks == nullptr || cu_seqlens == nullptr) return ATTN_SINK_ERR_NULL_PTR;
   const int T = shape->total_tokens;
@@ -217,7 +221,8 @@ int attn_sink_fwd(const void* q, const void* k, const void* v, const float* sink
   a.v = static_cast<const __bf16*>(v);
   a.sinks = sinks;
   a.cu = cu_seqlens;
-  a.out = static_cast<float*>(out);
+  a.out = out;
+  a.out_bf16 = shape->out_dtype == ATTN_SINK_BF16 ? 1 : 0;
   a.lse = lse;
   a.T = T;
   a.B = shape->num_seqs;

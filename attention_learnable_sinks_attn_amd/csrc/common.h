@@ -258,8 +258,9 @@ struct FwdArgs {
   const __bf16* v;
   const float* sinks;
   const int32_t* cu;
-  float* out;
+  void* out;             // [T, Hq, 64], fp32 or bf16 (out_bf16)
   float* lse;
+  int out_bf16;
   int T, B, Hq, Hkv, G;  // G = Hq / Hkv
   int hpw;               // query heads per workgroup (= waves per workgroup), divides G
   int n_qblocks;         // ceil(max_seqlen / rows per wave)

@@ -253,14 +253,20 @@ __global__ __launch_bounds__(64 * HPW, 2) void attn_sink_fwd_kernel(FwdArgs a) {
     const float inv = ltot > 0.0f ? 1.0f / ltot : 0.0f;
     const int qi = q0 + 32 * nb + l32;
     if (qi < len) {
-      float* orow = a.out + ((size_t)(cs + qi) * a.Hq + h) * kHeadDim;
+      const size_t orow = ((size_t)(cs + qi) * a.Hq + h) * kHeadDim;
 #pragma unroll
       for (int db = 0; db < 2; ++db) {
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
           f32x4 val = {o[db][nb][4 * r4] * inv, o[db][nb][4 * r4 + 1] * inv, o[db][nb][4 * r4 + 2] * inv,
                        o[db][nb][4 * r4 + 3] * inv};
-          *reinterpret_cast<f32x4*>(orow + 32 * db + 8 * r4 + 4 * grp) = val;
+          const size_t e = orow + 32 * db + 8 * r4 + 4 * grp;
+          if (a.out_bf16) {  // round to nearest even, as a separate conversion of the fp32 result would
+            typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+            *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(a.out) + e) = __builtin_convertvector(val, bf16x4);
+          } else {
+            *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + e) = val;
+          }
         }
       }
       if (grp == 0) {

@@ -23,7 +23,7 @@
  *      q, dout   [T, Hq, 64]  bfloat16
  *      k, v      [T, Hkv, 64] bfloat16
  *      sinks     [Hq]         float32 (one logit per query head, natural-log units, NOT scaled)
- *      out       [T, Hq, 64]  float32
+ *      out       [T, Hq, 64]  float32 (attn_sink_fwd may store bf16 instead: out_dtype)
  *      lse       [Hq, T]      float32, natural log of the full denominator (sink included)
  *      dq        [T, Hq, 64]  float32;  dk, dv [T, Hkv, 64] float32;  dsinks [Hq] float32
  *      cu_seqlens [B+1] int32 on the device, cu[0] = 0, non-decreasing, cu[B] = T
@@ -61,7 +61,8 @@ enum {
   ATTN_SINK_ERR_BAD_SHAPE = -2,   /* T < 0, B < 1, Hq < 1, Hkv < 1, Hq % Hkv != 0, max_seqlen < 0
                                      or max_seqlen > T, max_seqlen * Hq * 64 >= 2^31 (offsets
                                      inside one sequence are 32-bit), or T * Hq > 2^34 (grid size) */
-  ATTN_SINK_ERR_UNSUPPORTED = -3, /* head_dim != 64 or out_dtype != ATTN_SINK_F32 */
+  ATTN_SINK_ERR_UNSUPPORTED = -3, /* head_dim != 64, or out_dtype not ATTN_SINK_F32 (attn_sink_bwd)
+                                     or not ATTN_SINK_F32 / ATTN_SINK_BF16 (attn_sink_fwd) */
   ATTN_SINK_ERR_BAD_WINDOW = -4,  /* window < 0 (attn_sink_decode_fwd only) */
   ATTN_SINK_ERR_WORKSPACE = -5,   /* workspace NULL or smaller than attn_sink_bwd_workspace_bytes() */
   ATTN_SINK_ERR_HIP = -6,         /* a HIP launch failed (hipGetLastError after the launch) */
@@ -79,7 +80,9 @@ typedef struct attn_sink_shape {
   int32_t num_heads_kv;  /* Hkv, divides Hq */
   int32_t head_dim;      /* must be 64 */
   float softmax_scale;   /* <= 0 selects 1/sqrt(head_dim) */
-  int32_t out_dtype;     /* must be ATTN_SINK_F32 (out, dq, dk, dv are float32) */
+  int32_t out_dtype;     /* ATTN_SINK_F32; attn_sink_fwd also takes ATTN_SINK_BF16 (out rounded to
+                            bf16, nearest even, e.g. for inference prefill). attn_sink_bwd needs the
+                            fp32 forward output: out, dq, dk, dv are float32 there */
 } attn_sink_shape;
 
 /*

@@ -85,7 +85,7 @@ def test_forward_argument_errors():
     assert fwd(lib, shape(maxlen=-1)) == -2
     assert fwd(lib, shape(maxlen=129)) == -2
     assert fwd(lib, shape(d=128)) == -3
-    assert fwd(lib, shape(dtype=1)) == -3
+    assert fwd(lib, shape(dtype=2)) == -3  # bf16 (1) is a valid forward output dtype
     assert fwd(lib, shape(), q=PM) == -7
     assert fwd(lib, shape(), out=PM) == -7
 
@@ -99,6 +99,7 @@ def test_backward_argument_errors():
     assert bwd(lib, shape(), dq=None) == -1
     assert bwd(lib, shape(hq=5, hkv=2)) == -2
     assert bwd(lib, shape(d=32)) == -3
+    assert bwd(lib, shape(dtype=1)) == -3  # the backward reads the fp32 forward output
     s = shape()
     need = lib.attn_sink_bwd_workspace_bytes(ctypes.byref(s))
     assert bwd(lib, s, ws=None) == -5

@@ -207,3 +207,19 @@ def test_full_size_sampled(name):
     ds_heads = heads[:2]
     ds_ref = oracle.dsink_heads(inp.q, inp.k, inp.v, inp.sinks, inp.dout, cu, ds_heads, inp.causal, inp.window)
     check_dsink(g["dsinks"].cpu().double().numpy()[ds_heads], ds_ref, ds_heads, label=f" (heads {ds_heads})")
+
+
+@pytest.mark.parametrize("causal,window", [(True, 0), (True, 77), (False, 0), (False, 40)])
+def test_forward_bf16_output_is_rounded_fp32_output(causal, window):
+    """out_dtype bf16: the same fp32 result rounded to nearest even; LSE unchanged."""
+    inp = make_inputs((300, 1, 129), 8, 2, 64, causal=causal, window=window, seed=4)
+    dev = torch.device("cuda:0")
+    q, k, v = (t.to(dev) for t in (inp.q, inp.k, inp.v))
+    sinks, cu = inp.sinks.to(dev), inp.cu_seqlens.to(dev)
+    say(f"[gpu] bf16 forward output: causal={causal} window={window}")
+    o32, l32 = asa.fwd(q, k, v, sinks, cu, inp.max_seqlen, causal, window)
+    o16, l16 = asa.fwd(q, k, v, sinks, cu, inp.max_seqlen, causal, window, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert o16.dtype == torch.bfloat16
+    assert torch.equal(o16, o32.to(torch.bfloat16))
+    assert torch.equal(l16, l32)
