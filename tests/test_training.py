@@ -25,12 +25,13 @@ def test_cu_seqlens_from_position_ids_rejects(bad):
 
 
 @pytest.mark.gpu
-def test_autograd_matches_oracle():
+@pytest.mark.parametrize("causal,window", [(True, 0), (True, 40), (False, 0), (False, 40)])
+def test_autograd_matches_oracle(causal, window):
     import oracle
     from attention_learnable_sinks_attn_amd.training import SinkAttention
     from workloads import make_inputs
 
-    inp = make_inputs((150, 0, 70), 8, 2, 64, causal=True, window=0, seed=11)
+    inp = make_inputs((150, 0, 70), 8, 2, 64, causal=causal, window=window, seed=11)
     dev = torch.device("cuda:0")
     pos = torch.cat([torch.arange(n) for n in inp.lengths if n > 0])
     cu, maxlen = cu_seqlens_from_position_ids(pos)
@@ -38,7 +39,7 @@ def test_autograd_matches_oracle():
     q = inp.q.to(dev).requires_grad_(True)
     k = inp.k.to(dev).requires_grad_(True)
     v = inp.v.to(dev).requires_grad_(True)
-    layer = SinkAttention(8, 2, causal=True).to(dev)
+    layer = SinkAttention(8, 2, causal=causal, window=window).to(dev)
     with torch.no_grad():
         layer.sinks.copy_(inp.sinks.to(dev))
     out = layer(q, k, v, cu.to(dev), maxlen)
@@ -46,7 +47,7 @@ def test_autograd_matches_oracle():
     (out * dout).sum().backward()
 
     rdq, rdk, rdv, rds, rout, _ = oracle.backward(inp.q, inp.k, inp.v, inp.sinks, inp.dout, inp.cu_seqlens,
-                                                  True, 0, return_forward=True)
+                                                  causal, window, return_forward=True)
     assert abs(out.detach().cpu().double().numpy() - rout).max() <= 1e-2
     # gradients come back in the inputs' dtype (bf16): allow its storage rounding on top of 1e-2
     for name, g, r in (("dq", q.grad, rdq), ("dk", k.grad, rdk), ("dv", v.grad, rdv)):
