@@ -241,22 +241,19 @@ __global__ __launch_bounds__(128 * NS, 2) void attn_sink_bwd_dkdv_kernel(BwdArgs
       u32x2 tr[16];
       tr_all(slot_lds, tr);
       if (need_mask) {
-        // Row of register i: i0 + 8grp + r_i with r_i = 16(i/8) + i%8. Visible iff the row and
-        // the key exist, the key is not after the row (causal), the row is less than `window`
-        // rows after the key and, without causality, the key less than `window` keys after the
-        // row. (The empty asm keeps the comparisons in this branch.)
+        // Row of register i: i0 + 8grp + r_i with r_i = 16(i/8) + i%8. Key kj is seen by the
+        // rows lo .. hi: from the key itself (causal) or W - 1 rows before it (a non-causal
+        // window), up to W - 1 rows after it (any window), within the sequence; none if the key
+        // is past the end. (The empty asm keeps the arithmetic in this branch.)
         int kj = k0 + l32;
         asm volatile("" : "+v"(kj));
-        const int dq = i0 + 8 * grp - kj;     // row - key for r_i = 0
-        const int rlim = len - i0 - 8 * grp;  // row exists iff r_i < rlim
-        const bool key_ok = kj < len;
+        const int lo = a.causal ? kj : (a.window > 0 ? kj - a.window + 1 : 0);
+        const int hi = kj >= len ? lo - 1 : (a.window > 0 ? min(len - 1, kj + a.window - 1) : len - 1);
+        const unsigned cnt = (unsigned)max(hi - lo + 1, 0);
+        const int base = i0 + 8 * grp - lo;  // row - lo for r_i = 0
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const int r = 16 * (i >> 3) + (i & 7);
-          const int t = dq + r;
-          const bool vis = key_ok & (r < rlim) & ((a.causal == 0) | (t >= 0)) & ((a.window <= 0) | (t < a.window)) &
-                           ((a.causal != 0) | (a.window <= 0) | (t > -a.window));
-          sc[i] = vis ? sc[i] : kNegInf;
+          sc[i] = in_span(base + 16 * (i >> 3) + (i & 7), cnt) ? sc[i] : kNegInf;
         }
       }
       float pmax = 0.0f;
@@ -511,10 +508,11 @@ __global__ __launch_bounds__(64 * HPW, 2) void attn_sink_bwd_dq_kernel(BwdArgs a
       for (int mb = 0; mb < 2; ++mb) {
         if (need_mask) {  // uniform: only diagonal, window-edge and ragged tiles
           const KeyBounds kb = key_bounds(qi, len, a.causal, a.window);
+          const unsigned cnt = (unsigned)max(kb.hi - kb.lo, 0);  // visible keys kb.lo + 1 .. kb.hi
+          const int base = k0 + 32 * mb + 8 * grp - kb.lo - 1;   // key - (kb.lo + 1) for register 0
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
-            const int kj = k0 + 32 * mb + c_row(i, grp);
-            s[mb][i] = ((kj > kb.lo) & (kj <= kb.hi)) ? s[mb][i] : kNegInf;
+            s[mb][i] = in_span(base + 16 * (i >> 3) + (i & 7), cnt) ? s[mb][i] : kNegInf;
           }
         }
 #pragma unroll

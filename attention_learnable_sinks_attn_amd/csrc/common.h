@@ -134,6 +134,10 @@ __device__ __forceinline__ KeyBounds key_bounds(int i, int len, int causal, int 
   return {window > 0 ? i - window : -(1 << 30), hi};
 }
 
+// Membership of x in the interval first .. first + count - 1 as one unsigned comparison:
+// in_span(x - first, count) (a negative offset wraps to a large unsigned value).
+__device__ __forceinline__ bool in_span(int offset, unsigned count) { return (unsigned)offset < count; }
+
 // Makes a register value opaque to the optimiser (no instruction is emitted). Used at the top of
 // rarely taken branches so that their arithmetic is not speculated onto the common path.
 __device__ __forceinline__ void opaque(f32x16& x) {

@@ -162,12 +162,13 @@ __global__ __launch_bounds__(64 * HPW, 2) void attn_sink_fwd_kernel(FwdArgs a) {
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
         const KeyBounds kb = key_bounds(q0 + 32 * nb + l32, len, a.causal, a.window);
+        const unsigned cnt = (unsigned)max(kb.hi - kb.lo, 0);  // visible keys kb.lo + 1 .. kb.hi
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) {
+          const int base = k0 + 32 * mb + 8 * grp - kb.lo - 1;  // key - (kb.lo + 1) for register 0
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
-            const int kj = k0 + 32 * mb + c_row(i, grp);
-            s[mb][nb][i] = ((kj > kb.lo) & (kj <= kb.hi)) ? s[mb][nb][i] : kNegInf;
+            s[mb][nb][i] = in_span(base + 16 * (i >> 3) + (i & 7), cnt) ? s[mb][nb][i] : kNegInf;
           }
         }
       }
