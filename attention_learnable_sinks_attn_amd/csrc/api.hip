@@ -110,7 +110,12 @@ int bwd_impl(const void* q, const void* k, const void* v, const float* sinks, co
   a.dkv_part = reinterpret_cast<float*>(static_cast<char*>(workspace) + 2 * row_plane_bytes(shape) +
                                         dsink_part_bytes(shape));
   a.n_slots = dsink_slots(shape);
-  a.n_halves = kv_halves(shape);
+  // Head halves balance the causal triangle on short sequences; with a window every key block has
+  // the same work, and one round of full-group workgroups (two per CU) beats two rounds of halves
+  // plus the finish pass's sum. (The workspace is sized for the halves either way.)
+  const long long kv_blocks =
+      (long long)shape->num_seqs * ((shape->max_seqlen + kKvKeysPerBlock - 1) / kKvKeysPerBlock) * shape->num_heads_kv;
+  a.n_halves = (window > 0 && kv_blocks >= 512) ? 1 : kv_halves(shape);
   a.T = T;
   a.B = shape->num_seqs;
   a.Hq = shape->num_heads_q;
