@@ -123,7 +123,8 @@ int bwd_impl(const void* q, const void* k, const void* v, const float* sinks, co
   a.G = a.Hq / a.Hkv;
   a.hpw = heads_per_group_split(a.G);
   a.kv_streams = (a.G / a.n_halves) % 2 == 0 ? 2 : 1;  // two key halves x (two head streams if possible)
-  a.n_qblocks = (shape->max_seqlen + kDqRowsPerWave - 1) / kDqRowsPerWave;
+  const int dq_rows = kDqRowsPerWave * (4 / a.hpw);  // rows per dQ workgroup
+  a.n_qblocks = (shape->max_seqlen + dq_rows - 1) / dq_rows;
   a.n_kblocks = (shape->max_seqlen + kKvKeysPerBlock - 1) / kKvKeysPerBlock;
   a.causal = causal ? 1 : 0;
   a.window = window > 0 ? window : 0;
@@ -235,7 +236,8 @@ int attn_sink_fwd(const void* q, const void* k, const void* v, const float* sink
   a.Hkv = shape->num_heads_kv;
   a.G = a.Hq / a.Hkv;
   a.hpw = heads_per_group_split(a.G);
-  a.n_qblocks = (shape->max_seqlen + kFwdRowsPerWave - 1) / kFwdRowsPerWave;
+  const int fwd_rows = kFwdRowsPerWave * (4 / a.hpw);  // rows per forward workgroup
+  a.n_qblocks = (shape->max_seqlen + fwd_rows - 1) / fwd_rows;
   a.causal = causal ? 1 : 0;
   a.window = window > 0 ? window : 0;
   a.scale_log2 = resolve_scale(shape) * kLog2e;

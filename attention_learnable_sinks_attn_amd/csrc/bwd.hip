@@ -25,10 +25,11 @@
 //            workgroup it writes dK and dV; with head halves each half writes its own fp32
 //            partial. Halves double the number of workgroups, so that (launched longest first)
 //            short sequences still keep two per CU busy under a causal mask.
-//  3. dq:    row-parallel. A workgroup owns 32 query rows of `hpw` heads of one group (one head
-//            per wave) and streams 64-key tiles of K and V through a 3-slot LDS ring filled by
-//            direct copies two tiles ahead (swizzled like the dkdv tiles; K^T operands come from
-//            transposing LDS loads of the K tile).
+//  3. dq:    row-parallel. A workgroup of four waves owns `hpw` heads of one group and 4 / hpw
+//            blocks of 32 query rows (one head and row block per wave) and streams 64-key tiles
+//            of K and V through a 3-slot LDS ring filled by direct copies two tiles ahead
+//            (swizzled like the dkdv tiles; K^T operands come from transposing LDS loads of the K
+//            tile).
 //            Besides dQ it accumulates D~_i = sum_j P_ij dP_ij from the fp32 P and dP it already
 //            holds and writes sum_i P_{i,h} D~_i for its rows. D~ equals D mathematically but
 //            does not carry the bf16 rounding of the forward's P.V product, which matters
@@ -377,10 +378,12 @@ constexpr int kDqTileBytes = kDqTileKeys * kHeadDim * 2;  // one swizzled 64-key
 constexpr int kDqSlotBytes = 2 * kDqTileBytes;             // K tile, then V tile
 constexpr int kDqRing = 3;                                 // LDS ring slots (two tiles in flight)
 
+// HPW query heads of one KV group x RPW = 4 / HPW blocks of 32 rows per workgroup (four waves).
 template <int HPW>
-__global__ __launch_bounds__(64 * HPW, 2) void attn_sink_bwd_dq_kernel(BwdArgs a) {
-  constexpr int kRows = kDqRowsPerWave;
-  constexpr int CPW = 2 * (kDqTileBytes / 1024) / HPW;  // copies per wave and tile (K and V)
+__global__ __launch_bounds__(256, 2) void attn_sink_bwd_dq_kernel(BwdArgs a) {
+  constexpr int kRows = kDqRowsPerWave;                 // query rows per wave
+  constexpr int RPW = 4 / HPW;                          // row blocks per workgroup
+  constexpr int CPW = 2 * (kDqTileBytes / 1024) / 4;    // copies per wave and tile (K and V)
   __shared__ __attribute__((aligned(1024))) unsigned char ring[kDqRing * kDqSlotBytes];
 
   const int n_hs = a.Hq / HPW;
@@ -390,18 +393,20 @@ __global__ __launch_bounds__(64 * HPW, 2) void attn_sink_bwd_dq_kernel(BwdArgs a
   const int spg = a.G / HPW;
   const int hs = (inner % a.Hkv) * spg + inner / a.Hkv;
   const int b = rest % a.B;
-  const int qb = a.n_qblocks - 1 - rest / a.B;
   const int cs = a.cu[b];
   const int len = a.cu[b + 1] - cs;
-  const int q0 = qb * kRows;
-  if (q0 >= len) return;
+  const int qw0 = (a.n_qblocks - 1 - rest / a.B) * kRows * RPW;  // longest causal rows first
+  if (qw0 >= len) return;
 
   const int wave = wave_id();
   const int lane = threadIdx.x & 63;
   const int l32 = lane & 31;
   const int grp = lane >> 5;
-  const int h = hs * HPW + wave;
+  const int h = hs * HPW + wave % HPW;
   const int g = h / a.G;
+  const int q0 = qw0 + kRows * (wave / HPW);  // this wave's first row
+  const int qb = q0 / kRows;                   // its row block within the sequence
+  const bool rows_live = RPW == 1 || q0 < len;  // waves past the sequence end only copy
 
   // Q^T and dO^T as B operands: lane holds query q0 + l32, d = 16c + 8grp + (0..7).
   const int qi = q0 + l32;
@@ -420,10 +425,16 @@ __global__ __launch_bounds__(64 * HPW, 2) void attn_sink_bwd_dq_kernel(BwdArgs a
   f32x16 acc[2];  // dQ^T, [d block]
   acc[0] = acc[1] = zero_f32x16();
 
-  const int kend = a.causal ? min(len, q0 + kRows) : (a.window > 0 ? min(len, q0 + kRows - 1 + a.window) : len);
-  const int kbeg = a.window > 0 ? max(0, q0 - a.window + 1) : 0;
-  const int kt_begin = kbeg / kDqTileKeys;
-  const int kt_end = (kend + kDqTileKeys - 1) / kDqTileKeys;
+  // Keys a row range can see (as in the forward): the workgroup streams its whole range's tiles,
+  // each wave computes only its own.
+  auto key_end = [&](int r1) {  // rows before r1
+    return a.causal ? min(len, r1) : (a.window > 0 ? min(len, r1 - 1 + a.window) : len);
+  };
+  auto key_begin = [&](int r0) { return a.window > 0 ? max(0, r0 - a.window + 1) : 0; };
+  const int kt_begin = key_begin(qw0) / kDqTileKeys;
+  const int kt_end = (key_end(qw0 + kRows * RPW) + kDqTileKeys - 1) / kDqTileKeys;
+  const int kw_begin = key_begin(q0);
+  const int kw_end = rows_live ? key_end(q0 + kRows) : 0;
   const int kv_stride = a.Hkv * kHeadDim;
   const __bf16* kbase = a.k + (size_t)cs * kv_stride + (size_t)g * kHeadDim;
   const __bf16* vbase = a.v + (size_t)cs * kv_stride + (size_t)g * kHeadDim;
@@ -465,6 +476,8 @@ __global__ __launch_bounds__(64 * HPW, 2) void attn_sink_bwd_dq_kernel(BwdArgs a
     __syncthreads();
     if (kt + 2 < kt_end) issue(kt + 2);
     const int k0 = kt * kDqTileKeys;
+    // Wave-uniform: skip a tile that holds none of this wave's keys.
+    if (RPW > 1 && (k0 >= kw_end || k0 + kDqTileKeys <= kw_begin)) continue;
 
     const bool need_mask = (k0 + kDqTileKeys > len) || (a.causal && k0 + kDqTileKeys - 1 > q0) ||
                            (a.window > 0 && k0 <= q0 + kRows - 1 - a.window) ||
@@ -564,7 +577,7 @@ __global__ __launch_bounds__(64 * HPW, 2) void attn_sink_bwd_dq_kernel(BwdArgs a
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) wsum += __shfl_xor(wsum, off);
-  if (lane == 0) {
+  if (lane == 0 && rows_live) {  // a wave past the sequence end has no slot (its partial stays 0)
     // Unique slot per (sequence, row block): floor(cs / rows) + b + qb never collides.
     const int slot = cs / kRows + b + qb;
     a.dsink_part[(size_t)h * a.n_slots + slot] = wsum;
@@ -626,7 +639,7 @@ hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream) {
 hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream) {
   const long long nblocks = (long long)a.n_qblocks * (a.Hq / a.hpw) * a.B;
   if (nblocks <= 0) return hipSuccess;
-  const dim3 grid((unsigned)nblocks), block(64 * a.hpw);
+  const dim3 grid((unsigned)nblocks), block(256);
   switch (a.hpw) {
     case 4: hipLaunchKernelGGL(attn_sink_bwd_dq_kernel<4>, grid, block, 0, stream, a); break;
     case 2: hipLaunchKernelGGL(attn_sink_bwd_dq_kernel<2>, grid, block, 0, stream, a); break;

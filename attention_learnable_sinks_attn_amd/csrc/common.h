@@ -267,7 +267,7 @@ struct FwdArgs {
   int out_bf16;
   int T, B, Hq, Hkv, G;  // G = Hq / Hkv
   int hpw;               // query heads per workgroup (= waves per workgroup), divides G
-  int n_qblocks;         // ceil(max_seqlen / rows per wave)
+  int n_qblocks;         // ceil(max_seqlen / rows per workgroup)
   int causal, window;
   float scale_log2;      // softmax scale * log2(e)
 };

@@ -7,10 +7,11 @@
 // and the running denominator at exp(S_h - S_h) = 1, while the output accumulator starts at 0
 // because the sink has no value row. LSE = max + log(denominator) therefore includes the sink.
 //
-// Work split. A workgroup owns one block of 64 query rows of one sequence and HPW query heads
-// that share one KV head (GQA); wave w handles head hs*HPW + w. K and V tiles of 64 keys pass
-// through a 3-slot LDS ring shared by the workgroup's waves, filled by direct global->LDS copies
-// two tiles ahead (the waves split the copies); one barrier per tile. The tiles are stored with
+// Work split. A workgroup of four waves owns HPW query heads that share one KV head (GQA) and
+// 4 / HPW consecutive blocks of 64 query rows of one sequence; wave w handles head hs*HPW + w%HPW
+// and row block w/HPW. K and V tiles of 64 keys pass through a 3-slot LDS ring shared by the
+// workgroup's waves, filled by direct global->LDS copies two tiles ahead (the waves split the
+// copies); one barrier per tile; a wave skips the tiles its rows cannot see. The tiles are stored with
 // an XOR swizzle of their 16-byte chunks (tile_swz), so that neither the K fragment reads nor the
 // transposing V^T reads have bank conflicts. Per tile each wave computes
 //   S^T = K Q^T   (32x32x16 MFMA; keys on the C rows, the wave's 64 queries on the columns)
@@ -36,11 +37,14 @@ constexpr int kTileBytes = kTileKeys * kHeadDim * 2;  // one swizzled 64-key til
 constexpr int kSlotBytes = 2 * kTileBytes;             // K tile, then V tile
 constexpr int kRing = 3;                               // LDS ring slots (two tiles in flight)
 
+// HPW query heads of one KV group x RPW = 4 / HPW blocks of 64 rows per workgroup (four waves),
+// so that groups of fewer than four heads still share each K/V tile among four waves.
 template <int HPW>
-__global__ __launch_bounds__(64 * HPW, 2) void attn_sink_fwd_kernel(FwdArgs a) {
+__global__ __launch_bounds__(256, 2) void attn_sink_fwd_kernel(FwdArgs a) {
   constexpr int NB = 2;                                 // 32-query column blocks per wave
-  constexpr int kRows = 32 * NB;
-  constexpr int CPW = 2 * (kTileBytes / 1024) / HPW;    // copies per wave and tile (K and V)
+  constexpr int kRows = 32 * NB;                        // query rows per wave
+  constexpr int RPW = 4 / HPW;                          // row blocks per workgroup
+  constexpr int CPW = 2 * (kTileBytes / 1024) / 4;      // copies per wave and tile (K and V)
   __shared__ __attribute__((aligned(1024))) unsigned char ring[kRing * kSlotBytes];
 
   const int n_hs = a.Hq / HPW;
@@ -56,16 +60,18 @@ __global__ __launch_bounds__(64 * HPW, 2) void attn_sink_fwd_kernel(FwdArgs a) {
 
   const int cs = a.cu[b];
   const int len = a.cu[b + 1] - cs;
-  const int q0 = qb * kRows;
-  if (q0 >= len) return;
+  const int qw0 = qb * kRows * RPW;  // first row of the workgroup
+  if (qw0 >= len) return;
 
   const int tid = threadIdx.x;
   const int wave = wave_id();
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int grp = lane >> 5;
-  const int h = hs * HPW + wave;
+  const int h = hs * HPW + wave % HPW;
   const int g = h / a.G;
+  const int q0 = qw0 + kRows * (wave / HPW);  // this wave's first row
+  const bool rows_live = RPW == 1 || q0 < len;  // waves past the sequence end only copy
 
   // Q^T as the B operand of S^T = K Q^T: lane holds query q0 + 32nb + l32, d = 16c + 8grp + (0..7).
   bf16x8 qf[NB][4];
@@ -91,12 +97,17 @@ __global__ __launch_bounds__(64 * HPW, 2) void attn_sink_fwd_kernel(FwdArgs a) {
     o[1][nb] = zero_f32x16();
   }
 
-  // Keys some row of the block can see: up to the last row (causal), or up to W - 1 past it (a
-  // non-causal window), and from W - 1 before the first row (any window).
-  const int kend = a.causal ? min(len, q0 + kRows) : (a.window > 0 ? min(len, q0 + kRows - 1 + a.window) : len);
-  const int kbeg = a.window > 0 ? max(0, q0 - a.window + 1) : 0;
-  const int kt_begin = kbeg / kTileKeys;
-  const int kt_end = (kend + kTileKeys - 1) / kTileKeys;
+  // Keys some row of a row range can see: up to the last row (causal), or up to W - 1 past it (a
+  // non-causal window), and from W - 1 before the first row (any window). The workgroup streams
+  // the tiles of its whole range; each wave computes only the tiles of its own.
+  auto key_end = [&](int r1) {  // rows before r1
+    return a.causal ? min(len, r1) : (a.window > 0 ? min(len, r1 - 1 + a.window) : len);
+  };
+  auto key_begin = [&](int r0) { return a.window > 0 ? max(0, r0 - a.window + 1) : 0; };
+  const int kt_begin = key_begin(qw0) / kTileKeys;
+  const int kt_end = (key_end(qw0 + kRows * RPW) + kTileKeys - 1) / kTileKeys;
+  const int kw_begin = key_begin(q0);
+  const int kw_end = rows_live ? key_end(q0 + kRows) : 0;
 
   const int kv_stride = a.Hkv * kHeadDim;
   const __bf16* kbase = a.k + (size_t)cs * kv_stride + (size_t)g * kHeadDim;
@@ -141,6 +152,8 @@ __global__ __launch_bounds__(64 * HPW, 2) void attn_sink_fwd_kernel(FwdArgs a) {
     const unsigned char* slot = ring + (kt % kRing) * kSlotBytes;
     const unsigned vt_lds = ring_lds + (kt % kRing) * kSlotBytes + kTileBytes;
     const int k0 = kt * kTileKeys;
+    // Wave-uniform: skip a tile that holds none of this wave's keys.
+    if (RPW > 1 && (k0 >= kw_end || k0 + kTileKeys <= kw_begin)) continue;
 
     // S^T = K Q^T for two 32-key row blocks.
     f32x16 s[2][NB];
@@ -253,7 +266,7 @@ __global__ __launch_bounds__(64 * HPW, 2) void attn_sink_fwd_kernel(FwdArgs a) {
     const float ltot = sum_xor32(lsum[nb]);
     const float inv = ltot > 0.0f ? 1.0f / ltot : 0.0f;
     const int qi = q0 + 32 * nb + l32;
-    if (qi < len) {
+    if (qi < len) {  // also false for every lane of a wave past the sequence end
       const size_t orow = ((size_t)(cs + qi) * a.Hq + h) * kHeadDim;
 #pragma unroll
       for (int db = 0; db < 2; ++db) {
@@ -282,7 +295,7 @@ __global__ __launch_bounds__(64 * HPW, 2) void attn_sink_fwd_kernel(FwdArgs a) {
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
   const long long nblocks = (long long)a.n_qblocks * (a.Hq / a.hpw) * a.B;
   if (nblocks <= 0) return hipSuccess;
-  const dim3 grid((unsigned)nblocks), block(64 * a.hpw);
+  const dim3 grid((unsigned)nblocks), block(256);
   switch (a.hpw) {
     case 4: hipLaunchKernelGGL(attn_sink_fwd_kernel<4>, grid, block, 0, stream, a); break;
     case 2: hipLaunchKernelGGL(attn_sink_fwd_kernel<2>, grid, block, 0, stream, a); break;
