@@ -64,14 +64,14 @@ KERNEL_FLOPS_PER_PAIR_D = {
 # (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch) scaled by what the same counters read for the
 # copy probe; valid only for kernel sources with the recorded digest.
 TRAFFIC = {
-    ("causal4k", "attn_sink_bwd_dkdv_kernel"): {"bytes": 147683689, "digest": "b9d7f12f092249d0"},
-    ("window4k", "attn_sink_bwd_dkdv_kernel"): {"bytes": 115809686, "digest": "b9d7f12f092249d0"},
-    ("window4k", "attn_sink_bwd_dq_kernel"): {"bytes": 144907839, "digest": "b9d7f12f092249d0"},
-    ("varlen_window", "attn_sink_bwd_dkdv_kernel"): {"bytes": 1755224990, "digest": "b9d7f12f092249d0"},
-    ("varlen_window", "attn_sink_bwd_dq_kernel"): {"bytes": 2518725922, "digest": "b9d7f12f092249d0"},
-    ("band4k", "attn_sink_bwd_dkdv_kernel"): {"bytes": 118443714, "digest": "b9d7f12f092249d0"},
-    ("band4k", "attn_sink_bwd_dq_kernel"): {"bytes": 144900436, "digest": "b9d7f12f092249d0"},
-    ("decode32k", "attn_sink_decode_partial_kernel"): {"bytes": 368436655, "digest": "b9d7f12f092249d0"},
+    ("causal4k", "attn_sink_bwd_dkdv_kernel"): {"bytes": 147984513, "digest": "f0181bbc23a59041"},
+    ("window4k", "attn_sink_bwd_dkdv_kernel"): {"bytes": 106871599, "digest": "f0181bbc23a59041"},
+    ("window4k", "attn_sink_bwd_dq_kernel"): {"bytes": 144899288, "digest": "f0181bbc23a59041"},
+    ("varlen_window", "attn_sink_bwd_dkdv_kernel"): {"bytes": 1719659726, "digest": "f0181bbc23a59041"},
+    ("varlen_window", "attn_sink_bwd_dq_kernel"): {"bytes": 2519283309, "digest": "f0181bbc23a59041"},
+    ("band4k", "attn_sink_bwd_dkdv_kernel"): {"bytes": 125499721, "digest": "f0181bbc23a59041"},
+    ("band4k", "attn_sink_bwd_dq_kernel"): {"bytes": 144892437, "digest": "f0181bbc23a59041"},
+    ("decode32k", "attn_sink_decode_partial_kernel"): {"bytes": 368437140, "digest": "f0181bbc23a59041"},
 }
 
 
