@@ -165,31 +165,37 @@ __global__ __launch_bounds__(128 * NS, 2) void attn_sink_bwd_dkdv_kernel(BwdArgs
 
   // Each stream owns a ring of 2 slots; step s lives in slot s % 2. The two key halves of a
   // stream split the copies of a step: half 0 copies the Q tile and the -LSE/scale, -D rows,
-  // half 1 the dO tile (tile_copy layout; full tiles take a precomputed per-lane offset).
+  // half 1 the dO tile (tile_copy layout). Full tiles go through buffer resources; in the last,
+  // partial tile rows past the end repeat the last row (they are masked).
   unsigned char* ring = smem + st * kKvStreamBytes;
   const int qstride = a.Hq * kHeadDim;  // elements per token row of q / dout
-  const int crow = lane >> 3;
-  const int coff0 = crow * qstride + 8 * ((lane & 7) ^ tile_swz(crow));      // rows 8u + crow, u even
-  const int coff1 = crow * qstride + 8 * ((lane & 7) ^ tile_swz(8 + crow));  // u odd
+  const unsigned qrow_bytes = 2u * qstride;
+  unsigned coff[2];
+  tile_copy_offsets(lane, qrow_bytes, coff);
   auto issue = [&](int j, int t, int slot) {
-    const int h = h0 + NS * j;
-    const int i0 = i_begin + kKvRows * (n_sub - 1 - t);
+    // (The step counters are wave-uniform; reading them from lane 0 keeps the addresses scalar.)
+    const int h = __builtin_amdgcn_readfirstlane(h0 + NS * j);
+    const int i0 = __builtin_amdgcn_readfirstlane(i_begin + kKvRows * (n_sub - 1 - t));
     unsigned char* dst = ring + slot * kKvSlotBytes + kh * kKvTileBytes;
     const __bf16* src = (kh ? a.dout : a.q) + ((size_t)(cs + i0) * a.Hq + h) * kHeadDim;
+    unsigned char* rows = ring + slot * kKvSlotBytes + 2 * kKvTileBytes;
+    const float* nl = a.nlse + (size_t)h * a.T + cs + i0;
+    const float* nd = a.negd + (size_t)h * a.T + cs + i0;
     if (i0 + kKvRows <= len) {
+      const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(src, kKvRows * qrow_bytes);
 #pragma unroll
-      for (int u = 0; u < kKvTileBytes / 1024; ++u) {
-        dma16(src + 8 * u * qstride + ((u & 1) ? coff1 : coff0), dst + 1024 * u);
+      for (int u = 0; u < kKvTileBytes / 1024; ++u) tile_copy_full(rs, coff, qrow_bytes, dst, u);
+      if (kh == 0) {  // -LSE/scale rows, then -D rows (64 each)
+        bdma4(buffer_rsrc(nl, 4 * kKvRows), 4 * lane, 0, rows);
+        bdma4(buffer_rsrc(nd, 4 * kKvRows), 4 * lane, 0, rows + 4 * kKvRows);
       }
-    } else {  // last, partial tile: rows past the end repeat the last row (they are masked)
+    } else {
 #pragma unroll
       for (int u = 0; u < kKvTileBytes / 1024; ++u) tile_copy(src, 0, len - 1 - i0, qstride, dst, u, lane);
-    }
-    if (kh == 0) {  // -LSE/scale rows, then -D rows (64 each)
-      const float* nl = a.nlse + (size_t)h * a.T + cs;
-      const float* nd = a.negd + (size_t)h * a.T + cs;
-      dma4(nl + min(i0 + lane, len - 1), ring + slot * kKvSlotBytes + 2 * kKvTileBytes);
-      dma4(nd + min(i0 + lane, len - 1), ring + slot * kKvSlotBytes + 2 * kKvTileBytes + 4 * kKvRows);
+      if (kh == 0) {
+        dma4(nl + min(lane, len - 1 - i0), rows);
+        dma4(nd + min(lane, len - 1 - i0), rows + 4 * kKvRows);
+      }
     }
   };
   auto wait_own_step = [&]() { wait_vmcnt<0>(); };  // this wave's copies of the current step
@@ -440,18 +446,26 @@ __global__ __launch_bounds__(256, 2) void attn_sink_bwd_dq_kernel(BwdArgs a) {
   const __bf16* vbase = a.v + (size_t)cs * kv_stride + (size_t)g * kHeadDim;
 
   // K and V tiles of 64 keys, swizzled (see tile_swz), in a 3-slot ring filled by direct
-  // global->LDS copies issued two tiles ahead; the waves split each tile's 16 copies. Keys past
-  // the sequence end repeat its last key (finite data; they are masked).
+  // global->LDS copies issued two tiles ahead; the waves split each tile's 16 copies (waves 0-1
+  // the K tile, 2-3 the V tile). Full tiles go through a buffer resource; in the last, partial
+  // tile keys past the sequence end repeat its last key (finite data; they are masked).
+  static_assert(8 % CPW == 0, "a wave's copies stay within one tile");
+  const unsigned row_bytes = 2u * kv_stride;
+  unsigned coff[2];
+  tile_copy_offsets(lane, row_bytes, coff);
   auto issue = [&](int kt) {
-    unsigned char* slot = ring + (kt % kDqRing) * kDqSlotBytes;
+    const int u0 = wave * CPW;  // copies u0 .. u0 + CPW - 1 of 16: K for u < 8, V after
+    const bool is_v = u0 >= 8;
+    const __bf16* src = is_v ? vbase : kbase;
+    unsigned char* tile = ring + (kt % kDqRing) * kDqSlotBytes + (is_v ? kDqTileBytes : 0);
+    const int row0 = kt * kDqTileKeys;
+    if (row0 + kDqTileKeys <= len) {
+      const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(src + (size_t)row0 * kv_stride, kDqTileKeys * row_bytes);
 #pragma unroll
-    for (int i = 0; i < CPW; ++i) {
-      const int u = wave * CPW + i;  // 0..7: K copies, 8..15: V copies
-      if (u < 8) {
-        tile_copy(kbase, kt * kDqTileKeys, len - 1, kv_stride, slot, u, lane);
-      } else {
-        tile_copy(vbase, kt * kDqTileKeys, len - 1, kv_stride, slot + kDqTileBytes, u - 8, lane);
-      }
+      for (int i = 0; i < CPW; ++i) tile_copy_full(rs, coff, row_bytes, tile, (u0 + i) & 7);
+    } else {
+#pragma unroll
+      for (int i = 0; i < CPW; ++i) tile_copy(src, row0, len - 1, kv_stride, tile, (u0 + i) & 7, lane);
     }
   };
 

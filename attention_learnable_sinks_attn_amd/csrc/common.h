@@ -163,6 +163,21 @@ __device__ __forceinline__ void dma4(const void* src, void* lds_dst) {
   __builtin_amdgcn_global_load_lds(src, (lds_void*)lds_dst, 4, 0, 0);
 }
 
+// The same copies addressed through a buffer resource: the 64-bit base sits in scalar registers,
+// so a copy needs only a per-lane 32-bit offset `voff` and a wave-uniform offset `soff`, with no
+// 64-bit address arithmetic in vector registers. Reads at or past `bytes` from the base return
+// zero; the callers only use resources whose every read lies inside the tensor.
+constexpr int kRawBufferWord3 = 0x00020000;  // raw (unswizzled) buffer, 32-bit data format
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, unsigned bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, kRawBufferWord3);
+}
+__device__ __forceinline__ void bdma16(__amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff, void* lds_dst) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_dst, 16, (int)voff, (int)soff, 0, 0);
+}
+__device__ __forceinline__ void bdma4(__amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff, void* lds_dst) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_dst, 4, (int)voff, (int)soff, 0, 0);
+}
+
 // s_waitcnt vmcnt(N) (expcnt and lgkmcnt left unconstrained).
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -253,6 +268,20 @@ __device__ __forceinline__ void tile_copy(const __bf16* base, int row0, int last
                                           int u, int lane) {
   const int r = 8 * u + (lane >> 3);
   dma16(base + (size_t)min(row0 + r, last) * stride + 8 * ((lane & 7) ^ tile_swz(r)), tile + 1024 * u);
+}
+
+// Copies of a full tile (all 64 rows inside the sequence) through a buffer resource based at the
+// tile's first row, rows `row_bytes` apart. Copy u moves the same bytes as tile_copy(u): lane l's
+// offset is off[u % 2] (row l/8 and its swizzled chunk; the swizzle of row 8u + l/8 depends on u
+// only through u % 2) plus the uniform 8u rows.
+__device__ __forceinline__ void tile_copy_offsets(int lane, unsigned row_bytes, unsigned (&off)[2]) {
+  const int r = lane >> 3;
+  off[0] = r * row_bytes + 16 * ((lane & 7) ^ tile_swz(r));
+  off[1] = r * row_bytes + 16 * ((lane & 7) ^ tile_swz(r + 8));
+}
+__device__ __forceinline__ void tile_copy_full(__amdgpu_buffer_rsrc_t rsrc, const unsigned (&off)[2],
+                                               unsigned row_bytes, unsigned char* tile, int u) {
+  bdma16(rsrc, off[u & 1], 8u * u * row_bytes, tile + 1024 * u);
 }
 
 // Work descriptors (filled on the host).

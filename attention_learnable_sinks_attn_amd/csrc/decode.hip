@@ -71,12 +71,28 @@ __global__ __launch_bounds__(64) void attn_sink_decode_partial_kernel(DecodeArgs
     const int kv_stride = a.Hkv * kHeadDim;
     const __bf16* kbase = a.k + (size_t)ck * kv_stride + (size_t)g * kHeadDim;
     const __bf16* vbase = a.v + (size_t)ck * kv_stride + (size_t)g * kHeadDim;
+    // Full tiles go through buffer resources; in a partial last tile, keys past the end repeat
+    // the last key (finite data; they are masked).
+    const unsigned row_bytes = 2u * kv_stride;
+    unsigned coff[2];
+    tile_copy_offsets(lane, row_bytes, coff);
     auto issue = [&](int kt) {
       unsigned char* slot = ring + (kt % kDecRing) * kDecSlotBytes;
+      const int row0 = kt * kDecTileKeys;
+      if (row0 + kDecTileKeys <= lk) {
+        const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(kbase + (size_t)row0 * kv_stride, kDecTileKeys * row_bytes);
+        const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(vbase + (size_t)row0 * kv_stride, kDecTileKeys * row_bytes);
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        tile_copy(kbase, kt * kDecTileKeys, lk - 1, kv_stride, slot, u, lane);
-        tile_copy(vbase, kt * kDecTileKeys, lk - 1, kv_stride, slot + kDecTileBytes, u, lane);
+        for (int u = 0; u < 8; ++u) {
+          tile_copy_full(rk, coff, row_bytes, slot, u);
+          tile_copy_full(rv, coff, row_bytes, slot + kDecTileBytes, u);
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          tile_copy(kbase, row0, lk - 1, kv_stride, slot, u, lane);
+          tile_copy(vbase, row0, lk - 1, kv_stride, slot + kDecTileBytes, u, lane);
+        }
       }
     };
     int aoff[4];

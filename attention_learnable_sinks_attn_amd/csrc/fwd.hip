@@ -114,19 +114,27 @@ __global__ __launch_bounds__(256, 2) void attn_sink_fwd_kernel(FwdArgs a) {
   const __bf16* vbase = a.v + (size_t)cs * kv_stride + (size_t)g * kHeadDim;
 
   // K and V tiles of 64 keys, swizzled (see tile_swz), in a 3-slot ring filled by direct
-  // global->LDS copies issued two tiles ahead; the waves split each tile's 16 copies. Keys past
-  // the sequence end repeat its last key (finite data; they are masked). V^T operands come from
-  // transposing LDS loads of the V tile.
+  // global->LDS copies issued two tiles ahead; the waves split each tile's 16 copies (waves 0-1
+  // the K tile, 2-3 the V tile). Full tiles go through a buffer resource; in the last, partial
+  // tile keys past the sequence end repeat its last key (finite data; they are masked). V^T
+  // operands come from transposing LDS loads of the V tile.
+  static_assert(8 % CPW == 0, "a wave's copies stay within one tile");
+  const unsigned row_bytes = 2u * kv_stride;
+  unsigned coff[2];
+  tile_copy_offsets(lane, row_bytes, coff);
   auto issue = [&](int kt) {
-    unsigned char* slot = ring + (kt % kRing) * kSlotBytes;
+    const int u0 = wave * CPW;  // copies u0 .. u0 + CPW - 1 of 16: K for u < 8, V after
+    const bool is_v = u0 >= 8;
+    const __bf16* src = is_v ? vbase : kbase;
+    unsigned char* tile = ring + (kt % kRing) * kSlotBytes + (is_v ? kTileBytes : 0);
+    const int row0 = kt * kTileKeys;
+    if (row0 + kTileKeys <= len) {
+      const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(src + (size_t)row0 * kv_stride, kTileKeys * row_bytes);
 #pragma unroll
-    for (int i = 0; i < CPW; ++i) {
-      const int u = wave * CPW + i;  // 0..7: K copies, 8..15: V copies
-      if (u < 8) {
-        tile_copy(kbase, kt * kTileKeys, len - 1, kv_stride, slot, u, lane);
-      } else {
-        tile_copy(vbase, kt * kTileKeys, len - 1, kv_stride, slot + kTileBytes, u - 8, lane);
-      }
+      for (int i = 0; i < CPW; ++i) tile_copy_full(rs, coff, row_bytes, tile, (u0 + i) & 7);
+    } else {
+#pragma unroll
+      for (int i = 0; i < CPW; ++i) tile_copy(src, row0, len - 1, kv_stride, tile, (u0 + i) & 7, lane);
     }
   };
   int aoff[4];
