@@ -25,8 +25,8 @@ int check_shape(const attn_sink_shape* s, bool bf16_out = false) {
   if (s->head_dim != kHeadDim || (s->out_dtype != ATTN_SINK_F32 && !(bf16_out && s->out_dtype == ATTN_SINK_BF16))) {
     return ATTN_SINK_ERR_UNSUPPORTED;
   }
-  // Element offsets are 64-bit in the kernels, but grid sizes (the prep pass launches T * Hq / 16
-  // workgroups) and per-head row indices are 32-bit.
+  // Element offsets are 64-bit in the kernels, but grid sizes and per-head row indices are
+  // 32-bit.
   const long long rows_q = (long long)s->total_tokens * s->num_heads_q;
   if (rows_q > (1LL << 34)) return ATTN_SINK_ERR_BAD_SHAPE;
   // Within one sequence, element offsets (row * heads * 64) are 32-bit.
@@ -60,8 +60,8 @@ size_t dkv_part_bytes(const attn_sink_shape* s) {
   return n == 1 ? 0 : (size_t)2 * n * s->total_tokens * s->num_heads_kv * s->head_dim * sizeof(float);
 }
 
-// Workspace: -LSE/scale [Hq, T], -D [Hq, T], dSink partials [Hq, n_slots], dK/dV partials per head
-// half, each 256-byte aligned.
+// Workspace: -LSE/scale [Hq, T], -D [Hq, T] (both written by the dQ pass for the dK/dV pass), dSink
+// partials [Hq, n_slots], dK/dV partials per head half, each 256-byte aligned.
 size_t row_plane_bytes(const attn_sink_shape* s) {
   return round256((size_t)s->num_heads_q * s->total_tokens * sizeof(float));
 }
@@ -132,7 +132,7 @@ int bwd_impl(const void* q, const void* k, const void* v, const float* sinks, co
   a.scale_log2 = a.scale * kLog2e;
 
   typedef hipError_t (*launcher)(const BwdArgs&, hipStream_t);
-  const launcher steps[kBwdNumKernels] = {launch_bwd_prep, launch_bwd_dkdv, launch_bwd_dq, launch_bwd_finish};
+  const launcher steps[kBwdNumKernels] = {launch_bwd_dq, launch_bwd_dkdv, launch_bwd_finish};
   for (int i = 0; i < kBwdNumKernels; ++i) {
     if (events && hipEventRecord(static_cast<hipEvent_t>(events[i]), stream) != hipSuccess) return ATTN_SINK_ERR_HIP;
     if (steps[i](a, stream) != hipSuccess) return ATTN_SINK_ERR_HIP;
@@ -335,8 +335,8 @@ const char* attn_sink_decode_kernel_name(int i) {
 int attn_sink_bwd_num_kernels(void) { return kBwdNumKernels; }
 
 const char* attn_sink_bwd_kernel_name(int i) {
-  static const char* const names[kBwdNumKernels] = {"attn_sink_bwd_prep_kernel", "attn_sink_bwd_dkdv_kernel",
-                                                    "attn_sink_bwd_dq_kernel", "attn_sink_bwd_finish_kernel"};
+  static const char* const names[kBwdNumKernels] = {"attn_sink_bwd_dq_kernel", "attn_sink_bwd_dkdv_kernel",
+                                                    "attn_sink_bwd_finish_kernel"};
   return (i >= 0 && i < kBwdNumKernels) ? names[i] : nullptr;
 }
 

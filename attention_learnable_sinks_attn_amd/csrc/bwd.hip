@@ -11,8 +11,16 @@
 //   dQ = scale dS K,  dK = scale dS^T Q,  dV = P^T dO.
 //
 // Passes (all on the caller's stream, no atomics, bitwise reproducible):
-//  1. prep:  -LSE_i / scale and -D_i = -rowsum(dO * O) for every (head, row), in the workspace;
-//            clear the dSink partial sums.
+//  1. dq:    row-parallel. A workgroup of four waves owns `hpw` heads of one group and 4 / hpw
+//            blocks of 32 query rows (one head and row block per wave) and streams 64-key tiles
+//            of K and V through a 3-slot LDS ring filled by direct copies two tiles ahead
+//            (swizzled like the dkdv tiles; K^T operands come from transposing LDS loads of the K
+//            tile). Each wave first forms D_i = dO_i . O_i for its rows from the dO it holds as
+//            an operand and O, and leaves -D_i and -LSE_i / scale in the workspace for pass 2.
+//            Besides dQ it accumulates D~_i = sum_j P_ij dP_ij from the fp32 P and dP it already
+//            holds and writes sum_i P_{i,h} D~_i for its rows. D~ equals D mathematically but
+//            does not carry the bf16 rounding of the forward's P.V product, which matters
+//            because the terms of dL/dS_h cancel heavily.
 //  2. dkdv:  column-parallel. A workgroup owns 64 keys of one KV head and all, or one half, of
 //            the group's query heads: two key halves of 32 (one per wave) times one or two "head
 //            streams". Each stream walks its query rows 64 at a time through a 2-slot LDS ring
@@ -25,16 +33,7 @@
 //            workgroup it writes dK and dV; with head halves each half writes its own fp32
 //            partial. Halves double the number of workgroups, so that (launched longest first)
 //            short sequences still keep two per CU busy under a causal mask.
-//  3. dq:    row-parallel. A workgroup of four waves owns `hpw` heads of one group and 4 / hpw
-//            blocks of 32 query rows (one head and row block per wave) and streams 64-key tiles
-//            of K and V through a 3-slot LDS ring filled by direct copies two tiles ahead
-//            (swizzled like the dkdv tiles; K^T operands come from transposing LDS loads of the K
-//            tile).
-//            Besides dQ it accumulates D~_i = sum_j P_ij dP_ij from the fp32 P and dP it already
-//            holds and writes sum_i P_{i,h} D~_i for its rows. D~ equals D mathematically but
-//            does not carry the bf16 rounding of the forward's P.V product, which matters
-//            because the terms of dL/dS_h cancel heavily.
-//  4. finish: with head halves, dK = scale * (sum of the halves), dV = sum of the halves; and
+//  3. finish: with head halves, dK = scale * (sum of the halves), dV = sum of the halves; and
 //            dL/dS_h = -(sum of the partials of head h), summed in a fixed order.
 #include <type_traits>
 
@@ -43,56 +42,6 @@
 namespace attn_sink {
 
 namespace {
-
-constexpr int kLdsStride = 72;  // bf16 per staged 64-element row (16-byte aligned, 8 pad)
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-
-// ------------------------------------------------------------------------------------------
-// 1. -D_i = -sum_d dO[i,h,d] * O[i,h,d] and -LSE_i / scale. A block handles 64 consecutive rows
-//    of one head: 16 lanes per row (4 elements each), each 16-lane group 4 rows 16 apart, so the
-//    [Hq, T] results are written contiguously and each lane keeps 4 row loads in flight.
-// ------------------------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void attn_sink_bwd_prep_kernel(BwdArgs a) {
-  constexpr int kRowsPerBlock = 64;
-  const int tblocks = (a.T + kRowsPerBlock - 1) / kRowsPerBlock;
-  // With T = 0 there are no rows (tblocks = 0, and the single launched block only clears below).
-  if (tblocks > 0 && (int)blockIdx.x < a.Hq * tblocks) {
-    const int h = blockIdx.x / tblocks;
-    const int t0 = (blockIdx.x - h * tblocks) * kRowsPerBlock + (threadIdx.x >> 4);
-    const int part = threadIdx.x & 15;
-    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-    f32x4 o[4];
-    bf16x4 d[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int t = min(t0 + 16 * k, a.T - 1);  // in [0, T): rows past the end repeat the last (not stored)
-      const size_t row = (size_t)t * a.Hq + h;
-      o[k] = *reinterpret_cast<const f32x4*>(a.out + row * kHeadDim + 4 * part);
-      d[k] = *reinterpret_cast<const bf16x4*>(a.dout + row * kHeadDim + 4 * part);
-    }
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      float acc = o[k][0] * (float)d[k][0] + o[k][1] * (float)d[k][1] + o[k][2] * (float)d[k][2] +
-                  o[k][3] * (float)d[k][3];
-      acc += __shfl_xor(acc, 8, 16);
-      acc += __shfl_xor(acc, 4, 16);
-      acc += __shfl_xor(acc, 2, 16);
-      acc += __shfl_xor(acc, 1, 16);
-      const int t = t0 + 16 * k;
-      if (t < a.T && part == 0) {
-        const size_t r = (size_t)h * a.T + t;
-        a.negd[r] = -acc;
-        a.nlse[r] = -a.lse[r] / a.scale;
-      }
-    }
-  }
-  // Clear the dSink partials (rows of the dq pass that exit early never write theirs).
-  const long long nparts = (long long)a.Hq * a.n_slots;
-  for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < nparts;
-       i += (long long)gridDim.x * blockDim.x) {
-    a.dsink_part[i] = 0.0f;
-  }
-}
 
 // ------------------------------------------------------------------------------------------
 // 2. dK, dV: column-parallel over 64-key blocks.
@@ -377,7 +326,7 @@ __global__ __launch_bounds__(128 * NS, 2) void attn_sink_bwd_dkdv_kernel(BwdArgs
 }
 
 // ------------------------------------------------------------------------------------------
-// 3. dQ and the dSink partials: row-parallel over 32-row query blocks.
+// 1. dQ, D and the dSink partials: row-parallel over 32-row query blocks.
 // ------------------------------------------------------------------------------------------
 constexpr int kDqTileKeys = 64;
 constexpr int kDqTileBytes = kDqTileKeys * kHeadDim * 2;  // one swizzled 64-key tile (K or V)
@@ -425,8 +374,29 @@ __global__ __launch_bounds__(256, 2) void attn_sink_bwd_dq_kernel(BwdArgs a) {
     qf[c] = load_bf16x8(a.q + off);
     df[c] = load_bf16x8(a.dout + off);
   }
-  const float lse2 = -a.nlse[(size_t)h * a.T + cs + qc] * a.scale_log2;  // LSE_i * log2(e)
-  const float nd = a.negd[(size_t)h * a.T + cs + qc];                   // -D_i
+  // D_i = dO_i . O_i: this lane's 32 products (the d positions of its dO operand), then the other
+  // half of the row from lane ^ 32. -D_i and -LSE_i / scale go to the workspace for the dK/dV pass.
+  float dpart = 0.0f;
+  {
+    const float* orow = a.out + ((size_t)(cs + qc) * a.Hq + h) * kHeadDim + 8 * grp;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const f32x4 o0 = *reinterpret_cast<const f32x4*>(orow + 16 * c);
+      const f32x4 o1 = *reinterpret_cast<const f32x4*>(orow + 16 * c + 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        dpart = __builtin_fmaf(o0[e], (float)df[c][e], dpart);
+        dpart = __builtin_fmaf(o1[e], (float)df[c][4 + e], dpart);
+      }
+    }
+  }
+  const float nd = -sum_xor32(dpart);                              // -D_i
+  const float nl = -a.lse[(size_t)h * a.T + cs + qc] / a.scale;   // -LSE_i / scale
+  const float lse2 = -nl * a.scale_log2;                           // LSE_i * log2(e)
+  if (qok && grp == 0) {
+    a.negd[(size_t)h * a.T + cs + qi] = nd;
+    a.nlse[(size_t)h * a.T + cs + qi] = nl;
+  }
   float dsum = 0.0f;
   f32x16 acc[2];  // dQ^T, [d block]
   acc[0] = acc[1] = zero_f32x16();
@@ -591,15 +561,30 @@ __global__ __launch_bounds__(256, 2) void attn_sink_bwd_dq_kernel(BwdArgs a) {
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) wsum += __shfl_xor(wsum, off);
-  if (lane == 0 && rows_live) {  // a wave past the sequence end has no slot (its partial stays 0)
+  if (lane == 0 && rows_live) {  // a wave past the sequence end has no slot
     // Unique slot per (sequence, row block): floor(cs / rows) + b + qb never collides.
     const int slot = cs / kRows + b + qb;
     a.dsink_part[(size_t)h * a.n_slots + slot] = wsum;
   }
+  // The slots no row block maps to (a few between consecutive sequences with rows, those before
+  // the first and after the last) get zeros from the neighbouring first / last row blocks, so
+  // that every slot is written exactly once and the finish pass can sum all of them.
+  if (rows_live) {
+    float* part = a.dsink_part + (size_t)h * a.n_slots;
+    if (q0 + kRows >= len) {  // last row block: up to the first slot of the next sequence with rows
+      int nb = b + 1;
+      while (nb < a.B && a.cu[nb + 1] == a.cu[nb]) ++nb;
+      const int to = nb < a.B ? a.cu[nb] / kRows + nb : a.n_slots;
+      for (int j = cs / kRows + b + qb + 1 + lane; j < to; j += 64) part[j] = 0.0f;
+    }
+    if (q0 == 0 && cs == a.cu[0]) {  // first row block of the first sequence with rows
+      for (int j = lane; j < cs / kRows + b; j += 64) part[j] = 0.0f;
+    }
+  }
 }
 
 // ------------------------------------------------------------------------------------------
-// 4. Finish: with head halves, dK = scale * (sum of the halves' partials), dV = sum of the
+// 3. Finish: with head halves, dK = scale * (sum of the halves' partials), dV = sum of the
 //    partials (blocks below n_sum_blocks, grid-stride; none with a single half, whose dK/dV pass
 //    wrote dK and dV), and dL/dS_h = -(sum of the partials of head h) (one block per head after
 //    those, fixed summation order).
@@ -609,7 +594,10 @@ __global__ __launch_bounds__(256) void attn_sink_bwd_finish_kernel(BwdArgs a, in
     const int h = blockIdx.x - n_sum_blocks;
     __shared__ float part[4];
     float acc = 0.0f;
-    for (int i = threadIdx.x; i < a.n_slots; i += 256) acc += a.dsink_part[(size_t)h * a.n_slots + i];
+    // The dQ pass wrote every slot (partials or zeros), unless no sequence has rows.
+    if (a.cu[a.B] != a.cu[0]) {
+      for (int i = threadIdx.x; i < a.n_slots; i += 256) acc += a.dsink_part[(size_t)h * a.n_slots + i];
+    }
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
     if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = acc;
@@ -631,13 +619,6 @@ __global__ __launch_bounds__(256) void attn_sink_bwd_finish_kernel(BwdArgs a, in
 }
 
 }  // namespace
-
-hipError_t launch_bwd_prep(const BwdArgs& a, hipStream_t stream) {
-  long long nblocks = (long long)a.Hq * ((a.T + 63) / 64);
-  if (nblocks < 1) nblocks = 1;  // still clears the dSink partials when T = 0
-  hipLaunchKernelGGL(attn_sink_bwd_prep_kernel, dim3((unsigned)nblocks), dim3(256), 0, stream, a);
-  return hipGetLastError();
-}
 
 hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream) {
   const long long nblocks = (long long)a.n_kblocks * a.B * a.Hkv * a.n_halves;

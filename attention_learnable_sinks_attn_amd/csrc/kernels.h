@@ -12,11 +12,10 @@ constexpr int kKvKeysPerBlock = 64;   // keys per workgroup in the column-parall
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
 
 // Backward passes, in enqueue order.
-constexpr int kBwdNumKernels = 4;
+constexpr int kBwdNumKernels = 3;
 constexpr int kDecodeNumKernels = 2;  // partial, combine
-hipError_t launch_bwd_prep(const BwdArgs& a, hipStream_t stream);    // -LSE/scale, -D_i, zero dSink partials
-hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream);    // dK, dV partials per head half
-hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream);      // dQ, dSink partials
+hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream);      // dQ, -D_i, -LSE/scale, dSink partials
+hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream);    // dK, dV (or partials per head half)
 hipError_t launch_bwd_finish(const BwdArgs& a, hipStream_t stream);  // dK, dV = sum of halves; dSink
 
 // Inference-shaped forward: per-chunk partials, then the combine with the sink.

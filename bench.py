@@ -53,7 +53,6 @@ METRIC = "sink-attention fwd+bwd bf16 TFLOP/s + % MFMA peak (GQA 64/8, d=64, 4k 
 # forward QK^T + PV; dK/dV pass S, dP, dV, dK; dQ pass dQ only (its S/dP recomputation is not counted).
 KERNEL_FLOPS_PER_PAIR_D = {
     "attn_sink_fwd_kernel": 4,
-    "attn_sink_bwd_prep_kernel": 0,
     "attn_sink_bwd_dkdv_kernel": 8,
     "attn_sink_bwd_dq_kernel": 2,
     "attn_sink_bwd_finish_kernel": 0,
@@ -95,9 +94,9 @@ def kernel_bytes(name: str, T: int, hq: int, hkv: int, d: int) -> int:
     dkv32 = 2 * T * hkv * d * 4
     return {
         "attn_sink_fwd_kernel": q + kv + o32 + rows,
-        "attn_sink_bwd_prep_kernel": o32 + q + rows + 2 * rows,
         "attn_sink_bwd_dkdv_kernel": 2 * q + kv + 2 * rows + dkv32,
-        "attn_sink_bwd_dq_kernel": 2 * q + kv + 2 * rows + o32,
+        # q, dO, K, V and O in, LSE in, -LSE/scale and -D out, dQ out
+        "attn_sink_bwd_dq_kernel": 2 * q + kv + 3 * rows + 2 * o32,
         "attn_sink_bwd_finish_kernel": dkv32,
     }[name]
 
