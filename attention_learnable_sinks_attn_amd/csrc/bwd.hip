@@ -13,7 +13,7 @@
 // Passes (all on the caller's stream, no atomics, bitwise reproducible):
 //  1. dq:    row-parallel. A workgroup of four waves owns `hpw` heads of one group and 4 / hpw
 //            blocks of 32 query rows (one head and row block per wave) and streams 64-key tiles
-//            of K and V through a 3-slot LDS ring filled by direct copies two tiles ahead
+//            of K and V in pairs through a 4-slot LDS ring filled by direct copies one pair ahead
 //            (swizzled like the dkdv tiles; K^T operands come from transposing LDS loads of the K
 //            tile). Each wave first forms D_i = dO_i . O_i for its rows from the dO it holds as
 //            an operand and O, and leaves -D_i and -LSE_i / scale in the workspace for pass 2.
@@ -331,7 +331,7 @@ __global__ __launch_bounds__(128 * NS, 2) void attn_sink_bwd_dkdv_kernel(BwdArgs
 constexpr int kDqTileKeys = 64;
 constexpr int kDqTileBytes = kDqTileKeys * kHeadDim * 2;  // one swizzled 64-key tile (K or V)
 constexpr int kDqSlotBytes = 2 * kDqTileBytes;             // K tile, then V tile
-constexpr int kDqRing = 3;                                 // LDS ring slots (two tiles in flight)
+constexpr int kDqRing = 4;                                 // LDS ring slots (two pairs of tiles)
 
 // HPW query heads of one KV group x RPW = 4 / HPW blocks of 32 rows per workgroup (four waves).
 template <int HPW>
@@ -415,8 +415,8 @@ __global__ __launch_bounds__(256, 2) void attn_sink_bwd_dq_kernel(BwdArgs a) {
   const __bf16* kbase = a.k + (size_t)cs * kv_stride + (size_t)g * kHeadDim;
   const __bf16* vbase = a.v + (size_t)cs * kv_stride + (size_t)g * kHeadDim;
 
-  // K and V tiles of 64 keys, swizzled (see tile_swz), in a 3-slot ring filled by direct
-  // global->LDS copies issued two tiles ahead; the waves split each tile's 16 copies (waves 0-1
+  // K and V tiles of 64 keys, swizzled (see tile_swz), in a 4-slot ring filled by direct
+  // global->LDS copies issued one pair of tiles ahead; the waves split each tile's 16 copies (waves 0-1
   // the K tile, 2-3 the V tile). Full tiles go through a buffer resource; in the last, partial
   // tile keys past the sequence end repeat its last key (finite data; they are masked).
   static_assert(8 % CPW == 0, "a wave's copies stay within one tile");
@@ -427,7 +427,7 @@ __global__ __launch_bounds__(256, 2) void attn_sink_bwd_dq_kernel(BwdArgs a) {
     const int u0 = wave * CPW;  // copies u0 .. u0 + CPW - 1 of 16: K for u < 8, V after
     const bool is_v = u0 >= 8;
     const __bf16* src = is_v ? vbase : kbase;
-    unsigned char* tile = ring + (kt % kDqRing) * kDqSlotBytes + (is_v ? kDqTileBytes : 0);
+    unsigned char* tile = ring + ((kt - kt_begin) % kDqRing) * kDqSlotBytes + (is_v ? kDqTileBytes : 0);
     const int row0 = kt * kDqTileKeys;
     if (row0 + kDqTileKeys <= len) {
       const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(src + (size_t)row0 * kv_stride, kDqTileKeys * row_bytes);
@@ -450,15 +450,15 @@ __global__ __launch_bounds__(256, 2) void attn_sink_bwd_dq_kernel(BwdArgs a) {
   if (kt_begin + 1 < kt_end) issue(kt_begin + 1);
 
   for (int kt = kt_begin; kt < kt_end; ++kt) {
-    if (kt + 1 < kt_end) {
-      wait_vmcnt<CPW>();  // this wave's copies of tile kt (those of kt + 1 may stay in flight)
-    } else {
-      wait_vmcnt<0>();
+    const int j = kt - kt_begin;  // tiles go in pairs: one wait and one barrier per pair
+    if ((j & 1) == 0) {
+      wait_vmcnt<0>();  // this wave's copies of tiles kt and kt + 1
+      // Every wave's copies of tiles kt and kt + 1 have landed, and every wave is done with tiles
+      // kt - 2 and kt - 1, whose slots receive tiles kt + 2 and kt + 3.
+      __syncthreads();
+      if (kt + 2 < kt_end) issue(kt + 2);
+      if (kt + 3 < kt_end) issue(kt + 3);
     }
-    // Every wave's copies of tile kt have landed, and every wave is done with tile kt - 1, whose
-    // slot receives tile kt + 2.
-    __syncthreads();
-    if (kt + 2 < kt_end) issue(kt + 2);
     const int k0 = kt * kDqTileKeys;
     // Wave-uniform: skip a tile that holds none of this wave's keys.
     if (RPW > 1 && (k0 >= kw_end || k0 + kDqTileKeys <= kw_begin)) continue;
@@ -536,7 +536,7 @@ __global__ __launch_bounds__(256, 2) void attn_sink_bwd_dq_kernel(BwdArgs a) {
       if (!residual) dsum += part;
       return pmax;
     };
-    const unsigned off = (kt % kDqRing) * kDqSlotBytes;
+    const unsigned off = (j % kDqRing) * kDqSlotBytes;
     if (wave_any(tile(false, off) > kSplitThreshold)) {
       unsigned off2 = off;
       asm volatile("" : "+v"(off2));

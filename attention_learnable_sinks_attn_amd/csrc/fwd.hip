@@ -9,9 +9,9 @@
 //
 // Work split. A workgroup of four waves owns HPW query heads that share one KV head (GQA) and
 // 4 / HPW consecutive blocks of 64 query rows of one sequence; wave w handles head hs*HPW + w%HPW
-// and row block w/HPW. K and V tiles of 64 keys pass through a 3-slot LDS ring shared by the
-// workgroup's waves, filled by direct global->LDS copies two tiles ahead (the waves split the
-// copies); one barrier per tile; a wave skips the tiles its rows cannot see. The tiles are stored with
+// and row block w/HPW. K and V tiles of 64 keys pass in pairs through a 4-slot LDS ring shared by
+// the workgroup's waves, filled by direct global->LDS copies one pair ahead (the waves split the
+// copies); one barrier per pair of tiles; a wave skips the tiles its rows cannot see. The tiles are stored with
 // an XOR swizzle of their 16-byte chunks (tile_swz), so that neither the K fragment reads nor the
 // transposing V^T reads have bank conflicts. Per tile each wave computes
 //   S^T = K Q^T   (32x32x16 MFMA; keys on the C rows, the wave's 64 queries on the columns)
@@ -35,7 +35,7 @@ namespace {
 constexpr int kTileKeys = 64;
 constexpr int kTileBytes = kTileKeys * kHeadDim * 2;  // one swizzled 64-key tile (K or V)
 constexpr int kSlotBytes = 2 * kTileBytes;             // K tile, then V tile
-constexpr int kRing = 3;                               // LDS ring slots (two tiles in flight)
+constexpr int kRing = 4;                               // LDS ring slots (two pairs of tiles)
 
 // HPW query heads of one KV group x RPW = 4 / HPW blocks of 64 rows per workgroup (four waves),
 // so that groups of fewer than four heads still share each K/V tile among four waves.
@@ -113,8 +113,8 @@ __global__ __launch_bounds__(256, 2) void attn_sink_fwd_kernel(FwdArgs a) {
   const __bf16* kbase = a.k + (size_t)cs * kv_stride + (size_t)g * kHeadDim;
   const __bf16* vbase = a.v + (size_t)cs * kv_stride + (size_t)g * kHeadDim;
 
-  // K and V tiles of 64 keys, swizzled (see tile_swz), in a 3-slot ring filled by direct
-  // global->LDS copies issued two tiles ahead; the waves split each tile's 16 copies (waves 0-1
+  // K and V tiles of 64 keys, swizzled (see tile_swz), in a 4-slot ring filled by direct
+  // global->LDS copies issued one pair of tiles ahead; the waves split each tile's 16 copies (waves 0-1
   // the K tile, 2-3 the V tile). Full tiles go through a buffer resource; in the last, partial
   // tile keys past the sequence end repeat its last key (finite data; they are masked). V^T
   // operands come from transposing LDS loads of the V tile.
@@ -126,7 +126,7 @@ __global__ __launch_bounds__(256, 2) void attn_sink_fwd_kernel(FwdArgs a) {
     const int u0 = wave * CPW;  // copies u0 .. u0 + CPW - 1 of 16: K for u < 8, V after
     const bool is_v = u0 >= 8;
     const __bf16* src = is_v ? vbase : kbase;
-    unsigned char* tile = ring + (kt % kRing) * kSlotBytes + (is_v ? kTileBytes : 0);
+    unsigned char* tile = ring + ((kt - kt_begin) % kRing) * kSlotBytes + (is_v ? kTileBytes : 0);
     const int row0 = kt * kTileKeys;
     if (row0 + kTileKeys <= len) {
       const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(src + (size_t)row0 * kv_stride, kTileKeys * row_bytes);
@@ -148,17 +148,17 @@ __global__ __launch_bounds__(256, 2) void attn_sink_fwd_kernel(FwdArgs a) {
   if (kt_begin + 1 < kt_end) issue(kt_begin + 1);
 
   for (int kt = kt_begin; kt < kt_end; ++kt) {
-    if (kt + 1 < kt_end) {
-      wait_vmcnt<CPW>();  // this wave's copies of tile kt (those of kt + 1 may stay in flight)
-    } else {
-      wait_vmcnt<0>();
+    const int j = kt - kt_begin;  // tiles go in pairs: one wait and one barrier per pair
+    if ((j & 1) == 0) {
+      wait_vmcnt<0>();  // this wave's copies of tiles kt and kt + 1
+      // Every wave's copies of tiles kt and kt + 1 have landed, and every wave is done with tiles
+      // kt - 2 and kt - 1, whose slots receive tiles kt + 2 and kt + 3.
+      __syncthreads();
+      if (kt + 2 < kt_end) issue(kt + 2);
+      if (kt + 3 < kt_end) issue(kt + 3);
     }
-    // Every wave's copies of tile kt have landed, and every wave is done with tile kt - 1, whose
-    // slot receives tile kt + 2.
-    __syncthreads();
-    if (kt + 2 < kt_end) issue(kt + 2);
-    const unsigned char* slot = ring + (kt % kRing) * kSlotBytes;
-    const unsigned vt_lds = ring_lds + (kt % kRing) * kSlotBytes + kTileBytes;
+    const unsigned char* slot = ring + (j % kRing) * kSlotBytes;
+    const unsigned vt_lds = ring_lds + (j % kRing) * kSlotBytes + kTileBytes;
     const int k0 = kt * kTileKeys;
     // Wave-uniform: skip a tile that holds none of this wave's keys.
     if (RPW > 1 && (k0 >= kw_end || k0 + kTileKeys <= kw_begin)) continue;
