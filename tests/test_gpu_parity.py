@@ -35,7 +35,11 @@ def run_gpu(inp, scale=None, repeat_bwd=False):
     sinks = inp.sinks.to(dev)
     cu = inp.cu_seqlens.to(dev)
     out, lse = asa.fwd(q, k, v, sinks, cu, inp.max_seqlen, inp.causal, inp.window, scale)
-    dq, dk, dv, ds = asa.bwd(q, k, v, sinks, out, lse, dout, cu, inp.max_seqlen, inp.causal, inp.window, scale)
+    # The workspace starts as all-ones bytes (NaN as fp32): the backward must not read anything it
+    # did not write in the same call.
+    ws = torch.full((max(asa.bwd_workspace_bytes(q, k, cu, inp.max_seqlen), 1),), 255, dtype=torch.uint8, device=dev)
+    dq, dk, dv, ds = asa.bwd(q, k, v, sinks, out, lse, dout, cu, inp.max_seqlen, inp.causal, inp.window, scale,
+                             workspace=ws)
     res = {"out": out, "lse": lse, "dq": dq, "dk": dk, "dv": dv, "dsinks": ds}
     if repeat_bwd:
         res2 = asa.bwd(q, k, v, sinks, out, lse, dout, cu, inp.max_seqlen, inp.causal, inp.window, scale)
@@ -81,6 +85,7 @@ SMALL_CASES = {
     # name: (lengths, hq, hkv, causal, window, extra)
     "mha_causal_ragged": ((300,), 2, 2, True, 0, {}),
     "gqa8_varlen_causal": ((130, 0, 1, 257, 64, 200), 16, 2, True, 0, {}),
+    "varlen_empty_ends": ((0, 0, 70, 0, 33, 0), 4, 2, True, 0, {}),  # empty first, middle and last sequences
     "gqa2_window37": ((300, 77), 4, 2, True, 37, {}),
     "gqa8_window128": ((513, 129), 8, 1, True, 128, {}),
     "gqa4_noncausal": ((190, 65, 1), 8, 2, False, 0, {}),
