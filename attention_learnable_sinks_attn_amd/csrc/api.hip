@@ -36,6 +36,10 @@ int check_shape(const attn_sink_shape* s, bool bf16_out = false) {
   return ATTN_SINK_OK;
 }
 
+// A window of at least the longest sequence sees every key, exactly as one of that length does;
+// clamping keeps the kernels' index arithmetic (row + window) far from overflow.
+int clamp_window(int window, int longest) { return window > 0 ? std::min(window, std::max(longest, 1)) : 0; }
+
 int heads_per_group_split(int G) { return G % 4 == 0 ? 4 : (G % 2 == 0 ? 2 : 1); }
 
 float resolve_scale(const attn_sink_shape* s) {
@@ -127,7 +131,7 @@ int bwd_impl(const void* q, const void* k, const void* v, const float* sinks, co
   a.n_qblocks = (shape->max_seqlen + dq_rows - 1) / dq_rows;
   a.n_kblocks = (shape->max_seqlen + kKvKeysPerBlock - 1) / kKvKeysPerBlock;
   a.causal = causal ? 1 : 0;
-  a.window = window > 0 ? window : 0;
+  a.window = clamp_window(window, shape->max_seqlen);
   a.scale = resolve_scale(shape);
   a.scale_log2 = a.scale * kLog2e;
 
@@ -239,7 +243,7 @@ int attn_sink_fwd(const void* q, const void* k, const void* v, const float* sink
   const int fwd_rows = kFwdRowsPerWave * (4 / a.hpw);  // rows per forward workgroup
   a.n_qblocks = (shape->max_seqlen + fwd_rows - 1) / fwd_rows;
   a.causal = causal ? 1 : 0;
-  a.window = window > 0 ? window : 0;
+  a.window = clamp_window(window, shape->max_seqlen);
   a.scale_log2 = resolve_scale(shape) * kLog2e;
   return launch_fwd(a, stream) == hipSuccess ? ATTN_SINK_OK : ATTN_SINK_ERR_HIP;
 }
@@ -310,7 +314,7 @@ int attn_sink_decode_fwd_timed(const void* q, const void* k, const void* v, cons
   a.Hkv = shape->num_heads_kv;
   a.G = a.Hq / a.Hkv;
   a.n_cols = shape->max_q * a.G;
-  a.window = window;
+  a.window = clamp_window(window, shape->max_k);
   a.out_bf16 = shape->out_dtype == ATTN_SINK_BF16 ? 1 : 0;
   const float scale = shape->softmax_scale > 0.0f ? shape->softmax_scale : 1.0f / sqrtf((float)shape->head_dim);
   a.scale_log2 = scale * kLog2e;

@@ -121,15 +121,15 @@ __global__ __launch_bounds__(128 * NS, 2) void attn_sink_bwd_dkdv_kernel(BwdArgs
   const unsigned qrow_bytes = 2u * qstride;
   unsigned coff[2];
   tile_copy_offsets(lane, qrow_bytes, coff);
-  auto issue = [&](int j, int t, int slot) {
-    // (The step counters are wave-uniform; reading them from lane 0 keeps the addresses scalar.)
-    const int h = __builtin_amdgcn_readfirstlane(h0 + NS * j);
-    const int i0 = __builtin_amdgcn_readfirstlane(i_begin + kKvRows * (n_sub - 1 - t));
+  // Step (head j, tile t) starts at row i0 = i_begin + 64 (n_sub - 1 - t) of head h0 + NS j; its
+  // Q / dO rows start at element qoff = ((cs + i0) Hq + h) 64 and its -LSE/scale, -D rows at
+  // roff = h T + cs + i0. The loop below steps these offsets instead of recomputing them.
+  auto issue = [&](int i0, size_t qoff, size_t roff, int slot) {
     unsigned char* dst = ring + slot * kKvSlotBytes + kh * kKvTileBytes;
-    const __bf16* src = (kh ? a.dout : a.q) + ((size_t)(cs + i0) * a.Hq + h) * kHeadDim;
+    const __bf16* src = (kh ? a.dout : a.q) + qoff;
     unsigned char* rows = ring + slot * kKvSlotBytes + 2 * kKvTileBytes;
-    const float* nl = a.nlse + (size_t)h * a.T + cs + i0;
-    const float* nd = a.negd + (size_t)h * a.T + cs + i0;
+    const float* nl = a.nlse + roff;
+    const float* nd = a.negd + roff;
     if (i0 + kKvRows <= len) {
       const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(src, kKvRows * qrow_bytes);
 #pragma unroll
@@ -242,38 +242,61 @@ __global__ __launch_bounds__(128 * NS, 2) void attn_sink_bwd_dkdv_kernel(BwdArgs
     } while (again);
   };
 
-  int ij = 0, it = 0;  // (head, tile) of the next step to issue
-  auto advance = [&](int& j, int& t) {
-    if (++t == n_sub) {
-      t = 0;
-      ++j;
+  // The next step to issue (wave-uniform): tile index, first row and offsets.
+  int nx_t = 0;
+  int nx_i0 = i_begin + kKvRows * (n_sub - 1);
+  size_t nx_qoff = ((size_t)(cs + nx_i0) * a.Hq + h0) * kHeadDim;
+  size_t nx_roff = (size_t)h0 * a.T + cs + nx_i0;
+  const size_t tile_q = (size_t)kKvRows * qstride;                            // one tile back
+  const size_t head_q = (size_t)NS * kHeadDim + (size_t)(n_sub - 1) * tile_q;  // next head's last tile
+  const size_t head_r = (size_t)NS * a.T + (size_t)(n_sub - 1) * kKvRows;
+  auto issue_next = [&](int slot) {
+    issue(nx_i0, nx_qoff, nx_roff, slot);
+    if (++nx_t == n_sub) {
+      nx_t = 0;
+      nx_i0 += kKvRows * (n_sub - 1);
+      nx_qoff += head_q;
+      nx_roff += head_r;
+    } else {
+      nx_i0 -= kKvRows;
+      nx_qoff -= tile_q;
+      nx_roff -= kKvRows;
     }
   };
-  issue(ij, it, 0);
-  advance(ij, it);
-  int ct = 0;  // tile index of the current step
+
+  // Which 32-row blocks (first row i0) a wave computes, and which of them need the mask, as
+  // ranges of i0 fixed per wave: live iff live_lo <= i0 <= live_hi (causal: the block reaches the
+  // wave's first key; window: it starts before the last key's window ends; band: it ends after the
+  // first key's window starts; inside the sequence, and no block when the keys are past its end).
+  // The mask is needed iff i0 < mask_lo (diagonal, band's left edge) or i0 > mask_hi (sequence
+  // end, window's right edge), or always when some key is past the end.
+  constexpr int kBig = 1 << 29;
+  const int W = a.window;
+  int live_lo = a.causal ? k0 - (kKvSub - 1) : (W > 0 ? k0 - (kKvSub - 2) - W : -kBig);
+  const int live_hi = min(len - 1, W > 0 ? k0 + 30 + W : kBig);
+  if (k0 >= len) live_lo = kBig;
+  const int mask_lo = k0 + 32 > len ? kBig : (a.causal ? k0 + 31 : (W > 0 ? k0 + 32 - W : -kBig));
+  const int mask_hi = min(len - kKvSub - 1, W > 0 ? k0 + W - 32 : kBig);
+
+  int cur_i0 = nx_i0;  // first row of the current step
+  issue_next(0);
   for (int s = 0; s < n_steps; ++s) {
     wait_own_step();
     // Both halves of step s have landed, and every wave is done with step s - 1, whose slot
     // receives step s + 1.
     __syncthreads();
+    const int step_i0 = cur_i0;
     if (s + 1 < n_steps) {
-      issue(ij, it, (s + 1) % kKvRing);
-      advance(ij, it);
+      cur_i0 = nx_i0;
+      issue_next((s + 1) % kKvRing);
     }
 #pragma unroll
     for (int sub = 0; sub < kKvRows / kKvSub; ++sub) {
-      const int i0 = i_begin + kKvRows * (n_sub - 1 - ct) + kKvSub * sub;
-      const bool live = (!a.causal || k0 <= i0 + kKvSub - 1) && (a.window <= 0 || i0 <= k0 + 31 + a.window - 1) &&
-                        (a.causal || a.window <= 0 || k0 <= i0 + kKvSub - 1 + a.window - 1) && k0 < len && i0 < len;
-      if (live) {  // wave-uniform: skip blocks in which none of this wave's pairs is visible
-        const bool need_mask = (i0 + kKvSub > len) || (k0 + 32 > len) || (a.causal && k0 + 31 > i0) ||
-                               (a.window > 0 && k0 <= i0 + kKvSub - 1 - a.window) ||
-                               (!a.causal && a.window > 0 && k0 + 31 >= i0 + a.window);
-        step(s % kKvRing, sub, i0, need_mask);
+      const int i0 = step_i0 + kKvSub * sub;
+      if (i0 >= live_lo && i0 <= live_hi) {  // wave-uniform: skip blocks without visible pairs
+        step(s % kKvRing, sub, i0, i0 < mask_lo || i0 > mask_hi);
       }
     }
-    if (++ct == n_sub) ct = 0;
   }
 
   // Add the second stream's partial sums (LDS, [key][d] fp32 per key half), then store rows.

@@ -70,6 +70,7 @@ SMALL = {
     "big_sinks": ((257, 31), 1, 16, 2, 0, {"sink_scale": 3.0}),
     "scale_0p3": ((190,), 4, 8, 1, 0, {"scale": 0.3}),
     "window_ge_len": ((70, 20), 3, 8, 2, 500, {}),
+    "window_int_max": ((70, 20), 3, 8, 2, 2**31 - 1, {}),
 }
 
 

@@ -91,6 +91,7 @@ SMALL_CASES = {
     "gqa4_noncausal": ((190, 65, 1), 8, 2, False, 0, {}),
     "mha_single_tokens": ((1, 1, 3, 1), 2, 2, True, 0, {}),
     "window_ge_len": ((150, 40), 4, 1, True, 1000, {}),
+    "window_int_max": ((150, 40), 4, 1, True, 2**31 - 1, {}),  # no overflow in row + window
     "window1": ((97,), 2, 1, True, 1, {}),
     "sink_neg_inf_window": ((200, 63), 4, 2, True, 20, {"sinks": [-math.inf] * 4}),
     "sink_neg_inf_causal": ((130,), 2, 1, True, 0, {"sinks": [-math.inf, 0.5]}),
@@ -105,6 +106,7 @@ SMALL_CASES = {
     "band_gqa8_w128": ((513, 129), 8, 1, False, 128, {}),
     "band_w1": ((97, 33), 2, 1, False, 1, {}),
     "band_w_ge_len": ((150, 40), 4, 1, False, 1000, {}),
+    "band_int_max": ((97, 33), 2, 1, False, 2**31 - 1, {}),
     "band_neg_inf_sinks": ((200, 63), 4, 2, False, 20, {"sinks": [-math.inf] * 4}),
     "band_exact_tiles": ((256, 128), 8, 8, False, 64, {}),
 }
