@@ -446,20 +446,25 @@ __global__ __launch_bounds__(256, 2) void attn_sink_bwd_dq_kernel(BwdArgs a) {
   const unsigned row_bytes = 2u * kv_stride;
   unsigned coff[2];
   tile_copy_offsets(lane, row_bytes, coff);
-  auto issue = [&](int kt) {
-    const int u0 = wave * CPW;  // copies u0 .. u0 + CPW - 1 of 16: K for u < 8, V after
-    const bool is_v = u0 >= 8;
-    const __bf16* src = is_v ? vbase : kbase;
-    unsigned char* tile = ring + ((kt - kt_begin) % kDqRing) * kDqSlotBytes + (is_v ? kDqTileBytes : 0);
-    const int row0 = kt * kDqTileKeys;
+  // Tiles are issued in order, so the next one's source advances by a tile per issue.
+  const int u0 = wave * CPW;  // copies u0 .. u0 + CPW - 1 of 16: K for u < 8, V after
+  const bool is_v = u0 >= 8;
+  const size_t tile_elems = (size_t)kDqTileKeys * kv_stride;
+  const __bf16* nx_src = (is_v ? vbase : kbase) + (size_t)kt_begin * tile_elems;
+  int nx_kt = kt_begin;
+  auto issue_next = [&]() {
+    unsigned char* tile = ring + ((unsigned)(nx_kt - kt_begin) % kDqRing) * kDqSlotBytes + (is_v ? kDqTileBytes : 0);
+    const int row0 = nx_kt * kDqTileKeys;
     if (row0 + kDqTileKeys <= len) {
-      const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(src + (size_t)row0 * kv_stride, kDqTileKeys * row_bytes);
+      const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(nx_src, kDqTileKeys * row_bytes);
 #pragma unroll
       for (int i = 0; i < CPW; ++i) tile_copy_full(rs, coff, row_bytes, tile, (u0 + i) & 7);
     } else {
 #pragma unroll
-      for (int i = 0; i < CPW; ++i) tile_copy(src, row0, len - 1, kv_stride, tile, (u0 + i) & 7, lane);
+      for (int i = 0; i < CPW; ++i) tile_copy(nx_src, 0, len - 1 - row0, kv_stride, tile, (u0 + i) & 7, lane);
     }
+    nx_src += tile_elems;
+    ++nx_kt;
   };
 
   int aoff[4];
@@ -469,26 +474,32 @@ __global__ __launch_bounds__(256, 2) void attn_sink_bwd_dq_kernel(BwdArgs a) {
   tile_tr_offsets(lane, toff);
   const unsigned ring_lds = lds_addr(ring);
 
-  issue(kt_begin);
-  if (kt_begin + 1 < kt_end) issue(kt_begin + 1);
+  // Tiles (first key k0) that need the mask, as ranges fixed per wave: k0 > mask_hi when the
+  // sequence end, the diagonal or a band's right edge reaches into the tile, k0 < mask_lo when a
+  // window's left edge does.
+  constexpr int kBig = 1 << 29;
+  const int mask_hi = min(len - kDqTileKeys - 1,
+                          a.causal ? q0 - kDqTileKeys : (a.window > 0 ? q0 + a.window - kDqTileKeys : kBig));
+  const int mask_lo = a.window > 0 ? q0 + kRows - a.window : -kBig;
+
+  issue_next();
+  if (kt_begin + 1 < kt_end) issue_next();
 
   for (int kt = kt_begin; kt < kt_end; ++kt) {
-    const int j = kt - kt_begin;  // tiles go in pairs: one wait and one barrier per pair
+    const unsigned j = kt - kt_begin;  // tiles go in pairs: one wait and one barrier per pair
     if ((j & 1) == 0) {
       wait_vmcnt<0>();  // this wave's copies of tiles kt and kt + 1
       // Every wave's copies of tiles kt and kt + 1 have landed, and every wave is done with tiles
       // kt - 2 and kt - 1, whose slots receive tiles kt + 2 and kt + 3.
       __syncthreads();
-      if (kt + 2 < kt_end) issue(kt + 2);
-      if (kt + 3 < kt_end) issue(kt + 3);
+      if (kt + 2 < kt_end) issue_next();
+      if (kt + 3 < kt_end) issue_next();
     }
     const int k0 = kt * kDqTileKeys;
     // Wave-uniform: skip a tile that holds none of this wave's keys.
     if (RPW > 1 && (k0 >= kw_end || k0 + kDqTileKeys <= kw_begin)) continue;
 
-    const bool need_mask = (k0 + kDqTileKeys > len) || (a.causal && k0 + kDqTileKeys - 1 > q0) ||
-                           (a.window > 0 && k0 <= q0 + kRows - 1 - a.window) ||
-                           (!a.causal && a.window > 0 && k0 + kDqTileKeys - 1 >= q0 + a.window);
+    const bool need_mask = k0 > mask_hi || k0 < mask_lo;
     // One tile: S^T = K Q^T and dP^T = V dO^T (rows = keys, loaded with the swap23 permutation),
     // P = exp2(S*scale*log2e - LSE*log2e), dS = P (dP - D), dQ^T += K^T dS^T, one 32-key block
     // after the other so that block 1's softmax overlaps block 0's dQ products. Returns the
