@@ -158,21 +158,29 @@ __global__ __launch_bounds__(128 * NS, 2) void attn_sink_bwd_dkdv_kernel(BwdArgs
   tile_tr_offsets(lane, toff);
   // Transposed operands (see load_tr8): Q^T (tile 0) or dO^T (tile 1) rows d = 32db + l32, k
   // slots = query rows 16*half + 8grp + 0..7 of the slot at LDS address `slot_lds`.
-  auto tr8 = [&](unsigned slot_lds, auto tile_tag, int db, auto half_tag, u32x2& lo, u32x2& hi) {
-    constexpr int OFF = decltype(tile_tag)::value * kKvTileBytes + 2048 * decltype(half_tag)::value;
-    lo = ds_read_tr16_b64_asm<OFF>(slot_lds + toff[db][0]);
-    hi = ds_read_tr16_b64_asm<OFF>(slot_lds + toff[db][1]);
+  // The slot and the 32-row block are compile-time constants below (the step loop is unrolled
+  // over the two ring slots), so their LDS offset goes into the reads' offset fields.
+  unsigned trb[2][2];  // LDS addresses of the transposing reads at offset 0 of the ring
+#pragma unroll
+  for (int db = 0; db < 2; ++db) {
+    trb[db][0] = lds_addr(ring) + toff[db][0];
+    trb[db][1] = lds_addr(ring) + toff[db][1];
+  }
+  auto tr8 = [&](auto base_tag, auto tile_tag, int db, auto half_tag, u32x2& lo, u32x2& hi) {
+    constexpr int OFF =
+        decltype(base_tag)::value + decltype(tile_tag)::value * kKvTileBytes + 2048 * decltype(half_tag)::value;
+    lo = ds_read_tr16_b64_asm<OFF>(trb[db][0]);
+    hi = ds_read_tr16_b64_asm<OFF>(trb[db][1]);
   };
-  auto tr_all = [&](unsigned slot_lds, u32x2 (&tr)[16]) {  // [d block][query half][Q / dO][lo / hi]
+  auto tr_all = [&](auto base_tag, u32x2 (&tr)[16]) {  // [d block][query half][Q / dO][lo / hi]
 #pragma unroll
     for (int db = 0; db < 2; ++db) {
-      tr8(slot_lds, std::integral_constant<int, 0>(), db, std::integral_constant<int, 0>(), tr[8 * db], tr[8 * db + 1]);
-      tr8(slot_lds, std::integral_constant<int, 1>(), db, std::integral_constant<int, 0>(), tr[8 * db + 2], tr[8 * db + 3]);
-      tr8(slot_lds, std::integral_constant<int, 0>(), db, std::integral_constant<int, 1>(), tr[8 * db + 4], tr[8 * db + 5]);
-      tr8(slot_lds, std::integral_constant<int, 1>(), db, std::integral_constant<int, 1>(), tr[8 * db + 6], tr[8 * db + 7]);
+      tr8(base_tag, std::integral_constant<int, 0>(), db, std::integral_constant<int, 0>(), tr[8 * db], tr[8 * db + 1]);
+      tr8(base_tag, std::integral_constant<int, 1>(), db, std::integral_constant<int, 0>(), tr[8 * db + 2], tr[8 * db + 3]);
+      tr8(base_tag, std::integral_constant<int, 0>(), db, std::integral_constant<int, 1>(), tr[8 * db + 4], tr[8 * db + 5]);
+      tr8(base_tag, std::integral_constant<int, 1>(), db, std::integral_constant<int, 1>(), tr[8 * db + 6], tr[8 * db + 7]);
     }
   };
-  const unsigned ring_lds = lds_addr(ring);
 
   // One step: S' = Q K^T - LSE/scale and dP' = dO V^T - D for the 32 rows x 32 keys (the row
   // values preloaded as the accumulators; C: lane = key, registers = rows 16(i/8) + 8grp + i%8),
@@ -180,10 +188,11 @@ __global__ __launch_bounds__(128 * NS, 2) void attn_sink_bwd_dkdv_kernel(BwdArgs
   // probability of the step exceeds kSplitThreshold, the step runs a second time in residual
   // mode, multiplying the bf16 rounding residuals of P and dS instead (same instructions, so the
   // accumulators are not split over two code paths).
-  auto step = [&](int si, int sub, int i0, bool need_mask) {
-    const unsigned char* slot = ring + si * kKvSlotBytes + 4096 * sub;  // 32-row block `sub` of the tiles
-    const unsigned slot_lds = ring_lds + si * kKvSlotBytes + 4096 * sub;
-    const float* lp = reinterpret_cast<const float*>(ring + si * kKvSlotBytes + 2 * kKvTileBytes) + kKvSub * sub;
+  auto step = [&](auto si_tag, auto sub_tag, int i0, bool need_mask) {
+    constexpr int SI = decltype(si_tag)::value, SUB = decltype(sub_tag)::value;
+    constexpr int SO = SI * kKvSlotBytes + 4096 * SUB;  // 32-row block SUB of slot SI's tiles
+    const unsigned char* slot = ring + SO;
+    const float* lp = reinterpret_cast<const float*>(ring + SI * kKvSlotBytes + 2 * kKvTileBytes) + kKvSub * SUB;
     bool residual = false;
     bool again;
     do {
@@ -195,7 +204,7 @@ __global__ __launch_bounds__(128 * NS, 2) void attn_sink_bwd_dkdv_kernel(BwdArgs
         dp = mfma_32x32x16(*reinterpret_cast<const bf16x8*>(slot + kKvTileBytes + aoff[c]), vf[c], dp);
       }
       u32x2 tr[16];
-      tr_all(slot_lds, tr);
+      tr_all(std::integral_constant<int, SO>(), tr);
       if (need_mask) {
         // Row of register i: i0 + 8grp + r_i with r_i = 16(i/8) + i%8. Key kj is seen by the
         // rows lo .. hi: from the key itself (causal) or W - 1 rows before it (a non-causal
@@ -280,23 +289,30 @@ __global__ __launch_bounds__(128 * NS, 2) void attn_sink_bwd_dkdv_kernel(BwdArgs
 
   int cur_i0 = nx_i0;  // first row of the current step
   issue_next(0);
-  for (int s = 0; s < n_steps; ++s) {
+  static_assert(kKvRing == 2 && kKvRows == 2 * kKvSub, "two slots, two 32-row blocks per step");
+  auto do_step = [&](int s, auto si_tag) {  // step s, held in slot SI = s % 2
+    constexpr int SI = decltype(si_tag)::value;
     wait_own_step();
     // Both halves of step s have landed, and every wave is done with step s - 1, whose slot
     // receives step s + 1.
     __syncthreads();
-    const int step_i0 = cur_i0;
+    const int i0 = cur_i0;
     if (s + 1 < n_steps) {
       cur_i0 = nx_i0;
-      issue_next((s + 1) % kKvRing);
+      issue_next(1 - SI);
     }
-#pragma unroll
-    for (int sub = 0; sub < kKvRows / kKvSub; ++sub) {
-      const int i0 = step_i0 + kKvSub * sub;
-      if (i0 >= live_lo && i0 <= live_hi) {  // wave-uniform: skip blocks without visible pairs
-        step(s % kKvRing, sub, i0, i0 < mask_lo || i0 > mask_hi);
-      }
+    // Wave-uniform: skip blocks without visible pairs.
+    if (i0 >= live_lo && i0 <= live_hi) {
+      step(si_tag, std::integral_constant<int, 0>(), i0, i0 < mask_lo || i0 > mask_hi);
     }
+    const int i1 = i0 + kKvSub;
+    if (i1 >= live_lo && i1 <= live_hi) {
+      step(si_tag, std::integral_constant<int, 1>(), i1, i1 < mask_lo || i1 > mask_hi);
+    }
+  };
+  for (int s = 0; s < n_steps; s += 2) {
+    do_step(s, std::integral_constant<int, 0>());
+    if (s + 1 < n_steps) do_step(s + 1, std::integral_constant<int, 1>());
   }
 
   // Add the second stream's partial sums (LDS, [key][d] fp32 per key half), then store rows.
