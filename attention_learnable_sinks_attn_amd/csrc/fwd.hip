@@ -160,21 +160,21 @@ __global__ __launch_bounds__(256, 2) void attn_sink_fwd_kernel(FwdArgs a) {
   issue_next();
   if (kt_begin + 1 < kt_end) issue_next();
 
-  for (int kt = kt_begin; kt < kt_end; ++kt) {
-    const unsigned j = kt - kt_begin;  // tiles go in pairs: one wait and one barrier per pair
-    if ((j & 1) == 0) {
-      wait_vmcnt<0>();  // this wave's copies of tiles kt and kt + 1
-      // Every wave's copies of tiles kt and kt + 1 have landed, and every wave is done with tiles
-      // kt - 2 and kt - 1, whose slots receive tiles kt + 2 and kt + 3.
-      __syncthreads();
-      if (kt + 2 < kt_end) issue_next();
-      if (kt + 3 < kt_end) issue_next();
-    }
-    const unsigned char* slot = ring + (j % kRing) * kSlotBytes;
-    const unsigned vt_lds = ring_lds + (j % kRing) * kSlotBytes + kTileBytes;
+  // The work on tile kt, held in the ring slot at byte offset pair_off + K (K a compile-time
+  // constant: 0 for the first tile of a pair, one slot for the second).
+  unsigned trb[2][2];  // LDS addresses of the transposing reads at offset 0 of the ring
+#pragma unroll
+  for (int db = 0; db < 2; ++db) {
+    trb[db][0] = ring_lds + toff[db][0];
+    trb[db][1] = ring_lds + toff[db][1];
+  }
+  auto tile = [&](int kt, unsigned pair_off, auto k_tag) {
+    constexpr int K = decltype(k_tag)::value;
+    constexpr int VT = K + kTileBytes;  // the V tile, from the pair's base
+    const unsigned char* slot = ring + pair_off + K;
     const int k0 = kt * kTileKeys;
     // Wave-uniform: skip a tile that holds none of this wave's keys.
-    if (RPW > 1 && (k0 >= kw_end || k0 + kTileKeys <= kw_begin)) continue;
+    if (RPW > 1 && (k0 >= kw_end || k0 + kTileKeys <= kw_begin)) return;
 
     // S^T = K Q^T for two 32-key row blocks.
     f32x16 s[2][NB];
@@ -235,14 +235,15 @@ __global__ __launch_bounds__(256, 2) void attn_sink_fwd_kernel(FwdArgs a) {
     u32x2 tr[16];  // [d block][key block][half][lo / hi]
 #pragma unroll
     for (int db = 0; db < 2; ++db) {
-      tr[8 * db + 0] = ds_read_tr16_b64_asm<0>(vt_lds + toff[db][0]);
-      tr[8 * db + 1] = ds_read_tr16_b64_asm<0>(vt_lds + toff[db][1]);
-      tr[8 * db + 2] = ds_read_tr16_b64_asm<2048>(vt_lds + toff[db][0]);
-      tr[8 * db + 3] = ds_read_tr16_b64_asm<2048>(vt_lds + toff[db][1]);
-      tr[8 * db + 4] = ds_read_tr16_b64_asm<4096>(vt_lds + toff[db][0]);
-      tr[8 * db + 5] = ds_read_tr16_b64_asm<4096>(vt_lds + toff[db][1]);
-      tr[8 * db + 6] = ds_read_tr16_b64_asm<6144>(vt_lds + toff[db][0]);
-      tr[8 * db + 7] = ds_read_tr16_b64_asm<6144>(vt_lds + toff[db][1]);
+      const unsigned t0 = trb[db][0] + pair_off, t1 = trb[db][1] + pair_off;
+      tr[8 * db + 0] = ds_read_tr16_b64_asm<VT + 0>(t0);
+      tr[8 * db + 1] = ds_read_tr16_b64_asm<VT + 0>(t1);
+      tr[8 * db + 2] = ds_read_tr16_b64_asm<VT + 2048>(t0);
+      tr[8 * db + 3] = ds_read_tr16_b64_asm<VT + 2048>(t1);
+      tr[8 * db + 4] = ds_read_tr16_b64_asm<VT + 4096>(t0);
+      tr[8 * db + 5] = ds_read_tr16_b64_asm<VT + 4096>(t1);
+      tr[8 * db + 6] = ds_read_tr16_b64_asm<VT + 6144>(t0);
+      tr[8 * db + 7] = ds_read_tr16_b64_asm<VT + 6144>(t1);
     }
 
 #pragma unroll
@@ -276,6 +277,21 @@ __global__ __launch_bounds__(256, 2) void attn_sink_fwd_kernel(FwdArgs a) {
         }
       }
     }
+  };
+
+  // Tiles go in pairs, one wait and one barrier per pair; a pair sits in slots 0-1 or 2-3, so the
+  // second tile's LDS addresses are the first's plus a constant.
+  static_assert(kRing == 4, "two pairs of slots");
+  for (int kt = kt_begin; kt < kt_end; kt += 2) {
+    wait_vmcnt<0>();  // this wave's copies of tiles kt and kt + 1
+    // Every wave's copies of tiles kt and kt + 1 have landed, and every wave is done with tiles
+    // kt - 2 and kt - 1, whose slots receive tiles kt + 2 and kt + 3.
+    __syncthreads();
+    if (kt + 2 < kt_end) issue_next();
+    if (kt + 3 < kt_end) issue_next();
+    const unsigned pair_off = ((unsigned)(kt - kt_begin) & 2) * kSlotBytes;
+    tile(kt, pair_off, std::integral_constant<int, 0>());
+    if (kt + 1 < kt_end) tile(kt + 1, pair_off, std::integral_constant<int, kSlotBytes>());
   }
 
   // Epilogue: combine the two lane halves' partial denominators, normalise, store.
