@@ -63,14 +63,14 @@ KERNEL_FLOPS_PER_PAIR_D = {
 # (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch) scaled by what the same counters read for the
 # copy probe; valid only for kernel sources with the recorded digest.
 TRAFFIC = {
-    ("causal4k", "attn_sink_bwd_dkdv_kernel"): {"bytes": 147018904, "digest": "61f4b42c5c6ddfde"},
-    ("window4k", "attn_sink_bwd_dkdv_kernel"): {"bytes": 106892526, "digest": "61f4b42c5c6ddfde"},
-    ("window4k", "attn_sink_bwd_dq_kernel"): {"bytes": 213251398, "digest": "61f4b42c5c6ddfde"},
-    ("varlen_window", "attn_sink_bwd_dkdv_kernel"): {"bytes": 1720481555, "digest": "61f4b42c5c6ddfde"},
-    ("varlen_window", "attn_sink_bwd_dq_kernel"): {"bytes": 3791389718, "digest": "61f4b42c5c6ddfde"},
-    ("band4k", "attn_sink_bwd_dkdv_kernel"): {"bytes": 126291622, "digest": "61f4b42c5c6ddfde"},
-    ("band4k", "attn_sink_bwd_dq_kernel"): {"bytes": 213290267, "digest": "61f4b42c5c6ddfde"},
-    ("decode32k", "attn_sink_decode_partial_kernel"): {"bytes": 368468421, "digest": "61f4b42c5c6ddfde"},
+    ("causal4k", "attn_sink_bwd_dkdv_kernel"): {"bytes": 146943601, "digest": "15d39eeefe02f120"},
+    ("window4k", "attn_sink_bwd_dkdv_kernel"): {"bytes": 106543324, "digest": "15d39eeefe02f120"},
+    ("window4k", "attn_sink_bwd_dq_kernel"): {"bytes": 213277868, "digest": "15d39eeefe02f120"},
+    ("varlen_window", "attn_sink_bwd_dkdv_kernel"): {"bytes": 1719518766, "digest": "15d39eeefe02f120"},
+    ("varlen_window", "attn_sink_bwd_dq_kernel"): {"bytes": 3790396208, "digest": "15d39eeefe02f120"},
+    ("band4k", "attn_sink_bwd_dkdv_kernel"): {"bytes": 126232173, "digest": "15d39eeefe02f120"},
+    ("band4k", "attn_sink_bwd_dq_kernel"): {"bytes": 213276541, "digest": "15d39eeefe02f120"},
+    ("decode32k", "attn_sink_decode_partial_kernel"): {"bytes": 368465420, "digest": "15d39eeefe02f120"},
 }
 
 
