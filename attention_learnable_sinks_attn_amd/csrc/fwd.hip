@@ -26,6 +26,8 @@
 // The running max is exact (so each row's largest probability is exactly 1.0, which bf16 holds
 // without rounding); the sum and the accumulator are only rescaled when some row of the wave
 // sees a larger max in the tile.
+#include <type_traits>
+
 #include "kernels.h"
 
 namespace attn_sink {
@@ -36,6 +38,10 @@ constexpr int kTileKeys = 64;
 constexpr int kTileBytes = kTileKeys * kHeadDim * 2;  // one swizzled 64-key tile (K or V)
 constexpr int kSlotBytes = 2 * kTileBytes;             // K tile, then V tile
 constexpr int kRing = 4;                               // LDS ring slots (two pairs of tiles)
+// Probabilities above this share of their row get the residual P.V product (see the tile body).
+// The largest ones dominate the rounding error of O: on peaked rows a quarter already removes
+// most of it, and the rows that reach it are few, so the extra products stay rare.
+constexpr float kFwdSplitThreshold = 0.25f;
 
 // HPW query heads of one KV group x RPW = 4 / HPW blocks of 64 rows per workgroup (four waves),
 // so that groups of fewer than four heads still share each K/V tile among four waves.
@@ -249,6 +255,19 @@ __global__ __launch_bounds__(256, 2) void attn_sink_fwd_kernel(FwdArgs a) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       const float moff = m[nb] == kNegInf ? 0.0f : m[nb];  // nothing visible yet: exp2(-inf) = 0
+      // A row's final probabilities are its values in this tile divided by at least its
+      // denominator so far (later tiles only add to it), and those values are at most
+      // 2^(tile max - running max). So when no row's largest value here reaches
+      // kFwdSplitThreshold of its denominator before this tile, no probability of the tile will
+      // exceed that share. Otherwise the tile also multiplies the bf16 rounding residuals of P:
+      // O then carries about 16 significant bits of its largest probabilities, which matters
+      // twice downstream, in O itself and in D = dO . O of the backward, where an error in D
+      // scales every dS of the row (dQ of peaked rows crossed 1e-2 through it without this
+      // product). The test needs only values known before the softmax, which keeps it off the
+      // common path's critical chain; on N(0,1) inputs it is mostly a row block's first tile
+      // that takes the extra products, and rows that a large sink dominates never do.
+      const float pm = fast_exp2(tmax[nb] - moff);  // 0 for a fully masked row
+      const bool split = wave_any(pm > kFwdSplitThreshold * sum_xor32(lsum[nb]));
       float rs = 0.0f;
       bf16x8 pb[2][2];
 #pragma unroll
@@ -273,6 +292,20 @@ __global__ __launch_bounds__(256, 2) void attn_sink_fwd_kernel(FwdArgs a) {
           for (int cc = 0; cc < 2; ++cc) {
             const u32x2* t = tr + 8 * db + 4 * mb + 2 * cc;
             o[db][nb] = mfma_32x32x16(join_tr(t[0], t[1]), pb[mb][cc], o[db][nb]);
+          }
+        }
+      }
+      if (split) {
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+          for (int cc = 0; cc < 2; ++cc) {
+            const bf16x8 pl = residual8(s[mb][nb], cc, pb[mb][cc]);
+#pragma unroll
+            for (int db = 0; db < 2; ++db) {
+              const u32x2* t = tr + 8 * db + 4 * mb + 2 * cc;
+              o[db][nb] = mfma_32x32x16(join_tr(t[0], t[1]), pl, o[db][nb]);
+            }
           }
         }
       }
