@@ -23,9 +23,11 @@
 // The two 32-query column blocks are processed one after the other, so the second block's
 // softmax (VALU) can overlap the first block's P.V products (MFMA).
 //
-// The running max is exact (so each row's largest probability is exactly 1.0, which bf16 holds
-// without rounding); the sum and the accumulator are only rescaled when some row of the wave
-// sees a larger max in the tile.
+// The reference max is lazy: the sum and the accumulator are only rescaled when some row of a
+// 32-query block sees a score more than 2^8 above its reference, so the unnormalised values
+// exp2(s - m) stay below 256 and most tiles skip the rescale. Their bf16 rounding is then not
+// exact for a row's largest value, and tiles where a value can reach a quarter of its row's
+// probability mass also multiply the rounding residuals (see the tile body).
 #include <type_traits>
 
 #include "kernels.h"
@@ -42,6 +44,8 @@ constexpr int kRing = 4;                               // LDS ring slots (two pa
 // The largest ones dominate the rounding error of O: on peaked rows a quarter already removes
 // most of it, and the rows that reach it are few, so the extra products stay rare.
 constexpr float kFwdSplitThreshold = 0.25f;
+// Growth of a row's maximum (log2 units) that forces a rescale of its sum and accumulator.
+constexpr float kLazyMax = 8.0f;
 
 // HPW query heads of one KV group x RPW = 4 / HPW blocks of 64 rows per workgroup (four waves),
 // so that groups of fewer than four heads still share each K/V tile among four waves.
@@ -223,11 +227,12 @@ __global__ __launch_bounds__(256, 2) void attn_sink_fwd_kernel(FwdArgs a) {
       }
       tmax[nb] = max_xor32(t) * a.scale_log2;
     }
-    // Rescale a 32-query column block only when one of its rows saw a larger maximum (deciding
-    // per block rather than per wave skips about a third of the rescales on long rows).
+    // Rescale a 32-query column block only when one of its rows saw a maximum more than
+    // kLazyMax above its reference (deciding per block rather than per wave, and lazily, skips
+    // most rescales on long rows). Below that the tile's values exp2(s - m) stay under 2^kLazyMax.
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      if (wave_any(tmax[nb] > m[nb])) {
+      if (wave_any(tmax[nb] > m[nb] + kLazyMax)) {
         const float mnew = fmaxf(m[nb], tmax[nb]);
         const float alpha = mnew == kNegInf ? 1.0f : fast_exp2(m[nb] - mnew);
         lsum[nb] *= alpha;
