@@ -174,7 +174,8 @@ def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, sinks: torch.Tensor, 
         dv: Optional[torch.Tensor] = None, dsinks: Optional[torch.Tensor] = None,
         workspace: Optional[torch.Tensor] = None, events: Optional[Sequence[int]] = None):
     """Backward. Returns (dq [T,Hq,64], dk [T,Hkv,64], dv [T,Hkv,64], dsinks [Hq]), all fp32.
-    ``events``: optional raw hipEvent_t handles (num kernels + 1) recorded around each kernel."""
+    ``events``: optional raw hipEvent_t handles (num kernels + 1) recorded around each kernel; an
+    entry may be None (nothing recorded there)."""
     lib = load_library()
     dev = q.device
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (dout, "dout")):
@@ -236,7 +237,7 @@ def decode_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, sinks: torch.T
     """Decode forward: q [Tq,Hq,64] (each sequence's last Nq_b tokens), k/v [Tk,Hkv,64] caches, bf16;
     sinks [Hq] fp32; cu_seqlens_q / cu_seqlens_k [B+1] int32 (device). Returns (out [Tq,Hq,64] in
     ``out_dtype``, lse [Hq,Tq] fp32). ``events``: optional raw hipEvent_t handles (num kernels + 1)
-    recorded around each kernel."""
+    recorded around each kernel; an entry may be None (nothing recorded there)."""
     lib = load_library()
     dev = q.device
     for t, n in ((q, "q"), (k, "k"), (v, "v")):

@@ -138,10 +138,13 @@ int bwd_impl(const void* q, const void* k, const void* v, const float* sinks, co
   typedef hipError_t (*launcher)(const BwdArgs&, hipStream_t);
   const launcher steps[kBwdNumKernels] = {launch_bwd_dq, launch_bwd_dkdv, launch_bwd_finish};
   for (int i = 0; i < kBwdNumKernels; ++i) {
-    if (events && hipEventRecord(static_cast<hipEvent_t>(events[i]), stream) != hipSuccess) return ATTN_SINK_ERR_HIP;
+    if (events && events[i] && hipEventRecord(static_cast<hipEvent_t>(events[i]), stream) != hipSuccess) {
+      return ATTN_SINK_ERR_HIP;
+    }
     if (steps[i](a, stream) != hipSuccess) return ATTN_SINK_ERR_HIP;
   }
-  if (events && hipEventRecord(static_cast<hipEvent_t>(events[kBwdNumKernels]), stream) != hipSuccess) {
+  if (events && events[kBwdNumKernels] &&
+      hipEventRecord(static_cast<hipEvent_t>(events[kBwdNumKernels]), stream) != hipSuccess) {
     return ATTN_SINK_ERR_HIP;
   }
   return ATTN_SINK_OK;
@@ -291,7 +294,7 @@ int attn_sink_decode_fwd_timed(const void* q, const void* k, const void* v, cons
   hipEvent_t const* ev = reinterpret_cast<hipEvent_t const*>(events);
   if (shape->total_q == 0) {  // nothing to compute; the events still mark the (empty) interval
     for (int i = 0; ev && i <= kDecodeNumKernels; ++i) {
-      if (hipEventRecord(ev[i], stream) != hipSuccess) return ATTN_SINK_ERR_HIP;
+      if (ev[i] && hipEventRecord(ev[i], stream) != hipSuccess) return ATTN_SINK_ERR_HIP;
     }
     return ATTN_SINK_OK;
   }

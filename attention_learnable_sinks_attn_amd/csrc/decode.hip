@@ -285,14 +285,14 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream, hipEvent_t con
   const long long parts = (long long)a.B * a.Hkv * a.n_chunks;
   if (parts <= 0) return hipSuccess;
   hipError_t e;
-  if (events && (e = hipEventRecord(events[0], stream)) != hipSuccess) return e;
+  if (events && events[0] && (e = hipEventRecord(events[0], stream)) != hipSuccess) return e;
   hipLaunchKernelGGL(attn_sink_decode_partial_kernel, dim3((unsigned)parts), dim3(64), 0, stream, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  if (events && (e = hipEventRecord(events[1], stream)) != hipSuccess) return e;
+  if (events && events[1] && (e = hipEventRecord(events[1], stream)) != hipSuccess) return e;
   hipLaunchKernelGGL(attn_sink_decode_combine_kernel, dim3((unsigned)(a.B * a.Hkv * a.n_cols)),
                      dim3(64 * kCombineWaves), 0, stream, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  if (events && (e = hipEventRecord(events[2], stream)) != hipSuccess) return e;
+  if (events && events[2] && (e = hipEventRecord(events[2], stream)) != hipSuccess) return e;
   return hipSuccess;
 }
 

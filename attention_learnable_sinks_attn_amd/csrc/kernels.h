@@ -19,7 +19,8 @@ hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream);    // dK, dV (
 hipError_t launch_bwd_finish(const BwdArgs& a, hipStream_t stream);  // dK, dV = sum of halves; dSink
 
 // Inference-shaped forward: per-chunk partials, then the combine with the sink.
-// events: NULL, or kDecodeNumKernels + 1 events recorded before, between and after the kernels.
+// events: NULL, or kDecodeNumKernels + 1 events recorded before, between and after the kernels
+// (a NULL entry records nothing at that point).
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream, hipEvent_t const* events);
 
 }  // namespace attn_sink

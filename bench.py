@@ -16,10 +16,15 @@ algorithmic HBM GB/s (q, every cached K/V row a new token sees, out and LSE, eac
 Prints one JSON line. ``value`` is algorithmic TFLOP/s over the timed steps: 4*d FLOPs per visible
 (query, key, head) in the forward (QK^T and PV) plus 10*d in the backward (S, dP, dV, dK, dQ);
 recomputation and masked tile work are not counted. ``roofline`` describes the kernel with the
-largest share of the step time, timed with HIP events recorded on the stream the kernels run on:
-against the bf16 MFMA peak for the causal workloads, and against HBM bandwidth (algorithmic bytes:
+largest share of the step time (in the per-kernel breakdown ``kernel_ms``, taken with events around
+every kernel in the last warm-up steps), timed with HIP events recorded around it, on the stream
+the kernels run on, in every timed step: against the bf16 MFMA peak for the causal workloads, and against HBM bandwidth (algorithmic bytes:
 each tensor the kernel needs read or written once at its ABI dtype) for the banded window ones.
 ``cpu_baseline`` times the fp64 CPU oracle on a bounded sample of the same workload.
+
+Each HIP event record costs about 3 us of GPU time on MI355X; events around every kernel of every
+timed step added about 2.5% to a 4k step (and 10% to a decode call), so the timed steps carry only
+the two events around the dominant kernel.
 
 ``--copy-probe-mib N`` also runs one device-to-device copy of N MiB before the timed steps, the
 known-size kernel that scales the FETCH_SIZE / WRITE_SIZE counters of a ``rocprofv3 --pmc`` run.
@@ -175,6 +180,65 @@ def decode_bytes(d, hq: int, hkv: int, out_bytes: int):
             "attn_sink_decode_combine_kernel": tq * hq * 64 * out_bytes + hq * tq * 4}
 
 
+BREAKDOWN_STEPS = 10  # last warm-up steps that carry events around every kernel
+
+
+def breakdown_source(warmup: int) -> str:
+    return f"the last {min(BREAKDOWN_STEPS, warmup)} warm-up steps" if warmup > 0 else "the timed steps"
+
+
+def run_timed(step, names, hip, warmup: int, steps: int):
+    """Warm-up, then exactly `steps` timed steps.
+
+    step(evs) runs one step; evs is None or a list of len(names) + 1 event handles (entries may be
+    None), entry i recorded before kernel i and the last after the last kernel. Each event record
+    costs about 3 us of GPU time, so only the last BREAKDOWN_STEPS warm-up steps carry events
+    around every kernel (the per-kernel breakdown and the choice of the dominant kernel), and the
+    timed steps carry just the two around the dominant kernel, whose average duration over the
+    timed steps is its measured launch time. Returns (ms per step, wall seconds of the timed
+    steps, per-kernel ms, dominant kernel, its ms over the timed steps)."""
+    n = len(names)
+    bd = min(BREAKDOWN_STEPS, warmup)
+    full = [[hip.event() for _ in range(n + 1)] for _ in range(bd)]
+    for w in range(warmup):
+        j = w - (warmup - bd)
+        step(full[j] if j >= 0 else None)
+    torch.cuda.synchronize()
+    per_kernel = {nm: sum(hip.elapsed_ms(full[j][i], full[j][i + 1]) for j in range(bd)) / max(bd, 1)
+                  for i, nm in enumerate(names)}
+    if bd > 0:
+        dom = max(per_kernel, key=per_kernel.get)
+        di = names.index(dom)
+        timed = [[hip.event(), hip.event()] for _ in range(steps)]
+
+        def evs_for(st):
+            e = [None] * (n + 1)
+            e[di], e[di + 1] = timed[st]
+            return e
+    else:  # no warm-up to take the breakdown from: the timed steps carry every event
+        timed = [[hip.event() for _ in range(n + 1)] for _ in range(steps)]
+
+        def evs_for(st):
+            return timed[st]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record()
+    for st in range(steps):
+        step(evs_for(st))
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = start.elapsed_time(end) / steps
+    if bd > 0:
+        dom_ms = sum(hip.elapsed_ms(a, b) for a, b in timed) / steps
+    else:
+        per_kernel = {nm: sum(hip.elapsed_ms(timed[st][i], timed[st][i + 1]) for st in range(steps)) / steps
+                      for i, nm in enumerate(names)}
+        dom = max(per_kernel, key=per_kernel.get)
+        dom_ms = per_kernel[dom]
+    return ms_step, wall, per_kernel, dom, dom_ms
+
+
 def bench_decode(args):
     """Decode forward (attn_sink_decode_fwd, bf16 output) over resident KV caches."""
     d = make_decode_workload_inputs(args.workload, args.seed)
@@ -189,37 +253,19 @@ def bench_decode(args):
     ws = torch.empty((asa.decode_workspace_bytes(q, k, cu_q, d.max_q, d.max_k),), dtype=torch.uint8, device=dev)
     names = asa.decode_kernel_names()
     hip = Hip()
-    stream = torch.cuda.current_stream(dev).cuda_stream
-    events = [[hip.event() for _ in range(len(names) + 1)] for _ in range(args.steps)]
 
     def step(evs=None):
         asa.decode_fwd(q, k, v, sinks, cu_q, cu_k, d.max_q, d.max_k, window=window, out_dtype=torch.bfloat16,
                        out=out, lse=lse, workspace=ws, events=evs)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    start.record()
-    for s in range(args.steps):
-        step(events[s])
-    end.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_step = start.elapsed_time(end) / args.steps
-    per_kernel = {n: 0.0 for n in names}
-    for s in range(args.steps):
-        for i, n in enumerate(names):
-            per_kernel[n] += hip.elapsed_ms(events[s][i], events[s][i + 1]) / args.steps
+    ms_step, wall, per_kernel, dom, dom_ms = run_timed(step, names, hip, args.warmup, args.steps)
     kb = decode_bytes(d, hq, hkv, 2)
     total = sum(kb.values())
     gbs = total / (ms_step * 1e-3) / 1e9
-    dom = max(per_kernel, key=per_kernel.get)
-    achieved = kb[dom] / (per_kernel[dom] * 1e-3) / 1e9
+    achieved = kb[dom] / (dom_ms * 1e-3) / 1e9
     roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                "avg_launch_ms": round(per_kernel[dom], 4), "algorithmic_bytes": kb[dom]}
+                "avg_launch_ms": round(dom_ms, 4), "algorithmic_bytes": kb[dom]}
     rec = TRAFFIC.get((args.workload, dom))
     if rec is not None and rec["digest"] == kernel_source_digest():
         roofline["traffic"] = rec["bytes"]
@@ -233,6 +279,7 @@ def bench_decode(args):
                    "seed": args.seed, "parallelism": "none (1 GPU)"},
         "tokens_per_s": round(Tq / (ms_step * 1e-3), 1),
         "kernel_ms": {n: round(t, 4) for n, t in per_kernel.items()},
+        "kernel_ms_from": breakdown_source(args.warmup),
         "wall_s_timed": round(wall, 4),
         "roofline": roofline,
     }
@@ -294,50 +341,32 @@ def main():
 
     hip = Hip()
     stream = torch.cuda.current_stream(dev).cuda_stream
-    nk = len(names)
-    events = [[hip.event() for _ in range(nk + 1)] for _ in range(args.steps)]
 
     def step(evs=None):
-        if evs is not None:
+        if evs is not None and evs[0] is not None:
             hip.record(evs[0], stream)
+        bwd_ev = None if evs is None or all(e is None for e in evs[1:]) else evs[1:]
         asa.fwd(q, k, v, sinks, cu, inp.max_seqlen, inp.causal, inp.window, out=out, lse=lse)
         asa.bwd(q, k, v, sinks, out, lse, dout, cu, inp.max_seqlen, inp.causal, inp.window, dq=dq, dk=dk, dv=dv,
-                dsinks=dsinks, workspace=ws, events=None if evs is None else evs[1:])
+                dsinks=dsinks, workspace=ws, events=bwd_ev)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    start.record()
-    for s in range(args.steps):
-        step(events[s])
-    end.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_step = start.elapsed_time(end) / args.steps
-
-    per_kernel = {n: 0.0 for n in names}
-    for s in range(args.steps):
-        for i, n in enumerate(names):
-            per_kernel[n] += hip.elapsed_ms(events[s][i], events[s][i + 1]) / args.steps
+    ms_step, wall, per_kernel, dom, dom_ms = run_timed(step, names, hip, args.warmup, args.steps)
 
     pairs = visible_pairs(inp.lengths, inp.causal, inp.window) * Hq
     flops = pairs * 14 * d
     tflops = flops / (ms_step * 1e-3) / 1e12
-    dom = max(per_kernel, key=per_kernel.get)
     if inp.window > 0:  # banded: far less compute per byte than the ridge point
         dom_bytes = kernel_bytes(dom, T, Hq, Hkv, d)
-        achieved = dom_bytes / (per_kernel[dom] * 1e-3) / 1e9
+        achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
         roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                    "avg_launch_ms": round(per_kernel[dom], 4), "algorithmic_bytes": dom_bytes}
+                    "avg_launch_ms": round(dom_ms, 4), "algorithmic_bytes": dom_bytes}
     else:
         dom_flops = pairs * KERNEL_FLOPS_PER_PAIR_D[dom] * d
-        achieved = dom_flops / (per_kernel[dom] * 1e-3) / 1e12
+        achieved = dom_flops / (dom_ms * 1e-3) / 1e12
         roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                     "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
-                    "avg_launch_ms": round(per_kernel[dom], 4), "algorithmic_flops": dom_flops}
+                    "avg_launch_ms": round(dom_ms, 4), "algorithmic_flops": dom_flops}
     rec = TRAFFIC.get((w.name, dom))
     if rec is not None and rec["digest"] == kernel_source_digest():
         roofline["traffic"] = rec["bytes"]
@@ -351,6 +380,7 @@ def main():
                    "seed": args.seed, "parallelism": "none (1 GPU)"},
         "pct_mfma_peak": round(100 * tflops / MFMA_BF16_PEAK_TFLOPS, 2),
         "kernel_ms": {n: round(t, 4) for n, t in per_kernel.items()},
+        "kernel_ms_from": breakdown_source(args.warmup),
         "wall_s_timed": round(wall, 4),
         "roofline": roofline,
     }

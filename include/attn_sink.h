@@ -121,7 +121,9 @@ int attn_sink_bwd(const void* q, const void* k, const void* v, const float* sink
  * Same as attn_sink_bwd, and additionally records events[0..num_events-1] on `stream` around the
  * backward's kernels (events[i] before kernel i, events[num_kernels] after the last), for
  * per-kernel timing. `events` holds hipEvent_t handles created by the caller; num_events must be
- * attn_sink_bwd_num_kernels() + 1. Passing events == NULL behaves like attn_sink_bwd.
+ * attn_sink_bwd_num_kernels() + 1. An entry may be NULL: nothing is recorded at that point (each
+ * record costs a few microseconds of GPU time, so a caller timing one kernel passes only the two
+ * events around it). Passing events == NULL behaves like attn_sink_bwd.
  */
 int attn_sink_bwd_timed(const void* q, const void* k, const void* v, const float* sinks, const void* out,
                         const float* lse, const void* dout, int causal, int window, const int32_t* cu_seqlens,
@@ -171,8 +173,9 @@ int attn_sink_decode_fwd(const void* q, const void* k, const void* v, const floa
 /*
  * attn_sink_decode_fwd with timing: events (hipEvent_t handles owned by the caller) are recorded on
  * `stream` before the first kernel, between the kernels and after the last; num_events must equal
- * attn_sink_decode_num_kernels() + 1, else ATTN_SINK_ERR_BAD_SHAPE. events == NULL behaves like
- * attn_sink_decode_fwd. attn_sink_decode_kernel_name(i) names kernel i (static string, or NULL).
+ * attn_sink_decode_num_kernels() + 1, else ATTN_SINK_ERR_BAD_SHAPE; an entry may be NULL (nothing
+ * is recorded there). events == NULL behaves like attn_sink_decode_fwd.
+ * attn_sink_decode_kernel_name(i) names kernel i (static string, or NULL).
  */
 int attn_sink_decode_fwd_timed(const void* q, const void* k, const void* v, const float* sinks, int window,
                                const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,

@@ -244,3 +244,37 @@ def test_forward_bf16_output_is_rounded_fp32_output(causal, window):
     assert o16.dtype == torch.bfloat16
     assert torch.equal(o16, o32.to(torch.bfloat16))
     assert torch.equal(l16, l32)
+
+
+def test_timed_backward_records_only_the_given_events():
+    """attn_sink_bwd_timed with NULL entries: results unchanged, the given events bracket a kernel."""
+    import ctypes
+    hip = ctypes.CDLL("libamdhip64.so")
+    hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+    hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    evs = []
+    for _ in range(2):
+        e = ctypes.c_void_p()
+        assert hip.hipEventCreate(ctypes.byref(e)) == 0
+        evs.append(e.value)
+    inp = make_inputs((300, 77), 16, 2, 64, causal=True, window=0, seed=5)
+    dev = torch.device("cuda:0")
+    q, k, v, dout = (t.to(dev) for t in (inp.q, inp.k, inp.v, inp.dout))
+    sinks, cu = inp.sinks.to(dev), inp.cu_seqlens.to(dev)
+    say("[gpu] timed backward with events around the dK/dV kernel only")
+    out, lse = asa.fwd(q, k, v, sinks, cu, inp.max_seqlen, True, 0)
+    ref = asa.bwd(q, k, v, sinks, out, lse, dout, cu, inp.max_seqlen, True, 0)
+    names = list(asa.bwd_kernel_names())
+    i = names.index("attn_sink_bwd_dkdv_kernel")
+    events = [None] * (len(names) + 1)
+    events[i], events[i + 1] = evs
+    got = asa.bwd(q, k, v, sinks, out, lse, dout, cu, inp.max_seqlen, True, 0, events=events)
+    torch.cuda.synchronize()
+    for a, b in zip(ref, got):
+        assert torch.equal(a, b)
+    ms = ctypes.c_float()
+    assert hip.hipEventElapsedTime(ctypes.byref(ms), evs[0], evs[1]) == 0
+    assert ms.value > 0.0
+    for e in evs:
+        hip.hipEventDestroy(e)
