@@ -68,14 +68,14 @@ KERNEL_FLOPS_PER_PAIR_D = {
 # (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch) scaled by what the same counters read for the
 # copy probe; valid only for kernel sources with the recorded digest.
 TRAFFIC = {
-    ("causal4k", "attn_sink_bwd_dkdv_kernel"): {"bytes": 146989635, "digest": "a85b8fbd28b26bce"},
-    ("window4k", "attn_sink_bwd_dkdv_kernel"): {"bytes": 106320440, "digest": "a85b8fbd28b26bce"},
-    ("window4k", "attn_sink_bwd_dq_kernel"): {"bytes": 213268199, "digest": "a85b8fbd28b26bce"},
-    ("varlen_window", "attn_sink_bwd_dkdv_kernel"): {"bytes": 1719028369, "digest": "a85b8fbd28b26bce"},
-    ("varlen_window", "attn_sink_bwd_dq_kernel"): {"bytes": 3785463194, "digest": "a85b8fbd28b26bce"},
-    ("band4k", "attn_sink_bwd_dkdv_kernel"): {"bytes": 125982588, "digest": "a85b8fbd28b26bce"},
-    ("band4k", "attn_sink_bwd_dq_kernel"): {"bytes": 213271579, "digest": "a85b8fbd28b26bce"},
-    ("decode32k", "attn_sink_decode_partial_kernel"): {"bytes": 368474106, "digest": "a85b8fbd28b26bce"},
+    ("causal4k", "attn_sink_bwd_dkdv_kernel"): {"bytes": 146981480, "digest": "f3d498da4ea91067"},
+    ("window4k", "attn_sink_bwd_dkdv_kernel"): {"bytes": 106979536, "digest": "f3d498da4ea91067"},
+    ("window4k", "attn_sink_bwd_dq_kernel"): {"bytes": 213277939, "digest": "f3d498da4ea91067"},
+    ("varlen_window", "attn_sink_bwd_dkdv_kernel"): {"bytes": 1721671051, "digest": "f3d498da4ea91067"},
+    ("varlen_window", "attn_sink_bwd_dq_kernel"): {"bytes": 3790946667, "digest": "f3d498da4ea91067"},
+    ("band4k", "attn_sink_bwd_dkdv_kernel"): {"bytes": 126419728, "digest": "f3d498da4ea91067"},
+    ("band4k", "attn_sink_bwd_dq_kernel"): {"bytes": 213303058, "digest": "f3d498da4ea91067"},
+    ("decode32k", "attn_sink_decode_partial_kernel"): {"bytes": 368465214, "digest": "f3d498da4ea91067"},
 }
 
 
