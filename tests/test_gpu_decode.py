@@ -133,3 +133,33 @@ def test_train_inference_consistency(window):
     dl = (lse_d - lse_t[:, rows_t]).abs().max().item()
     say(f"  training vs decode: out max-abs diff {do:.3e}, lse max-abs diff {dl:.3e}")
     assert do <= CONSIST_TOL["out"] and dl <= CONSIST_TOL["lse"]
+
+
+def test_decode_timed_records_only_the_given_events():
+    """attn_sink_decode_fwd_timed with a NULL entry: results unchanged, the given events bracket the
+    partial kernel."""
+    import ctypes
+    hip = ctypes.CDLL("libamdhip64.so")
+    hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+    hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    evs = []
+    for _ in range(2):
+        e = ctypes.c_void_p()
+        assert hip.hipEventCreate(ctypes.byref(e)) == 0
+        evs.append(e.value)
+    d = make_decode_inputs((700, 1500, 90), 2, 8, 2, seed=3)
+    dev = torch.device("cuda:0")
+    args = ((d.q.to(dev), d.k.to(dev), d.v.to(dev), d.sinks.to(dev), d.cu_q.to(dev), d.cu_k.to(dev), d.max_q,
+             d.max_k))
+    say("[gpu] timed decode with events around the partial kernel only")
+    ref = asa.decode_fwd(*args)
+    got = asa.decode_fwd(*args, events=[evs[0], evs[1], None])
+    torch.cuda.synchronize()
+    for a, b in zip(ref, got):
+        assert torch.equal(a, b)
+    ms = ctypes.c_float()
+    assert hip.hipEventElapsedTime(ctypes.byref(ms), evs[0], evs[1]) == 0
+    assert ms.value > 0.0
+    for e in evs:
+        hip.hipEventDestroy(e)
