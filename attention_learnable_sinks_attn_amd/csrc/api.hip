@@ -161,10 +161,10 @@ int check_decode_shape(const attn_sink_decode_shape* s) {
   if (s->head_dim != kHeadDim || (s->out_dtype != ATTN_SINK_F32 && s->out_dtype != ATTN_SINK_BF16)) {
     return ATTN_SINK_ERR_UNSUPPORTED;
   }
-  if ((long long)s->max_q * (s->num_heads_q / s->num_heads_kv) > 32) return ATTN_SINK_ERR_UNSUPPORTED;
+  if ((long long)s->max_q * (s->num_heads_q / s->num_heads_kv) > kDecodeMaxCols) return ATTN_SINK_ERR_UNSUPPORTED;
   if ((long long)s->total_k * s->num_heads_kv * kHeadDim >= (1LL << 40) ||
       (long long)s->total_q * s->num_heads_q >= (1LL << 31) ||
-      (long long)s->num_seqs * s->num_heads_kv * 32 >= (1LL << 31) ||  // workgroups of one launch
+      (long long)s->num_seqs * s->num_heads_kv * kDecodeMaxCols >= (1LL << 31) ||  // workgroups of one launch
       (s->total_q > 0 && s->max_q < 1)) {
     return ATTN_SINK_ERR_BAD_SHAPE;
   }
@@ -184,8 +184,14 @@ void split_keys(long long pairs, long long tiles, long long* per, long long* n) 
 // Chunks for a call with the given window. The workspace is sized for window 0; a window only
 // shortens the span to chunk (the keys from the 64-aligned start of the first visible one), and the
 // chunk count never exceeds the workspace's.
+// Groups of 32 (new token, query head) columns per (sequence, KV head).
+int decode_col_groups(const attn_sink_decode_shape* s) {
+  const long long cols = (long long)s->max_q * (s->num_heads_q / s->num_heads_kv);
+  return (int)std::max<long long>(1, (cols + 31) / 32);
+}
+
 void decode_chunks(const attn_sink_decode_shape* s, int window, int* n_chunks, int* chunk_keys) {
-  const long long pairs = (long long)s->num_seqs * s->num_heads_kv;
+  const long long pairs = (long long)s->num_seqs * s->num_heads_kv * decode_col_groups(s);
   long long per, n;
   split_keys(pairs, ((long long)s->max_k + 63) / 64, &per, &n);
   if (window > 0) {
@@ -205,13 +211,15 @@ void decode_chunks(const attn_sink_decode_shape* s, int window, int* n_chunks, i
 }
 
 size_t decode_part_o_bytes(const attn_sink_decode_shape* s, int n_chunks) {
-  return round256((size_t)s->num_seqs * s->num_heads_kv * n_chunks * kHeadDim * 32 * sizeof(float));
+  return round256((size_t)s->num_seqs * s->num_heads_kv * decode_col_groups(s) * n_chunks * kHeadDim * 32 *
+                  sizeof(float));
 }
 
 size_t decode_workspace_bytes(const attn_sink_decode_shape* s) {
   int n, ck;
   decode_chunks(s, 0, &n, &ck);
-  return decode_part_o_bytes(s, n) + round256((size_t)s->num_seqs * s->num_heads_kv * n * 2 * 32 * sizeof(float));
+  return decode_part_o_bytes(s, n) +
+         round256((size_t)s->num_seqs * s->num_heads_kv * decode_col_groups(s) * n * 2 * 32 * sizeof(float));
 }
 
 }  // namespace
@@ -317,6 +325,7 @@ int attn_sink_decode_fwd_timed(const void* q, const void* k, const void* v, cons
   a.Hkv = shape->num_heads_kv;
   a.G = a.Hq / a.Hkv;
   a.n_cols = shape->max_q * a.G;
+  a.n_cg = decode_col_groups(shape);
   a.window = clamp_window(window, shape->max_k);
   a.out_bf16 = shape->out_dtype == ATTN_SINK_BF16 ? 1 : 0;
   const float scale = shape->softmax_scale > 0.0f ? shape->softmax_scale : 1.0f / sqrtf((float)shape->head_dim);

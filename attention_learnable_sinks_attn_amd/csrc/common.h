@@ -339,10 +339,11 @@ struct DecodeArgs {
   const int32_t* cu_k;
   void* out;           // [Tq, Hq, 64], fp32 or bf16 (out_bf16)
   float* lse;          // [Hq, Tq]
-  float* part_o;       // per (sequence, KV head, chunk): [32 columns][64] unnormalised outputs
-  float* part_ml;      // per (sequence, KV head, chunk): [2][32] running max (log2), denominator
+  float* part_o;       // per (sequence, KV head, column group, chunk): [32 columns][64] unnormalised outputs
+  float* part_ml;      // per (sequence, KV head, column group, chunk): [2][32] running max (log2), denominator
   int Tq, B, Hq, Hkv, G;
-  int n_cols;          // max_q * G <= 32: the columns any (sequence, KV head) uses
+  int n_cols;          // max_q * G: the columns any (sequence, KV head) uses
+  int n_cg;            // ceil(n_cols / 32): groups of 32 columns, one wave each per chunk
   int n_chunks;        // key chunks per sequence
   int chunk_keys;      // keys per chunk (multiple of 64)
   int window;

@@ -7,8 +7,9 @@
 // with no value row; section "数学公式深入解读", eq. P_ij).
 //
 // Split over the key axis. attn_sink_decode_partial_kernel: one wave per (sequence, KV head,
-// chunk of keys). Its 32 MFMA columns are the group's (new query, query head) pairs, so the G
-// query heads of a KV head share every K and V tile: S^T = K Q^T (32x32x16 MFMA, keys on the C
+// group of 32 columns, chunk of keys). The columns are the group's (new query, query head) pairs,
+// column c = j * G + (query head - g * G) for new token j, taken 32 at a time as the wave's MFMA
+// columns, so the G query heads of a KV head share every K and V tile: S^T = K Q^T (32x32x16 MFMA, keys on the C
 // rows), a sink-free online softmax per column (lane), O^T += V^T P^T, with K and V tiles of 64
 // keys streamed through a 3-slot LDS ring of swizzled tiles (direct global->LDS copies two tiles
 // ahead, transposing reads for V^T; see common.h). It writes the chunk's running max (log2
@@ -31,12 +32,13 @@ __global__ __launch_bounds__(64) void attn_sink_decode_partial_kernel(DecodeArgs
   __shared__ __attribute__((aligned(1024))) unsigned char ring[kDecRing * kDecSlotBytes];
 
   // The KV heads of one chunk of keys are neighbours in the launch, so that the rows they share
-  // are read from HBM at about the same time.
+  // are read from HBM at about the same time; then the column groups of the same chunk.
   const int g = blockIdx.x % a.Hkv;
-  const int rest = blockIdx.x / a.Hkv;  // = b * n_chunks + chunk
+  const int rest = blockIdx.x / a.Hkv;  // = (b * n_cg + cg) * n_chunks + chunk
   const int chunk = rest % a.n_chunks;
-  const int b = rest / a.n_chunks;
-  const int pidx = (b * a.Hkv + g) * a.n_chunks + chunk;  // the partial's index
+  const int cg = (rest / a.n_chunks) % a.n_cg;
+  const int b = rest / a.n_chunks / a.n_cg;
+  const int pidx = ((b * a.Hkv + g) * a.n_cg + cg) * a.n_chunks + chunk;  // the partial's index
   const int cq = a.cu_q[b];
   const int nq = a.cu_q[b + 1] - cq;
   const int ck = a.cu_k[b];
@@ -45,9 +47,10 @@ __global__ __launch_bounds__(64) void attn_sink_decode_partial_kernel(DecodeArgs
   const int lane = threadIdx.x & 63;
   const int l32 = lane & 31;
   const int grp = lane >> 5;
-  const int j = l32 / a.G;                 // column = (new query j, query head g*G + l32 % G)
-  const int hq = g * a.G + l32 % a.G;
-  const bool col_ok = j < nq;              // nq * G <= 32 (checked on the host)
+  const int col = 32 * cg + l32;
+  const int j = col / a.G;                 // column = (new query j, query head g*G + col % G)
+  const int hq = g * a.G + col % a.G;
+  const bool col_ok = j < nq;              // columns past the last pair repeat the last query
   const int pos = lk - nq + min(j, nq - 1);  // the column's query position (< 0: sees no key)
 
   // Keys of this chunk that some column can see. Chunks tile the keys from the 64-aligned start of
@@ -225,7 +228,7 @@ constexpr int kCombineWaves = 4;
 __global__ __launch_bounds__(64 * kCombineWaves) void attn_sink_decode_combine_kernel(DecodeArgs a) {
   __shared__ float red[kCombineWaves][kHeadDim + 1];
   const int c = blockIdx.x % a.n_cols;
-  const int rest = blockIdx.x / a.n_cols;
+  const int rest = blockIdx.x / a.n_cols;  // = b * Hkv + g
   const int g = rest % a.Hkv;
   const int b = rest / a.Hkv;
   const int cq = a.cu_q[b];
@@ -235,8 +238,10 @@ __global__ __launch_bounds__(64 * kCombineWaves) void attn_sink_decode_combine_k
   const int hq = g * a.G + c % a.G;
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
-  const size_t p0 = (size_t)rest * a.n_chunks;  // first partial of this (sequence, KV head)
-  const float* ml = a.part_ml + p0 * 64 + c;    // chunk ch: max at ml[64 ch], denominator at ml[64 ch + 32]
+  // First partial of this (sequence, KV head, column group); chunk ch: max at ml[64 ch],
+  // denominator at ml[64 ch + 32].
+  const size_t p0 = ((size_t)rest * a.n_cg + c / 32) * a.n_chunks;
+  const float* ml = a.part_ml + p0 * 64 + c % 32;
 
   // Largest running max over the chunks and the sink (log2 units).
   const float sink2 = a.sinks[hq] * kLog2e;
@@ -252,7 +257,7 @@ __global__ __launch_bounds__(64 * kCombineWaves) void attn_sink_decode_combine_k
   __syncthreads();  // red[.][kHeadDim] is reused below
 
   float acc = 0.0f, L = 0.0f;
-  const float* po = a.part_o + p0 * 32 * kHeadDim + c * kHeadDim + lane;
+  const float* po = a.part_o + p0 * 32 * kHeadDim + (c % 32) * kHeadDim + lane;
 #pragma unroll 4
   for (int ch = w; ch < a.n_chunks; ch += kCombineWaves) {
     const float wt = fast_exp2(ml[(size_t)ch * 64] - Ms);  // 0 for an empty chunk (max -inf)
@@ -282,7 +287,7 @@ __global__ __launch_bounds__(64 * kCombineWaves) void attn_sink_decode_combine_k
 }  // namespace
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream, hipEvent_t const* events) {
-  const long long parts = (long long)a.B * a.Hkv * a.n_chunks;
+  const long long parts = (long long)a.B * a.Hkv * a.n_cg * a.n_chunks;
   if (parts <= 0) return hipSuccess;
   hipError_t e;
   if (events && events[0] && (e = hipEventRecord(events[0], stream)) != hipSuccess) return e;

@@ -146,8 +146,8 @@ int attn_sink_bwd_timed(const void* q, const void* k, const void* v, const float
  *   out    [Tq, Hq, 64] fp32 (out_dtype ATTN_SINK_F32) or bf16 (ATTN_SINK_BF16)
  *   lse    [Hq, Tq] fp32, natural log, sink included
  *   cu_seqlens_q / cu_seqlens_k  [B+1] int32 on the device, non-decreasing, Nq_b <= Lk_b (trusted)
- * Requires max_q * (Hq / Hkv) <= 32 (the new queries of one KV head's query heads fill one
- * 32-column MFMA block), else ATTN_SINK_ERR_UNSUPPORTED. workspace: caller-owned device memory
+ * Requires max_q * (Hq / Hkv) <= 1024 (the (new token, query head) pairs of one KV head, taken 32
+ * at a time as MFMA columns), else ATTN_SINK_ERR_UNSUPPORTED. workspace: caller-owned device memory
  * of at least attn_sink_decode_workspace_bytes(shape) bytes (per-chunk partial results); its
  * contents on entry do not matter. Same ownership, asynchrony and error conventions as above.
  */

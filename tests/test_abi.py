@@ -168,10 +168,10 @@ def test_decode_argument_errors():
     assert decode(lib, dshape(max_q=0)) == -2    # new tokens but max_q = 0
     assert decode(lib, dshape(d=128)) == -3
     assert decode(lib, dshape(dtype=2)) == -3
-    # the new queries of one KV head's query heads must fit 32 MFMA columns
-    assert decode(lib, dshape(max_q=5, hq=8, hkv=1)) == -3
-    assert decode(lib, dshape(max_q=8, hq=64, hkv=8)) == -3
-    assert decode(lib, dshape(max_q=2, hq=32, hkv=1)) == -3
+    # at most 1024 (new token, query head) pairs per KV head
+    assert decode(lib, dshape(tq=300, max_q=129, hq=8, hkv=1)) == -3
+    assert decode(lib, dshape(tq=300, max_q=129, hq=64, hkv=8)) == -3
+    assert decode(lib, dshape(tq=300, max_q=33, hq=32, hkv=1)) == -3
     assert decode(lib, dshape(), window=-1) == -4
     s = dshape()
     need = lib.attn_sink_decode_workspace_bytes(ctypes.byref(s))
@@ -194,7 +194,12 @@ def test_decode_workspace_formula():
     need = lib.attn_sink_decode_workspace_bytes(ctypes.byref(s))
     assert need == 64 * 64 * 32 * 64 * 4 + 64 * 64 * 2 * 32 * 4
     assert lib.attn_sink_decode_workspace_bytes(None) == 0
-    assert lib.attn_sink_decode_workspace_bytes(ctypes.byref(dshape(max_q=5))) == 0
+    assert lib.attn_sink_decode_workspace_bytes(ctypes.byref(dshape(tq=300, max_q=129))) == 0
+    # 40 columns per KV head: two groups of 32, each with its own partials
+    s2 = dshape(tq=8, tk=200000, B=8, max_q=5, max_k=32768, hq=64, hkv=8)
+    need2 = lib.attn_sink_decode_workspace_bytes(ctypes.byref(s2))
+    # 128 (sequence, KV head, column group) triples -> 4096 / 128 = 32 chunks of 16 tiles
+    assert need2 == 128 * 32 * 32 * 64 * 4 + 128 * 32 * 2 * 32 * 4
 
 
 @needs_lib

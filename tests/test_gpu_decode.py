@@ -97,8 +97,17 @@ def test_decode_empty_batch():
     assert out.shape == (0, 8, 64) and lse.shape == (8, 0)
 
 
+@pytest.mark.parametrize("nq,hq,hkv,window", [(5, 8, 1, 0), (16, 64, 8, 0), (9, 16, 2, 40), (31, 32, 1, 0)])
+def test_decode_several_column_groups(nq, hq, hkv, window):
+    # more (new token, query head) pairs per KV head than one 32-column MFMA block holds
+    d = make_decode_inputs((300, 70, 1029), nq, hq, hkv, window=window, seed=2)
+    say(f"decode: {nq} new tokens x {hq // hkv} heads per KV head, window {window}")
+    out, lse = run_decode(d)
+    check_against_oracle(d, out, lse)
+
+
 def test_decode_rejects_too_many_columns():
-    d = make_decode_inputs((40, 50), 5, 8, 1, seed=1)  # 5 new tokens x 8 heads > 32 columns
+    d = make_decode_inputs((200, 250), 129, 8, 1, seed=1)  # 129 new tokens x 8 heads > 1024 columns
     say("decode: unsupported max_q * group")
     with pytest.raises(asa.AttnSinkError) as e:
         run_decode(d)
