@@ -68,14 +68,14 @@ KERNEL_FLOPS_PER_PAIR_D = {
 # (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch) scaled by what the same counters read for the
 # copy probe; valid only for kernel sources with the recorded digest.
 TRAFFIC = {
-    ("causal4k", "attn_sink_bwd_dkdv_kernel"): {"bytes": 146981480, "digest": "f3d498da4ea91067"},
-    ("window4k", "attn_sink_bwd_dkdv_kernel"): {"bytes": 106979536, "digest": "f3d498da4ea91067"},
-    ("window4k", "attn_sink_bwd_dq_kernel"): {"bytes": 213277939, "digest": "f3d498da4ea91067"},
-    ("varlen_window", "attn_sink_bwd_dkdv_kernel"): {"bytes": 1721671051, "digest": "f3d498da4ea91067"},
-    ("varlen_window", "attn_sink_bwd_dq_kernel"): {"bytes": 3790946667, "digest": "f3d498da4ea91067"},
-    ("band4k", "attn_sink_bwd_dkdv_kernel"): {"bytes": 126419728, "digest": "f3d498da4ea91067"},
-    ("band4k", "attn_sink_bwd_dq_kernel"): {"bytes": 213303058, "digest": "f3d498da4ea91067"},
-    ("decode32k", "attn_sink_decode_partial_kernel"): {"bytes": 368465214, "digest": "f3d498da4ea91067"},
+    ("causal4k", "attn_sink_bwd_dkdv_kernel"): {"bytes": 146899847, "digest": "beedb3e3d3ae39ef"},
+    ("window4k", "attn_sink_bwd_dkdv_kernel"): {"bytes": 106394479, "digest": "beedb3e3d3ae39ef"},
+    ("window4k", "attn_sink_bwd_dq_kernel"): {"bytes": 213271453, "digest": "beedb3e3d3ae39ef"},
+    ("varlen_window", "attn_sink_bwd_dkdv_kernel"): {"bytes": 1718894312, "digest": "beedb3e3d3ae39ef"},
+    ("varlen_window", "attn_sink_bwd_dq_kernel"): {"bytes": 3792490999, "digest": "beedb3e3d3ae39ef"},
+    ("band4k", "attn_sink_bwd_dkdv_kernel"): {"bytes": 126190898, "digest": "beedb3e3d3ae39ef"},
+    ("band4k", "attn_sink_bwd_dq_kernel"): {"bytes": 213320343, "digest": "beedb3e3d3ae39ef"},
+    ("decode32k", "attn_sink_decode_partial_kernel"): {"bytes": 368464234, "digest": "beedb3e3d3ae39ef"},
 }
 
 
