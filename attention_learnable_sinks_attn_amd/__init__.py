@@ -17,7 +17,8 @@ from typing import Optional, Sequence
 import torch
 
 __all__ = ["fwd", "bwd", "decode_fwd", "bwd_workspace_bytes", "decode_workspace_bytes", "bwd_kernel_names",
-           "decode_kernel_names", "library_path", "load_library", "AttnSinkError", "ERROR_CODES", "HEAD_DIM"]
+           "decode_kernel_names", "check_cu_seqlens", "library_path", "load_library", "AttnSinkError",
+           "ERROR_CODES", "HEAD_DIM"]
 
 HEAD_DIM = 64
 _PKG_DIR = os.path.dirname(os.path.abspath(__file__))
@@ -27,7 +28,7 @@ _lib = None
 ERROR_CODES = {
     0: "ATTN_SINK_OK", -1: "ATTN_SINK_ERR_NULL_PTR", -2: "ATTN_SINK_ERR_BAD_SHAPE",
     -3: "ATTN_SINK_ERR_UNSUPPORTED", -4: "ATTN_SINK_ERR_BAD_WINDOW", -5: "ATTN_SINK_ERR_WORKSPACE",
-    -6: "ATTN_SINK_ERR_HIP", -7: "ATTN_SINK_ERR_ALIGN",
+    -6: "ATTN_SINK_ERR_HIP", -7: "ATTN_SINK_ERR_ALIGN", -8: "ATTN_SINK_ERR_BAD_SEQLENS",
 }
 
 
@@ -90,6 +91,8 @@ def load_library() -> ctypes.CDLL:
     lib.attn_sink_decode_num_kernels.restype = i32
     lib.attn_sink_decode_kernel_name.argtypes = [i32]
     lib.attn_sink_decode_kernel_name.restype = ctypes.c_char_p
+    lib.attn_sink_check_cu_seqlens.argtypes = [vp, i32, i32, i32]
+    lib.attn_sink_check_cu_seqlens.restype = i32
     lib.attn_sink_strerror.argtypes = [i32]
     lib.attn_sink_strerror.restype = ctypes.c_char_p
     _lib = lib
@@ -131,19 +134,57 @@ def _stream(device: torch.device) -> int:
     return torch.cuda.current_stream(device).cuda_stream
 
 
+def _shape_of(t: torch.Tensor, name: str, shape):
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _check_qkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, sinks: torch.Tensor, cu_seqlens: torch.Tensor,
+               total_k: Optional[int] = None):
+    """Shapes the kernels assume (they trust every size): q [Tq, Hq, d], k / v [Tk, Hkv, d] with the
+    same d, Hq a multiple of Hkv, sinks [Hq], cu_seqlens 1-D with at least two entries."""
+    if q.dim() != 3 or k.dim() != 3:
+        raise ValueError(f"q and k must be 3-D [tokens, heads, head_dim], got {tuple(q.shape)} and {tuple(k.shape)}")
+    T, Hq, d = q.shape
+    Tk, Hkv = k.shape[0], k.shape[1]
+    if k.shape[2] != d:
+        raise ValueError(f"k has head_dim {k.shape[2]}, q has {d}")
+    if total_k is None and Tk != T:
+        raise ValueError(f"k has {Tk} tokens, q has {T}")
+    _shape_of(v, "v", k.shape)
+    if Hkv < 1 or Hq % Hkv:
+        raise ValueError(f"query heads ({Hq}) must be a multiple of KV heads ({Hkv})")
+    _shape_of(sinks, "sinks", (Hq,))
+    if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
+        raise ValueError(f"cu_seqlens must be 1-D with at least 2 entries, got {tuple(cu_seqlens.shape)}")
+
+
+def check_cu_seqlens(cu_seqlens: torch.Tensor, total_tokens: int, max_seqlen: int, what: str = "cu_seqlens"):
+    """Debug validation of packed-sequence offsets (copies them to the host, so it synchronises):
+    cu[0] = 0, non-decreasing, cu[-1] = total_tokens, every length <= max_seqlen. The kernels trust
+    these values; an understated max_seqlen would leave rows unwritten. Raises AttnSinkError."""
+    host = cu_seqlens.detach().to("cpu", torch.int32).contiguous()
+    rc = load_library().attn_sink_check_cu_seqlens(host.data_ptr(), int(host.numel()) - 1, int(total_tokens),
+                                                   int(max_seqlen))
+    if rc != 0:
+        raise AttnSinkError(rc, what)
+
+
 def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, sinks: torch.Tensor, cu_seqlens: torch.Tensor,
         max_seqlen: int, causal: bool = True, window: int = 0, softmax_scale: Optional[float] = None,
         out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-        out_dtype: torch.dtype = torch.float32):
+        out_dtype: torch.dtype = torch.float32, validate_seqlens: bool = False):
     """Forward. q [T,Hq,64], k/v [T,Hkv,64] bf16; sinks [Hq] fp32; cu_seqlens [B+1] int32 (device).
     Returns (out [T,Hq,64] in ``out_dtype`` (fp32, or bf16 for inference; the backward needs fp32),
-    lse [Hq,T] fp32)."""
+    lse [Hq,T] fp32). ``validate_seqlens`` checks cu_seqlens against T and max_seqlen on the host
+    first (a synchronising copy; see check_cu_seqlens)."""
     lib = load_library()
     dev = q.device
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _check(t, n, torch.bfloat16, dev)
     _check(sinks, "sinks", torch.float32, dev)
     _check(cu_seqlens, "cu_seqlens", torch.int32, dev)
+    _check_qkv(q, k, v, sinks, cu_seqlens)
     T, Hq, d = q.shape
     if out is None:
         out = torch.empty((T, Hq, d), dtype=out_dtype, device=dev)
@@ -151,6 +192,10 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, sinks: torch.Tensor, 
         lse = torch.empty((Hq, T), dtype=torch.float32, device=dev)
     _check(out, "out", out_dtype, dev)
     _check(lse, "lse", torch.float32, dev)
+    _shape_of(out, "out", (T, Hq, d))
+    _shape_of(lse, "lse", (Hq, T))
+    if validate_seqlens:
+        check_cu_seqlens(cu_seqlens, T, max_seqlen)
     shape = make_shape(q, k, cu_seqlens, max_seqlen, softmax_scale, out_dtype)
     rc = lib.attn_sink_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(sinks), int(bool(causal)), int(window), _ptr(cu_seqlens),
                            ctypes.byref(shape), _ptr(out), _ptr(lse), _stream(dev))
@@ -172,10 +217,11 @@ def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, sinks: torch.Tensor, 
         dout: torch.Tensor, cu_seqlens: torch.Tensor, max_seqlen: int, causal: bool = True, window: int = 0,
         softmax_scale: Optional[float] = None, dq: Optional[torch.Tensor] = None, dk: Optional[torch.Tensor] = None,
         dv: Optional[torch.Tensor] = None, dsinks: Optional[torch.Tensor] = None,
-        workspace: Optional[torch.Tensor] = None, events: Optional[Sequence[int]] = None):
+        workspace: Optional[torch.Tensor] = None, events: Optional[Sequence[int]] = None,
+        validate_seqlens: bool = False):
     """Backward. Returns (dq [T,Hq,64], dk [T,Hkv,64], dv [T,Hkv,64], dsinks [Hq]), all fp32.
     ``events``: optional raw hipEvent_t handles (num kernels + 1) recorded around each kernel; an
-    entry may be None (nothing recorded there)."""
+    entry may be None (nothing recorded there). ``validate_seqlens``: as in fwd."""
     lib = load_library()
     dev = q.device
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (dout, "dout")):
@@ -183,18 +229,30 @@ def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, sinks: torch.Tensor, 
     for t, n in ((sinks, "sinks"), (out, "out"), (lse, "lse")):
         _check(t, n, torch.float32, dev)
     _check(cu_seqlens, "cu_seqlens", torch.int32, dev)
+    _check_qkv(q, k, v, sinks, cu_seqlens)
     T, Hq, d = q.shape
     Hkv = k.shape[1]
+    _shape_of(out, "out", (T, Hq, d))
+    _shape_of(dout, "dout", (T, Hq, d))
+    _shape_of(lse, "lse", (Hq, T))
     dq = torch.empty((T, Hq, d), dtype=torch.float32, device=dev) if dq is None else dq
     dk = torch.empty((T, Hkv, d), dtype=torch.float32, device=dev) if dk is None else dk
     dv = torch.empty((T, Hkv, d), dtype=torch.float32, device=dev) if dv is None else dv
     dsinks = torch.empty((Hq,), dtype=torch.float32, device=dev) if dsinks is None else dsinks
     for t, n in ((dq, "dq"), (dk, "dk"), (dv, "dv"), (dsinks, "dsinks")):
         _check(t, n, torch.float32, dev)
+    _shape_of(dq, "dq", (T, Hq, d))
+    _shape_of(dk, "dk", (T, Hkv, d))
+    _shape_of(dv, "dv", (T, Hkv, d))
+    _shape_of(dsinks, "dsinks", (Hq,))
+    if validate_seqlens:
+        check_cu_seqlens(cu_seqlens, T, max_seqlen)
     shape = make_shape(q, k, cu_seqlens, max_seqlen, softmax_scale)
     need = int(lib.attn_sink_bwd_workspace_bytes(ctypes.byref(shape)))
     if workspace is None:
         workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
+    else:
+        _check(workspace, "workspace", workspace.dtype, dev)
     args = [_ptr(q), _ptr(k), _ptr(v), _ptr(sinks), _ptr(out), _ptr(lse), _ptr(dout), int(bool(causal)), int(window),
             _ptr(cu_seqlens), ctypes.byref(shape), _ptr(workspace), workspace.numel() * workspace.element_size(),
             _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dsinks), _stream(dev)]
@@ -233,11 +291,13 @@ def decode_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, sinks: torch.T
                cu_seqlens_k: torch.Tensor, max_q: int, max_k: int, window: int = 0,
                softmax_scale: Optional[float] = None, out_dtype: torch.dtype = torch.float32,
                out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-               workspace: Optional[torch.Tensor] = None, events: Optional[Sequence[int]] = None):
+               workspace: Optional[torch.Tensor] = None, events: Optional[Sequence[int]] = None,
+               validate_seqlens: bool = False):
     """Decode forward: q [Tq,Hq,64] (each sequence's last Nq_b tokens), k/v [Tk,Hkv,64] caches, bf16;
     sinks [Hq] fp32; cu_seqlens_q / cu_seqlens_k [B+1] int32 (device). Returns (out [Tq,Hq,64] in
     ``out_dtype``, lse [Hq,Tq] fp32). ``events``: optional raw hipEvent_t handles (num kernels + 1)
-    recorded around each kernel; an entry may be None (nothing recorded there)."""
+    recorded around each kernel; an entry may be None (nothing recorded there).
+    ``validate_seqlens``: check both offset arrays on the host first (see check_cu_seqlens)."""
     lib = load_library()
     dev = q.device
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
@@ -245,6 +305,9 @@ def decode_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, sinks: torch.T
     _check(sinks, "sinks", torch.float32, dev)
     _check(cu_seqlens_q, "cu_seqlens_q", torch.int32, dev)
     _check(cu_seqlens_k, "cu_seqlens_k", torch.int32, dev)
+    _check_qkv(q, k, v, sinks, cu_seqlens_q, total_k=int(k.shape[0]))
+    if cu_seqlens_k.shape != cu_seqlens_q.shape:
+        raise ValueError(f"cu_seqlens_k {tuple(cu_seqlens_k.shape)} and cu_seqlens_q {tuple(cu_seqlens_q.shape)} differ")
     Tq, Hq, d = q.shape
     if out is None:
         out = torch.empty((Tq, Hq, d), dtype=out_dtype, device=dev)
@@ -252,10 +315,17 @@ def decode_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, sinks: torch.T
         lse = torch.empty((Hq, Tq), dtype=torch.float32, device=dev)
     _check(out, "out", out_dtype, dev)
     _check(lse, "lse", torch.float32, dev)
+    _shape_of(out, "out", (Tq, Hq, d))
+    _shape_of(lse, "lse", (Hq, Tq))
+    if validate_seqlens:
+        check_cu_seqlens(cu_seqlens_q, Tq, max_q, "cu_seqlens_q")
+        check_cu_seqlens(cu_seqlens_k, int(k.shape[0]), max_k, "cu_seqlens_k")
     shape = make_decode_shape(q, k, cu_seqlens_q, max_q, max_k, softmax_scale, out_dtype)
     need = int(lib.attn_sink_decode_workspace_bytes(ctypes.byref(shape)))
     if workspace is None:
         workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
+    else:
+        _check(workspace, "workspace", workspace.dtype, dev)
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(sinks), int(window), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k),
             ctypes.byref(shape), _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(out), _ptr(lse),
             _stream(dev))

@@ -348,6 +348,17 @@ const char* attn_sink_decode_kernel_name(int i) {
   return (i >= 0 && i < kDecodeNumKernels) ? names[i] : nullptr;
 }
 
+int attn_sink_check_cu_seqlens(const int32_t* cu, int32_t num_seqs, int32_t total_tokens, int32_t max_seqlen) {
+  if (cu == nullptr) return ATTN_SINK_ERR_NULL_PTR;
+  if (num_seqs < 1 || total_tokens < 0 || max_seqlen < 0) return ATTN_SINK_ERR_BAD_SHAPE;
+  if (cu[0] != 0 || cu[num_seqs] != total_tokens) return ATTN_SINK_ERR_BAD_SEQLENS;
+  for (int32_t b = 0; b < num_seqs; ++b) {
+    const int64_t len = (int64_t)cu[b + 1] - cu[b];
+    if (len < 0 || len > max_seqlen) return ATTN_SINK_ERR_BAD_SEQLENS;
+  }
+  return ATTN_SINK_OK;
+}
+
 int attn_sink_bwd_num_kernels(void) { return kBwdNumKernels; }
 
 const char* attn_sink_bwd_kernel_name(int i) {
@@ -366,6 +377,8 @@ const char* attn_sink_strerror(int code) {
     case ATTN_SINK_ERR_WORKSPACE: return "workspace missing or smaller than attn_sink_bwd_workspace_bytes()";
     case ATTN_SINK_ERR_HIP: return "a HIP launch failed";
     case ATTN_SINK_ERR_ALIGN: return "a tensor base pointer is not 16-byte aligned";
+    case ATTN_SINK_ERR_BAD_SEQLENS:
+      return "cu_seqlens: not 0 at the start, decreasing, not ending at total_tokens, or a length above max_seqlen";
     default: return "unknown error code";
   }
 }

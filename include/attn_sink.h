@@ -66,7 +66,8 @@ enum {
   ATTN_SINK_ERR_BAD_WINDOW = -4,  /* window < 0 (attn_sink_decode_fwd only) */
   ATTN_SINK_ERR_WORKSPACE = -5,   /* workspace NULL or smaller than attn_sink_bwd_workspace_bytes() */
   ATTN_SINK_ERR_HIP = -6,         /* a HIP launch failed (hipGetLastError after the launch) */
-  ATTN_SINK_ERR_ALIGN = -7        /* a tensor base pointer is not 16-byte aligned */
+  ATTN_SINK_ERR_ALIGN = -7,       /* a tensor base pointer is not 16-byte aligned */
+  ATTN_SINK_ERR_BAD_SEQLENS = -8  /* attn_sink_check_cu_seqlens: offsets inconsistent with the shape */
 };
 
 enum { ATTN_SINK_F32 = 0, ATTN_SINK_BF16 = 1 };
@@ -183,6 +184,23 @@ int attn_sink_decode_fwd_timed(const void* q, const void* k, const void* v, cons
                                float* lse, hipStream_t stream, void* const* events, int num_events);
 int attn_sink_decode_num_kernels(void);
 const char* attn_sink_decode_kernel_name(int i);
+
+/*
+ * Optional host-side validation of sequence offsets, for callers that cannot vouch for them.
+ * The kernels trust cu_seqlens (it lives on the device): a max_seqlen below the longest sequence
+ * leaves that sequence's later rows unwritten (the grid is sized from it), and offsets that are
+ * not non-decreasing or that run past T make the kernels read and write outside the tensors.
+ * This check takes a HOST copy of the offsets, cu_seqlens_host[0 .. num_seqs], and returns
+ * ATTN_SINK_OK when cu[0] = 0, cu[b] <= cu[b+1] for every b, cu[num_seqs] = total_tokens and
+ * every length cu[b+1] - cu[b] <= max_seqlen; ATTN_SINK_ERR_NULL_PTR for a NULL array,
+ * ATTN_SINK_ERR_BAD_SHAPE for num_seqs < 1, total_tokens < 0 or max_seqlen < 0, and
+ * ATTN_SINK_ERR_BAD_SEQLENS otherwise. For the decode forward, check cu_seqlens_q (total_q,
+ * max_q) and cu_seqlens_k (total_k, max_k) separately. Pure host code: no HIP call, no
+ * allocation, thread-safe. (The packing it describes: nmedialink.com "惊爆！GPT-OSS-20B强化学习…",
+ * section "结合Flash Attention V3的序列并行技术", padding removed and sequences concatenated.)
+ */
+int attn_sink_check_cu_seqlens(const int32_t* cu_seqlens_host, int32_t num_seqs, int32_t total_tokens,
+                               int32_t max_seqlen);
 
 /* Number of kernels attn_sink_bwd enqueues, and the name of kernel i (static string, or NULL). */
 int attn_sink_bwd_num_kernels(void);

@@ -135,6 +135,18 @@ def make_workload_inputs(name: str, seed: int = 0) -> Inputs:
     return inp
 
 
+def input_digest(inp: Inputs) -> str:
+    """sha256 (first 32 hex digits) over the exact bytes of q, k, v, dout, sinks and cu_seqlens, so
+    that a stored reference is only used for the inputs it was computed from."""
+    import hashlib
+    h = hashlib.sha256()
+    for t in (inp.q, inp.k, inp.v, inp.dout, inp.sinks, inp.cu_seqlens):
+        t = t.detach().contiguous().cpu()
+        h.update(str(t.dtype).encode() + str(tuple(t.shape)).encode())
+        h.update(t.view(torch.uint8).numpy().tobytes())
+    return h.hexdigest()[:32]
+
+
 def visible_pairs(lengths, causal: bool, window: int) -> int:
     """Number of (query, key) pairs a query may attend to, summed over sequences (one head)."""
     total = 0
