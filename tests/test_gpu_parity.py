@@ -7,7 +7,9 @@ Small cases compare every element; they span several 64-row / 64-key tiles and e
 tails. The full-size GPT-OSS-shaped workloads run in the same launch configuration the bench
 times and are compared on sampled rows, keys and heads that the oracle evaluates one by one.
 """
+import json
 import math
+import os
 import sys
 
 import numpy as np
@@ -16,7 +18,7 @@ import torch
 
 import attention_learnable_sinks_attn_amd as asa
 import oracle
-from workloads import make_inputs, make_workload_inputs
+from workloads import input_digest, make_inputs, make_workload_inputs
 
 pytestmark = pytest.mark.gpu
 
@@ -109,6 +111,12 @@ SMALL_CASES = {
     "band_int_max": ((97, 33), 2, 1, False, 2**31 - 1, {}),
     "band_neg_inf_sinks": ((200, 63), 4, 2, False, 20, {"sinks": [-math.inf] * 4}),
     "band_exact_tiles": ((256, 128), 8, 8, False, 64, {}),
+    # Enough (sequence, key block, KV head) triples that the dK/dV pass keeps each KV group's query
+    # heads in one workgroup (two head streams, dK/dV written directly): 512 or more with a window,
+    # 2048 or more without. Both reach that with 8 KV heads and 64 or 256 short sequences.
+    "one_half_window": (tuple(int(x) for x in np.random.default_rng(3).integers(1, 130, 64)), 16, 8, True, 32, {}),
+    "one_half_causal": (tuple(int(x) for x in np.random.default_rng(4).integers(1, 65, 256)), 16, 8, True, 0, {}),
+    "one_half_band": (tuple(int(x) for x in np.random.default_rng(5).integers(1, 130, 64)), 16, 8, False, 20, {}),
 }
 
 
@@ -146,8 +154,83 @@ def test_backward_is_deterministic():
 
 
 # ---------------------------------------------------------------------------------------------
-# Full-size workloads: the bench's launch configuration, checked on sampled outputs.
+# Full-size workloads, in the launch configuration the bench times.
+#  * causal4k, window4k, band4k, varlen_window: every element of every output against the whole
+#    oracle (seconds of fp64 CPU work);
+#  * varlen_causal, long32k: every element of one whole KV group (its 8 query heads' O, LSE, dQ and
+#    dSink, every key of its dK and dV, key block 0 included, whose sums run over every row of the
+#    sequence), and dSink of all 64 heads against stored oracle values (tests/golden,
+#    make_dsink_golden.py), since a head's dSink needs that head's softmax over every row.
 # ---------------------------------------------------------------------------------------------
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _oracle_row_block(inp):
+    # With a window, row blocks of 256 keep the oracle's key range per block near the window; the
+    # arithmetic of each row is the same for any blocking.
+    return 256 if inp.window > 0 else 1024
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", ["causal4k", "window4k", "band4k", "varlen_window"])
+def test_full_size_every_element(name):
+    inp = make_workload_inputs(name)
+    say(f"[gpu] full-size workload {name}, every element: T={inp.total_tokens} B={len(inp.lengths)} "
+        f"window={inp.window}")
+    g = run_gpu(inp)
+    rb = _oracle_row_block(inp)
+    dq, dk, dv, ds, out, lse = oracle.backward(inp.q, inp.k, inp.v, inp.sinks, inp.dout, inp.cu_seqlens,
+                                               inp.causal, inp.window, row_block=rb, return_forward=True)
+    compare_all(g, {"out": out, "lse": lse, "dq": dq, "dk": dk, "dv": dv}, ds)
+
+
+def compare_all(g, ref, ds_ref, heads=None, kv_heads=None):
+    """Every element of the GPU outputs (restricted to `heads` / `kv_heads` when given) against the
+    oracle's."""
+    sel = {"out": heads, "dq": heads, "lse": heads, "dk": kv_heads, "dv": kv_heads}
+    for name, r in ref.items():
+        t = g[name]
+        idx = sel[name]
+        if idx is not None:
+            ix = torch.tensor(idx, device=t.device)
+            t = t.index_select(0 if name == "lse" else 1, ix)
+        x = t.double().cpu().numpy()
+        assert np.isfinite(x).all(), f"{name} has non-finite values"
+        err = maxabs(x, r)
+        say(f"  {name} {tuple(x.shape)}: max-abs err {err:.3e} (max |ref| {np.abs(r).max() if r.size else 0:.3f})")
+        assert err <= TOL[name], f"{name}: max-abs err {err:.3e} > {TOL[name]}"
+    got = g["dsinks"].double().cpu().numpy()
+    check_dsink(got if heads is None else got[heads], ds_ref, heads, label="" if heads is None else f" {heads}")
+
+
+def load_golden_dsink(name, inp):
+    path = os.path.join(GOLDEN, f"dsink_{name}_seed0.json")
+    with open(path) as f:
+        rec = json.load(f)
+    assert rec["input_digest"] == input_digest(inp), f"{path} was computed from other inputs"
+    return np.array(rec["dsink"], dtype=np.float64), np.array(rec["abs_terms"], dtype=np.float64)
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", ["varlen_causal", "long32k"])
+def test_full_size_one_kv_group(name):
+    inp = make_workload_inputs(name)
+    Hq, Hkv = inp.q.shape[1], inp.k.shape[1]
+    G = Hq // Hkv
+    grp = int(np.random.default_rng(11).integers(0, Hkv))
+    heads = list(range(grp * G, (grp + 1) * G))
+    say(f"[gpu] full-size workload {name}: T={inp.total_tokens} B={len(inp.lengths)}; every element of KV group "
+        f"{grp} (query heads {heads[0]}..{heads[-1]}), dSink of all {Hq} heads")
+    g = run_gpu(inp)
+    dq, dk, dv, ds, out, lse = oracle.backward(inp.q[:, heads], inp.k[:, grp:grp + 1], inp.v[:, grp:grp + 1],
+                                               inp.sinks[heads], inp.dout[:, heads], inp.cu_seqlens, inp.causal,
+                                               inp.window, return_forward=True)
+    compare_all(g, {"out": out, "lse": lse, "dq": dq, "dk": dk, "dv": dv}, ds, heads=heads, kv_heads=[grp])
+    ref, terms = load_golden_dsink(name, inp)
+    check_dsink(g["dsinks"].double().cpu().numpy(), ref, list(range(Hq)), label=" (all heads, stored oracle values)")
+    say(f"  dsinks: condition number sum|terms|/|sum| up to {np.max(terms / np.abs(ref)):.1f}")
+
 
 def _sample_rows(cu, rng, n):
     T = int(cu[-1])
@@ -174,13 +257,6 @@ def _sample_keys(cu, causal, window, rng, n):
     if len(keys) > n:
         keys = sorted(rng.choice(keys, size=n, replace=False).tolist())
     return keys
-
-
-@pytest.mark.parametrize("name", ["causal4k", "window4k", "varlen_causal", "varlen_window", "long32k", "band4k"])
-def test_full_size_sampled(name):
-    inp = make_workload_inputs(name)
-    say(f"[gpu] full-size workload {name}: T={inp.total_tokens} B={len(inp.lengths)} window={inp.window}")
-    check_sampled(inp, run_gpu(inp))
 
 
 def test_longest_sequence_131072_sampled():
