@@ -16,6 +16,9 @@ ROOT = os.path.dirname(PKG_DIR)
 CSRC = os.path.join(PKG_DIR, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG_DIR, "libattn_sink.so")
+# The benchmark's matrix-core throughput probe, a library of its own (the attention path never loads it).
+PROBE_LIB_PATH = os.path.join(PKG_DIR, "libattn_sink_probe.so")
+PROBE_SOURCES = ("probe.hip",)
 BUILD_DIR = os.path.join(ROOT, "_build")
 SOURCES = ("fwd.hip", "bwd.hip", "decode.hip", "api.hip")
 ARCH = "gfx950"
@@ -45,21 +48,21 @@ def _run(cmd):
 def build_library(verbose: bool = False) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
     cc = hipcc()
-    objs = []
     jobs = []
-    for src in SOURCES:
+    for src in SOURCES + PROBE_SOURCES:
         obj = os.path.join(BUILD_DIR, src.replace(".hip", ".o"))
-        objs.append(obj)
         jobs.append([cc, *compile_flags(), "-c", os.path.join(CSRC, src), "-o", obj])
     with concurrent.futures.ThreadPoolExecutor(max_workers=len(jobs)) as ex:
         for out in ex.map(_run, jobs):
             if verbose and out.strip():
                 print(out)
-    tmp = LIB_PATH + ".tmp"
-    _run([cc, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp, *objs])
-    os.replace(tmp, LIB_PATH)
-    if verbose:
-        print("built", LIB_PATH)
+    for path, srcs in ((LIB_PATH, SOURCES), (PROBE_LIB_PATH, PROBE_SOURCES)):
+        objs = [os.path.join(BUILD_DIR, src.replace(".hip", ".o")) for src in srcs]
+        tmp = path + ".tmp"
+        _run([cc, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp, *objs])
+        os.replace(tmp, path)
+        if verbose:
+            print("built", path)
     return LIB_PATH
 
 

@@ -16,11 +16,18 @@ algorithmic HBM GB/s (q, every cached K/V row a new token sees, out and LSE, eac
 Prints one JSON line. ``value`` is algorithmic TFLOP/s over the timed steps: 4*d FLOPs per visible
 (query, key, head) in the forward (QK^T and PV) plus 10*d in the backward (S, dP, dV, dK, dQ);
 recomputation and masked tile work are not counted. ``roofline`` describes the kernel with the
-largest share of the step time (in the per-kernel breakdown ``kernel_ms``, taken with events around
-every kernel in the last warm-up steps), timed with HIP events recorded around it, on the stream
-the kernels run on, in every timed step: against the bf16 MFMA peak for the causal workloads, and against HBM bandwidth (algorithmic bytes:
-each tensor the kernel needs read or written once at its ABI dtype) for the banded window ones.
-``cpu_baseline`` times the fp64 CPU oracle on a bounded sample of the same workload.
+largest share of the step time (in the per-kernel breakdown ``kernel_ms``, taken in a pass between
+the warm-up and the timed steps, each of its steps with events around one kernel only), timed with
+HIP events recorded around it, on the stream the kernels run on, in every timed step: against the
+bf16 MFMA peak for the causal workloads, and against HBM bandwidth (algorithmic bytes: each tensor
+the kernel needs read or written once at its ABI dtype) for the banded window ones.
+``measured_peaks`` gives a bf16 GEMM's and a device copy's rates on the same GPU, measured after the
+timed steps, beside the spec peaks. ``cpu_baseline`` times the fp64 CPU oracle on a bounded sample
+of the same workload (with the host's CPU model and core count).
+
+``--table`` times every training workload instead (forward and backward separately, median of
+``--steps``) and prints one JSON line per workload with the max errors of that run against the
+oracle and the oracle's time.
 
 Each HIP event record costs about 3 us of GPU time on MI355X; events around every kernel of every
 timed step added about 2.5% to a 4k step (and 10% to a decode call), so the timed steps carry only
@@ -161,9 +168,11 @@ def cpu_baseline(inp, w, max_heads_kv: int):
     oracle.backward(q, k, v, sinks, dout, inp.cu_seqlens, inp.causal, inp.window, return_forward=True)
     dt = time.perf_counter() - t0
     flops = visible_pairs(inp.lengths, inp.causal, inp.window) * hq_s * 14 * w.d
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{w.name}: all {inp.total_tokens} rows of {max_heads_kv} KV group(s) ({hq_s} query heads), "
-                      f"fwd+bwd in fp64 numpy, {dt:.2f} s"}
+    res = {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+           "sample": f"{w.name}: all {inp.total_tokens} rows of {max_heads_kv} KV group(s) ({hq_s} query heads), "
+                     f"fwd+bwd in fp64 numpy, {dt:.2f} s"}
+    res.update(cpu_info())
+    return res
 
 
 def decode_bytes(d, hq: int, hkv: int, out_bytes: int):
@@ -180,63 +189,128 @@ def decode_bytes(d, hq: int, hkv: int, out_bytes: int):
             "attn_sink_decode_combine_kernel": tq * hq * 64 * out_bytes + hq * tq * 4}
 
 
-BREAKDOWN_STEPS = 10  # last warm-up steps that carry events around every kernel
+BREAKDOWN_STEPS = 5  # steps per kernel in the breakdown pass
 
 
-def breakdown_source(warmup: int) -> str:
-    return f"the last {min(BREAKDOWN_STEPS, warmup)} warm-up steps" if warmup > 0 else "the timed steps"
+def breakdown_source(n_kernels: int) -> str:
+    return (f"a pass of {n_kernels} x {BREAKDOWN_STEPS} steps after the timed steps, step j with events "
+            f"around kernel j % {n_kernels} only")
 
 
 def run_timed(step, names, hip, warmup: int, steps: int):
-    """Warm-up, then exactly `steps` timed steps.
+    """`warmup` untimed steps; a short pass that picks the dominant kernel; exactly `steps` timed
+    steps; then the breakdown pass.
 
     step(evs) runs one step; evs is None or a list of len(names) + 1 event handles (entries may be
     None), entry i recorded before kernel i and the last after the last kernel. Each event record
-    costs about 3 us of GPU time, so only the last BREAKDOWN_STEPS warm-up steps carry events
-    around every kernel (the per-kernel breakdown and the choice of the dominant kernel), and the
-    timed steps carry just the two around the dominant kernel, whose average duration over the
-    timed steps is its measured launch time. Returns (ms per step, wall seconds of the timed
-    steps, per-kernel ms, dominant kernel, its ms over the timed steps)."""
+    costs about 3 us of GPU time, so no step carries more than two. The picking pass (2 steps per
+    kernel) and the breakdown pass after the timed steps (BREAKDOWN_STEPS per kernel) time kernel
+    j % n in their step j, with events around that kernel alone, so every kernel's samples spread
+    over the whole pass. Each timed step carries the two events around the dominant kernel, whose
+    average over the timed steps is its measured launch time. Returns (ms per step, wall seconds of
+    the timed steps, per-kernel ms from the breakdown pass, dominant kernel, its ms over the timed
+    steps)."""
     n = len(names)
-    bd = min(BREAKDOWN_STEPS, warmup)
-    full = [[hip.event() for _ in range(n + 1)] for _ in range(bd)]
-    for w in range(warmup):
-        j = w - (warmup - bd)
-        step(full[j] if j >= 0 else None)
-    torch.cuda.synchronize()
-    per_kernel = {nm: sum(hip.elapsed_ms(full[j][i], full[j][i + 1]) for j in range(bd)) / max(bd, 1)
-                  for i, nm in enumerate(names)}
-    if bd > 0:
-        dom = max(per_kernel, key=per_kernel.get)
-        di = names.index(dom)
-        timed = [[hip.event(), hip.event()] for _ in range(steps)]
 
-        def evs_for(st):
-            e = [None] * (n + 1)
-            e[di], e[di + 1] = timed[st]
-            return e
-    else:  # no warm-up to take the breakdown from: the timed steps carry every event
-        timed = [[hip.event() for _ in range(n + 1)] for _ in range(steps)]
+    def evs_around(i, pair):
+        e = [None] * (n + 1)
+        e[i], e[i + 1] = pair
+        return e
 
-        def evs_for(st):
-            return timed[st]
+    def rotating_pass(per_kernel_steps):
+        pairs = [(hip.event(), hip.event()) for _ in range(n * per_kernel_steps)]
+        for j, pair in enumerate(pairs):
+            step(evs_around(j % n, pair))
+        torch.cuda.synchronize()
+        return {nm: sum(hip.elapsed_ms(*pairs[j]) for j in range(i, len(pairs), n)) / per_kernel_steps
+                for i, nm in enumerate(names)}
+
+    for _ in range(warmup):
+        step(None)
+    pick = rotating_pass(2)
+    dom = max(pick, key=pick.get)
+    di = names.index(dom)
+    timed = [(hip.event(), hip.event()) for _ in range(steps)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     start.record()
-    for st in range(steps):
-        step(evs_for(st))
+    for pair in timed:
+        step(evs_around(di, pair))
     end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = start.elapsed_time(end) / steps
-    if bd > 0:
-        dom_ms = sum(hip.elapsed_ms(a, b) for a, b in timed) / steps
-    else:
-        per_kernel = {nm: sum(hip.elapsed_ms(timed[st][i], timed[st][i + 1]) for st in range(steps)) / steps
-                      for i, nm in enumerate(names)}
-        dom = max(per_kernel, key=per_kernel.get)
-        dom_ms = per_kernel[dom]
+    dom_ms = sum(hip.elapsed_ms(a, b) for a, b in timed) / steps
+    per_kernel = rotating_pass(BREAKDOWN_STEPS)
     return ms_step, wall, per_kernel, dom, dom_ms
+
+
+def cpu_info() -> dict:
+    """Host CPU model and the cores this process may run on."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:  # pragma: no cover
+        pass
+    return {"cpu_model": model, "host_cores": len(os.sched_getaffinity(0))}
+
+
+def measured_peaks(dev) -> dict:
+    """Practical ceilings on this GPU, beside the spec peaks: a bf16 GEMM (torch.matmul, 8192^3,
+    median of 10) and a device-to-device copy of 1 GiB (read + write bytes, median of 10)."""
+    def median_ms(fn, reps=10):
+        ts = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b))
+        return sorted(ts)[len(ts) // 2]
+
+    n = 8192
+    x = torch.randn((n, n), dtype=torch.bfloat16, device=dev)
+    y = torch.randn((n, n), dtype=torch.bfloat16, device=dev)
+    z = torch.empty((n, n), dtype=torch.bfloat16, device=dev)
+    for _ in range(3):
+        torch.matmul(x, y, out=z)
+    gemm_ms = median_ms(lambda: torch.matmul(x, y, out=z))
+    del x, y, z
+    src = torch.empty((1 << 28,), dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    copy_ms = median_ms(lambda: dst.copy_(src))
+    nbytes = src.numel() * 4
+    del src, dst
+    torch.cuda.synchronize()
+    res = {"bf16_gemm_tflops": round(2 * n ** 3 / (gemm_ms * 1e-3) / 1e12, 1),
+           "copy_gbs": round(2 * nbytes / (copy_ms * 1e-3) / 1e9, 1)}
+    probe = os.path.join(ROOT, "attention_learnable_sinks_attn_amd", "libattn_sink_probe.so")
+    how = "torch.matmul bf16 8192x8192x8192 and a 1 GiB device copy"
+    if os.path.exists(probe):
+        lib = ctypes.CDLL(probe)
+        lib.attn_sink_probe_mfma.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+        lib.attn_sink_probe_mfma.restype = ctypes.c_int
+        blocks, iters = 2048, 4000
+        buf = torch.empty((blocks * 256,), dtype=torch.float32, device=dev)
+        stream = torch.cuda.current_stream(dev).cuda_stream
+
+        def run_probe():
+            if lib.attn_sink_probe_mfma(buf.data_ptr(), blocks, iters, stream) != 0:
+                raise RuntimeError("MFMA probe launch failed")
+
+        run_probe()
+        probe_ms = median_ms(run_probe)
+        res["bf16_mfma_loop_tflops"] = round(blocks * 4 * iters * 8 * 32768 / (probe_ms * 1e-3) / 1e12, 1)
+        how += ", and a register-only loop of 32x32x16 bf16 MFMAs on every SIMD (libattn_sink_probe.so)"
+        del buf
+    res["how"] = how + "; median of 10 each"
+    return res
 
 
 def bench_decode(args):
@@ -279,7 +353,8 @@ def bench_decode(args):
                    "seed": args.seed, "parallelism": "none (1 GPU)"},
         "tokens_per_s": round(Tq / (ms_step * 1e-3), 1),
         "kernel_ms": {n: round(t, 4) for n, t in per_kernel.items()},
-        "kernel_ms_from": breakdown_source(args.warmup),
+        "kernel_ms_from": breakdown_source(len(names)),
+        "kernel_ms_sum": round(sum(per_kernel.values()), 4),
         "wall_s_timed": round(wall, 4),
         "roofline": roofline,
     }
@@ -291,6 +366,7 @@ def bench_decode(args):
         res["cpu_baseline"] = {"value": round(total / dt / 1e9, 3), "unit": "GB/s", "cores": _oracle_threads(),
                                "kind": "oracle", "sample": f"{args.workload}: the whole batch ({B} sequences, "
                                                            f"{Tq} new tokens) in fp64 numpy, {dt:.2f} s"}
+        res["cpu_baseline"].update(cpu_info())
     print(json.dumps(res), flush=True)
 
 
@@ -304,6 +380,11 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-kv-groups", type=int, default=8)
     ap.add_argument("--copy-probe-mib", type=int, default=0)
+    ap.add_argument("--no-peaks", action="store_true", help="skip the GEMM / copy ceiling measurements")
+    ap.add_argument("--table", action="store_true",
+                    help="results table: every training workload, t_fwd and t_bwd (median of --steps), max "
+                         "errors and oracle time (one JSON line per workload)")
+    ap.add_argument("--table-workloads", nargs="+", default=[w for w in WORKLOAD_NAMES])
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
@@ -319,6 +400,9 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    if args.table:
+        bench_table(args)
+        return
     if args.workload in DECODE_WORKLOADS:
         bench_decode(args)
         return
@@ -380,13 +464,133 @@ def main():
                    "seed": args.seed, "parallelism": "none (1 GPU)"},
         "pct_mfma_peak": round(100 * tflops / MFMA_BF16_PEAK_TFLOPS, 2),
         "kernel_ms": {n: round(t, 4) for n, t in per_kernel.items()},
-        "kernel_ms_from": breakdown_source(args.warmup),
+        "kernel_ms_from": breakdown_source(len(names)),
+        "kernel_ms_sum": round(sum(per_kernel.values()), 4),
         "wall_s_timed": round(wall, 4),
         "roofline": roofline,
     }
+    if not args.no_peaks:  # after the timed steps, so that they do not change the clocks those ran at
+        peaks = measured_peaks(dev)
+        res["measured_peaks"] = peaks
+        if roofline["bound"] == "mfma":
+            ceiling = peaks.get("bf16_mfma_loop_tflops", peaks["bf16_gemm_tflops"])
+            roofline["frac_of_measured_peak"] = round(roofline["achieved"] / ceiling, 4)
+        else:
+            roofline["frac_of_measured_peak"] = round(roofline["achieved"] / peaks["copy_gbs"], 4)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(inp, w, args.cpu_kv_groups)
     print(json.dumps(res), flush=True)
+
+
+# ---- results table: every training workload, forward and backward timed separately ----------
+
+def step_bytes(T: int, hq: int, hkv: int, d: int):
+    """Algorithmic HBM bytes of a forward and of a backward: each tensor once at its ABI dtype
+    (bf16 q, k, v, dO; fp32 O, LSE, dQ, dK, dV; the D workspace written and read once)."""
+    q = T * hq * d * 2
+    kv = 2 * T * hkv * d * 2
+    rows = hq * T * 4
+    o32 = T * hq * d * 4
+    fwd = q + kv + o32 + rows
+    bwd = 2 * q + kv + o32 + rows + o32 + 2 * T * hkv * d * 4 + 2 * rows
+    return fwd, bwd
+
+
+def oracle_leg(name, inp):
+    """The cpu_baseline leg of the table: the fp64 oracle, timed, on the same inputs; its results
+    also give the run's max errors. The whole oracle for the shorter workloads; one KV group (and
+    dSink of every head from the stored oracle values in tests/golden) for varlen_causal and
+    long32k, whose whole oracle takes minutes."""
+    import numpy as np
+    import oracle
+    from workloads import input_digest
+    Hq, Hkv = inp.q.shape[1], inp.k.shape[1]
+    G = Hq // Hkv
+    rb = 256 if inp.window > 0 else 1024
+    if name in ("varlen_causal", "long32k"):
+        grp = int(np.random.default_rng(11).integers(0, Hkv))
+        heads = list(range(grp * G, (grp + 1) * G))
+        t0 = time.perf_counter()
+        r = oracle.backward(inp.q[:, heads], inp.k[:, grp:grp + 1], inp.v[:, grp:grp + 1], inp.sinks[heads],
+                            inp.dout[:, heads], inp.cu_seqlens, inp.causal, inp.window, row_block=rb,
+                            return_forward=True)
+        dt = time.perf_counter() - t0
+        with open(os.path.join(ROOT, "tests", "golden", f"dsink_{name}_seed0.json")) as f:
+            gold = json.load(f)
+        assert gold["input_digest"] == input_digest(inp)
+        scope = f"KV group {grp} of {Hkv} (fwd+bwd); dSink of all heads from tests/golden"
+        return r, dt, scope, heads, [grp], np.array(gold["dsink"])
+    t0 = time.perf_counter()
+    r = oracle.backward(inp.q, inp.k, inp.v, inp.sinks, inp.dout, inp.cu_seqlens, inp.causal, inp.window,
+                        row_block=rb, return_forward=True)
+    return r, time.perf_counter() - t0, "whole workload (fwd+bwd)", None, None, None
+
+
+def bench_table(args):
+    import numpy as np
+    dev = torch.device("cuda:0")
+    rows = []
+    for name in args.table_workloads:
+        inp = make_workload_inputs(name, args.seed)
+        q, k, v, dout = (t.to(dev) for t in (inp.q, inp.k, inp.v, inp.dout))
+        sinks, cu = inp.sinks.to(dev), inp.cu_seqlens.to(dev)
+        T, Hq, d = q.shape
+        Hkv = k.shape[1]
+        out = torch.empty((T, Hq, d), dtype=torch.float32, device=dev)
+        lse = torch.empty((Hq, T), dtype=torch.float32, device=dev)
+        dq, dk = torch.empty_like(out), torch.empty((T, Hkv, d), dtype=torch.float32, device=dev)
+        dv, ds = torch.empty_like(dk), torch.empty((Hq,), dtype=torch.float32, device=dev)
+        ws = torch.empty((asa.bwd_workspace_bytes(q, k, cu, inp.max_seqlen),), dtype=torch.uint8, device=dev)
+
+        def f():
+            asa.fwd(q, k, v, sinks, cu, inp.max_seqlen, inp.causal, inp.window, out=out, lse=lse)
+
+        def b():
+            asa.bwd(q, k, v, sinks, out, lse, dout, cu, inp.max_seqlen, inp.causal, inp.window, dq=dq, dk=dk, dv=dv,
+                    dsinks=ds, workspace=ws)
+
+        for _ in range(args.warmup):
+            f()
+            b()
+        tf, tb = [], []
+        for _ in range(args.steps):
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            e[0].record()
+            f()
+            e[1].record()
+            b()
+            e[2].record()
+            torch.cuda.synchronize()
+            tf.append(e[0].elapsed_time(e[1]))
+            tb.append(e[1].elapsed_time(e[2]))
+        t_fwd, t_bwd = float(np.median(tf)), float(np.median(tb))
+        pairs = visible_pairs(inp.lengths, inp.causal, inp.window) * Hq
+        bf, bb = step_bytes(T, Hq, Hkv, d)
+        total_ms = t_fwd + t_bwd
+        row = {"workload": name, "tokens": int(T), "seqs": len(inp.lengths), "causal": inp.causal,
+               "window": inp.window, "reps": args.steps, "t_fwd_ms": round(t_fwd, 4), "t_bwd_ms": round(t_bwd, 4),
+               "tflops": round(pairs * 14 * d / (total_ms * 1e-3) / 1e12, 2),
+               "pct_mfma_peak": round(100 * pairs * 14 * d / (total_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 2),
+               "gbs": round((bf + bb) / (total_ms * 1e-3) / 1e9, 1),
+               "pct_hbm_peak": round(100 * (bf + bb) / (total_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2)}
+        if not args.no_cpu_baseline:
+            (rdq, rdk, rdv, rds, ro, rl), dt, scope, heads, kvh, gold_ds = oracle_leg(name, inp)
+            hsel = slice(None) if heads is None else heads
+            ksel = slice(None) if kvh is None else kvh
+            errs = {}
+            for nm, t, r in (("out", out[:, hsel], ro), ("dq", dq[:, hsel], rdq), ("dk", dk[:, ksel], rdk),
+                             ("dv", dv[:, ksel], rdv), ("lse", lse[hsel], rl)):
+                errs[nm] = float(np.max(np.abs(t.double().cpu().numpy() - r)))
+            got_ds = ds.double().cpu().numpy()
+            ref_ds = gold_ds if gold_ds is not None else rds
+            errs["dsink_rel_max"] = float(np.max(np.abs(got_ds - ref_ds) / np.abs(ref_ds)))
+            row["max_err"] = {n_: float(f"{e_:.3e}") for n_, e_ in errs.items()}
+            row["oracle"] = {"seconds": round(dt, 2), "scope": scope, "threads": _oracle_threads(), **cpu_info()}
+        rows.append(row)
+        print(json.dumps(row), flush=True)
+        del q, k, v, dout, out, lse, dq, dk, dv, ds, ws
+        torch.cuda.empty_cache()
+    return rows
 
 
 if __name__ == "__main__":
