@@ -16,7 +16,7 @@ from typing import Optional, Sequence
 
 import torch
 
-__all__ = ["fwd", "bwd", "decode_fwd", "bwd_workspace_bytes", "decode_workspace_bytes", "bwd_kernel_names",
+__all__ = ["fwd", "bwd", "bwd_noalloc", "decode_fwd", "bwd_workspace_bytes", "decode_workspace_bytes", "bwd_kernel_names",
            "decode_kernel_names", "check_cu_seqlens", "library_path", "load_library", "AttnSinkError",
            "ERROR_CODES", "HEAD_DIM"]
 
@@ -28,8 +28,9 @@ _lib = None
 ERROR_CODES = {
     0: "ATTN_SINK_OK", -1: "ATTN_SINK_ERR_NULL_PTR", -2: "ATTN_SINK_ERR_BAD_SHAPE",
     -3: "ATTN_SINK_ERR_UNSUPPORTED", -4: "ATTN_SINK_ERR_BAD_WINDOW", -5: "ATTN_SINK_ERR_WORKSPACE",
-    -6: "ATTN_SINK_ERR_HIP", -7: "ATTN_SINK_ERR_ALIGN", -8: "ATTN_SINK_ERR_BAD_SEQLENS",
+    -6: "ATTN_SINK_ERR_HIP", -7: "ATTN_SINK_ERR_ALIGN", -8: "ATTN_SINK_ERR_BAD_SEQLENS", -9: "ATTN_SINK_ERR_SCRATCH",
 }
+NOALLOC_SCRATCH_BYTES = 64 << 20  # ATTN_SINK_NOALLOC_SCRATCH_BYTES
 
 
 class AttnSinkError(RuntimeError):
@@ -76,6 +77,8 @@ def load_library() -> ctypes.CDLL:
     lib.attn_sink_bwd.restype = i32
     lib.attn_sink_bwd_timed.argtypes = bwd_args + [ctypes.POINTER(ctypes.c_void_p), i32]
     lib.attn_sink_bwd_timed.restype = i32
+    lib.attn_sink_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, vp, shp, vp, vp, vp, vp, vp]
+    lib.attn_sink_bwd_noalloc.restype = i32
     lib.attn_sink_bwd_num_kernels.argtypes = []
     lib.attn_sink_bwd_num_kernels.restype = i32
     lib.attn_sink_bwd_kernel_name.argtypes = [i32]
@@ -265,6 +268,37 @@ def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, sinks: torch.Tensor, 
         raise AttnSinkError(rc, "attn_sink_bwd")
     return dq, dk, dv, dsinks
 
+
+
+def bwd_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, sinks: torch.Tensor, out: torch.Tensor,
+                lse: torch.Tensor, dout: torch.Tensor, cu_seqlens: torch.Tensor, max_seqlen: int, causal: bool = True,
+                window: int = 0, softmax_scale: Optional[float] = None, *, dq: torch.Tensor, dk: torch.Tensor,
+                dv: torch.Tensor, dsinks: torch.Tensor):
+    """Backward through attn_sink_bwd_noalloc: same results as ``bwd``, but the library takes its
+    workspace from a static per-GPU scratch array (no allocation by the library; the caller passes
+    every output). Calls that overlap on one GPU race on that array. Returns (dq, dk, dv, dsinks)."""
+    lib = load_library()
+    dev = q.device
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (dout, "dout")):
+        _check(t, n, torch.bfloat16, dev)
+    for t, n in ((sinks, "sinks"), (out, "out"), (lse, "lse"), (dq, "dq"), (dk, "dk"), (dv, "dv"),
+                 (dsinks, "dsinks")):
+        _check(t, n, torch.float32, dev)
+    _check(cu_seqlens, "cu_seqlens", torch.int32, dev)
+    _check_qkv(q, k, v, sinks, cu_seqlens)
+    T, Hq, d = q.shape
+    Hkv = k.shape[1]
+    for t, n, shp in ((out, "out", (T, Hq, d)), (dout, "dout", (T, Hq, d)), (lse, "lse", (Hq, T)),
+                      (dq, "dq", (T, Hq, d)), (dk, "dk", (T, Hkv, d)), (dv, "dv", (T, Hkv, d)),
+                      (dsinks, "dsinks", (Hq,))):
+        _shape_of(t, n, shp)
+    shape = make_shape(q, k, cu_seqlens, max_seqlen, softmax_scale)
+    rc = lib.attn_sink_bwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(sinks), _ptr(out), _ptr(lse), _ptr(dout),
+                                   int(bool(causal)), int(window), _ptr(cu_seqlens), ctypes.byref(shape), _ptr(dq),
+                                   _ptr(dk), _ptr(dv), _ptr(dsinks), _stream(dev))
+    if rc != 0:
+        raise AttnSinkError(rc, "attn_sink_bwd_noalloc")
+    return dq, dk, dv, dsinks
 
 
 def make_decode_shape(q: torch.Tensor, k: torch.Tensor, cu_seqlens_q: torch.Tensor, max_q: int, max_k: int,

@@ -5,6 +5,7 @@
 
 #include "attn_sink.h"
 #include <algorithm>
+#include <mutex>
 
 #include "kernels.h"
 
@@ -78,10 +79,10 @@ size_t workspace_bytes(const attn_sink_shape* s) {
   return 2 * row_plane_bytes(s) + dsink_part_bytes(s) + round256(dkv_part_bytes(s));
 }
 
-int bwd_impl(const void* q, const void* k, const void* v, const float* sinks, const void* out, const float* lse,
-             const void* dout, int causal, int window, const int32_t* cu_seqlens, const attn_sink_shape* shape,
-             void* workspace, size_t ws_bytes, float* dq, float* dk, float* dv, float* dsinks, hipStream_t stream,
-             void* const* events, int num_events) {
+// Checks of the backward's shape and tensor pointers (everything but the workspace).
+int check_bwd_args(const void* q, const void* k, const void* v, const float* sinks, const void* out, const float* lse,
+                   const void* dout, const int32_t* cu_seqlens, const attn_sink_shape* shape, const float* dq,
+                   const float* dk, const float* dv, const float* dsinks) {
   int rc = check_shape(shape);
   if (rc) return rc;
   if (sinks == nullptr || cu_seqlens == nullptr || dsinks == nullptr) return ATTN_SINK_ERR_NULL_PTR;
@@ -91,6 +92,16 @@ int bwd_impl(const void* q, const void* k, const void* v, const float* sinks, co
       !aligned16(dk) || !aligned16(dv)) {
     return ATTN_SINK_ERR_ALIGN;
   }
+  return ATTN_SINK_OK;
+}
+
+int bwd_impl(const void* q, const void* k, const void* v, const float* sinks, const void* out, const float* lse,
+             const void* dout, int causal, int window, const int32_t* cu_seqlens, const attn_sink_shape* shape,
+             void* workspace, size_t ws_bytes, float* dq, float* dk, float* dv, float* dsinks, hipStream_t stream,
+             void* const* events, int num_events) {
+  int rc = check_bwd_args(q, k, v, sinks, out, lse, dout, cu_seqlens, shape, dq, dk, dv, dsinks);
+  if (rc) return rc;
+  const int T = shape->total_tokens;
   const size_t need = workspace_bytes(shape);
   if (workspace == nullptr || ws_bytes < need || !aligned16(workspace)) return ATTN_SINK_ERR_WORKSPACE;
   if (events != nullptr && num_events != kBwdNumKernels + 1) return ATTN_SINK_ERR_BAD_SHAPE;
@@ -224,6 +235,46 @@ size_t decode_workspace_bytes(const attn_sink_decode_shape* s) {
 
 }  // namespace
 
+// ---- backward without a caller workspace ----
+// Device memory for attn_sink_bwd_noalloc's workspace: a file-scope array of fixed size, one copy
+// per GPU the library runs on, held until the process ends. Its name is only a host-side stand-in:
+// host code must use the address hipGetSymbolAddress returns for the device (scratch_address).
+static __device__ __align__(256) unsigned char scratch[ATTN_SINK_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // device address of `scratch` per device, looked up once
+
+// Device address of `scratch` on the device `stream` belongs to (the current device for the
+// NULL stream). The first call per device makes that device current for the lookup and restores
+// the caller's device afterwards.
+int scratch_address(hipStream_t stream, void** out) {
+  int dev = -1;
+  if (stream != nullptr) {
+    if (hipStreamGetDevice(stream, &dev) != hipSuccess) return ATTN_SINK_ERR_HIP;
+  } else if (hipGetDevice(&dev) != hipSuccess) {
+    return ATTN_SINK_ERR_HIP;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return ATTN_SINK_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess) return ATTN_SINK_ERR_HIP;
+    if (cur != dev && hipSetDevice(dev) != hipSuccess) return ATTN_SINK_ERR_HIP;
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev && hipSetDevice(cur) != hipSuccess) return ATTN_SINK_ERR_HIP;
+    if (e != hipSuccess || p == nullptr) return ATTN_SINK_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return ATTN_SINK_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 int attn_sink_fwd(const void* q, const void* k, const void* v, const float* sinks, int causal, int window,
@@ -278,6 +329,20 @@ int attn_sink_bwd_timed(const void* q, const void* k, const void* v, const float
                         float* dv, float* dsinks, hipStream_t stream, void* const* events, int num_events) {
   return bwd_impl(q, k, v, sinks, out, lse, dout, causal, window, cu_seqlens, shape, workspace, workspace_bytes, dq,
                   dk, dv, dsinks, stream, events, num_events);
+}
+
+int attn_sink_bwd_noalloc(const void* q, const void* k, const void* v, const float* sinks, const void* out,
+                          const float* lse, const void* dout, int causal, int window, const int32_t* cu_seqlens,
+                          const attn_sink_shape* shape, float* dq, float* dk, float* dv, float* dsinks,
+                          hipStream_t stream) {
+  int rc = check_bwd_args(q, k, v, sinks, out, lse, dout, cu_seqlens, shape, dq, dk, dv, dsinks);
+  if (rc) return rc;
+  if (workspace_bytes(shape) > (size_t)ATTN_SINK_NOALLOC_SCRATCH_BYTES) return ATTN_SINK_ERR_SCRATCH;
+  void* ws = nullptr;
+  rc = scratch_address(stream, &ws);
+  if (rc) return rc;
+  return bwd_impl(q, k, v, sinks, out, lse, dout, causal, window, cu_seqlens, shape, ws,
+                  (size_t)ATTN_SINK_NOALLOC_SCRATCH_BYTES, dq, dk, dv, dsinks, stream, nullptr, 0);
 }
 
 size_t attn_sink_decode_workspace_bytes(const attn_sink_decode_shape* shape) {
@@ -377,6 +442,9 @@ const char* attn_sink_strerror(int code) {
     case ATTN_SINK_ERR_WORKSPACE: return "workspace missing or smaller than attn_sink_bwd_workspace_bytes()";
     case ATTN_SINK_ERR_HIP: return "a HIP launch failed";
     case ATTN_SINK_ERR_ALIGN: return "a tensor base pointer is not 16-byte aligned";
+    case ATTN_SINK_ERR_SCRATCH:
+      return "attn_sink_bwd_noalloc: the shape needs more workspace than its static scratch holds "
+             "(attn_sink_bwd_workspace_bytes > ATTN_SINK_NOALLOC_SCRATCH_BYTES); use attn_sink_bwd";
     case ATTN_SINK_ERR_BAD_SEQLENS:
       return "cu_seqlens: not 0 at the start, decreasing, not ending at total_tokens, or a length above max_seqlen";
     default: return "unknown error code";

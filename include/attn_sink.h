@@ -67,7 +67,8 @@ enum {
   ATTN_SINK_ERR_WORKSPACE = -5,   /* workspace NULL or smaller than attn_sink_bwd_workspace_bytes() */
   ATTN_SINK_ERR_HIP = -6,         /* a HIP launch failed (hipGetLastError after the launch) */
   ATTN_SINK_ERR_ALIGN = -7,       /* a tensor base pointer is not 16-byte aligned */
-  ATTN_SINK_ERR_BAD_SEQLENS = -8  /* attn_sink_check_cu_seqlens: offsets inconsistent with the shape */
+  ATTN_SINK_ERR_BAD_SEQLENS = -8, /* attn_sink_check_cu_seqlens: offsets inconsistent with the shape */
+  ATTN_SINK_ERR_SCRATCH = -9      /* attn_sink_bwd_noalloc: workspace needed > its static scratch */
 };
 
 enum { ATTN_SINK_F32 = 0, ATTN_SINK_BF16 = 1 };
@@ -117,6 +118,26 @@ int attn_sink_bwd(const void* q, const void* k, const void* v, const float* sink
                   const float* lse, const void* dout, int causal, int window, const int32_t* cu_seqlens,
                   const attn_sink_shape* shape, void* workspace, size_t workspace_bytes, float* dq, float* dk,
                   float* dv, float* dsinks, hipStream_t stream);
+
+/*
+ * attn_sink_bwd for callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): same arguments, semantics and kernels,
+ * minus the workspace, which comes from a static device array of ATTN_SINK_NOALLOC_SCRATCH_BYTES
+ * (64 MiB) that the library holds on each GPU it runs on until the process ends. The caller still
+ * passes every input and output. No hipMalloc, hipFree or other allocating call is made; the
+ * first call on a device looks the array's address up once (hipGetSymbolAddress, with that device
+ * made current for the lookup). Shapes whose attn_sink_bwd_workspace_bytes exceeds the array
+ * return ATTN_SINK_ERR_SCRATCH before anything is enqueued (e.g. 4k tokens x 64/8 heads needs
+ * about 34 MiB, 32k tokens about 16 MiB). Every call on one GPU shares that GPU's array and the
+ * array keeps the last call's contents (the backward writes every workspace value before reading
+ * it, so nothing needs clearing): calls that overlap on one GPU, on different streams or from
+ * different threads, race and give wrong results; serialise them.
+ */
+#define ATTN_SINK_NOALLOC_SCRATCH_BYTES (64u << 20)
+int attn_sink_bwd_noalloc(const void* q, const void* k, const void* v, const float* sinks, const void* out,
+                          const float* lse, const void* dout, int causal, int window, const int32_t* cu_seqlens,
+                          const attn_sink_shape* shape, float* dq, float* dk, float* dv, float* dsinks,
+                          hipStream_t stream);
 
 /*
  * Same as attn_sink_bwd, and additionally records events[0..num_events-1] on `stream` around the
