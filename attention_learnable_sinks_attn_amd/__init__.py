@@ -18,9 +18,9 @@ import torch
 
 __all__ = ["fwd", "bwd", "bwd_noalloc", "decode_fwd", "bwd_workspace_bytes", "decode_workspace_bytes", "bwd_kernel_names",
            "decode_kernel_names", "check_cu_seqlens", "library_path", "load_library", "AttnSinkError",
-           "ERROR_CODES", "HEAD_DIM"]
+           "ERROR_CODES", "HEAD_DIMS"]
 
-HEAD_DIM = 64
+HEAD_DIMS = (64, 128)  # head_dim values the kernels are built for
 _PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG_DIR, "libattn_sink.so")
 _lib = None
@@ -177,8 +177,8 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, sinks: torch.Tensor, 
         max_seqlen: int, causal: bool = True, window: int = 0, softmax_scale: Optional[float] = None,
         out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
         out_dtype: torch.dtype = torch.float32, validate_seqlens: bool = False):
-    """Forward. q [T,Hq,64], k/v [T,Hkv,64] bf16; sinks [Hq] fp32; cu_seqlens [B+1] int32 (device).
-    Returns (out [T,Hq,64] in ``out_dtype`` (fp32, or bf16 for inference; the backward needs fp32),
+    """Forward. q [T,Hq,D], k/v [T,Hkv,D] bf16 (D = 64 or 128); sinks [Hq] fp32; cu_seqlens [B+1] int32 (device).
+    Returns (out [T,Hq,D] in ``out_dtype`` (fp32, or bf16 for inference; the backward needs fp32),
     lse [Hq,T] fp32). ``validate_seqlens`` checks cu_seqlens against T and max_seqlen on the host
     first (a synchronising copy; see check_cu_seqlens)."""
     lib = load_library()
@@ -222,7 +222,7 @@ def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, sinks: torch.Tensor, 
         dv: Optional[torch.Tensor] = None, dsinks: Optional[torch.Tensor] = None,
         workspace: Optional[torch.Tensor] = None, events: Optional[Sequence[int]] = None,
         validate_seqlens: bool = False):
-    """Backward. Returns (dq [T,Hq,64], dk [T,Hkv,64], dv [T,Hkv,64], dsinks [Hq]), all fp32.
+    """Backward. Returns (dq [T,Hq,D], dk [T,Hkv,D], dv [T,Hkv,D], dsinks [Hq]), all fp32.
     ``events``: optional raw hipEvent_t handles (num kernels + 1) recorded around each kernel; an
     entry may be None (nothing recorded there). ``validate_seqlens``: as in fwd."""
     lib = load_library()
@@ -327,7 +327,7 @@ def decode_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, sinks: torch.T
                out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
                workspace: Optional[torch.Tensor] = None, events: Optional[Sequence[int]] = None,
                validate_seqlens: bool = False):
-    """Decode forward: q [Tq,Hq,64] (each sequence's last Nq_b tokens), k/v [Tk,Hkv,64] caches, bf16;
+    """Decode forward: q [Tq,Hq,D] (each sequence's last Nq_b tokens), k/v [Tk,Hkv,D] caches, bf16;
     sinks [Hq] fp32; cu_seqlens_q / cu_seqlens_k [B+1] int32 (device). Returns (out [Tq,Hq,64] in
     ``out_dtype``, lse [Hq,Tq] fp32). ``events``: optional raw hipEvent_t handles (num kernels + 1)
     recorded around each kernel; an entry may be None (nothing recorded there).

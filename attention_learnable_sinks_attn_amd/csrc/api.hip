@@ -15,6 +15,8 @@ namespace {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+bool head_dim_ok(int d) { return d == 64 || d == 128; }
+
 // bf16_out: whether the call can store its output in bf16 (the forward can; the backward reads
 // the forward's fp32 output).
 int check_shape(const attn_sink_shape* s, bool bf16_out = false) {
@@ -23,7 +25,8 @@ int check_shape(const attn_sink_shape* s, bool bf16_out = false) {
       s->max_seqlen < 0 || s->max_seqlen > s->total_tokens || s->num_heads_q % s->num_heads_kv != 0) {
     return ATTN_SINK_ERR_BAD_SHAPE;
   }
-  if (s->head_dim != kHeadDim || (s->out_dtype != ATTN_SINK_F32 && !(bf16_out && s->out_dtype == ATTN_SINK_BF16))) {
+  if (!head_dim_ok(s->head_dim) ||
+      (s->out_dtype != ATTN_SINK_F32 && !(bf16_out && s->out_dtype == ATTN_SINK_BF16))) {
     return ATTN_SINK_ERR_UNSUPPORTED;
   }
   // Element offsets are 64-bit in the kernels, but grid sizes and per-head row indices are
@@ -145,6 +148,7 @@ int bwd_impl(const void* q, const void* k, const void* v, const float* sinks, co
   a.window = clamp_window(window, shape->max_seqlen);
   a.scale = resolve_scale(shape);
   a.scale_log2 = a.scale * kLog2e;
+  a.D = shape->head_dim;
 
   typedef hipError_t (*launcher)(const BwdArgs&, hipStream_t);
   const launcher steps[kBwdNumKernels] = {launch_bwd_dq, launch_bwd_dkdv, launch_bwd_finish};
@@ -169,11 +173,11 @@ int check_decode_shape(const attn_sink_decode_shape* s) {
       s->max_q > s->total_q || s->max_k > s->total_k) {
     return ATTN_SINK_ERR_BAD_SHAPE;
   }
-  if (s->head_dim != kHeadDim || (s->out_dtype != ATTN_SINK_F32 && s->out_dtype != ATTN_SINK_BF16)) {
+  if (!head_dim_ok(s->head_dim) || (s->out_dtype != ATTN_SINK_F32 && s->out_dtype != ATTN_SINK_BF16)) {
     return ATTN_SINK_ERR_UNSUPPORTED;
   }
   if ((long long)s->max_q * (s->num_heads_q / s->num_heads_kv) > kDecodeMaxCols) return ATTN_SINK_ERR_UNSUPPORTED;
-  if ((long long)s->total_k * s->num_heads_kv * kHeadDim >= (1LL << 40) ||
+  if ((long long)s->total_k * s->num_heads_kv * s->head_dim >= (1LL << 40) ||
       (long long)s->total_q * s->num_heads_q >= (1LL << 31) ||
       (long long)s->num_seqs * s->num_heads_kv * kDecodeMaxCols >= (1LL << 31) ||  // workgroups of one launch
       (s->total_q > 0 && s->max_q < 1)) {
@@ -222,7 +226,7 @@ void decode_chunks(const attn_sink_decode_shape* s, int window, int* n_chunks, i
 }
 
 size_t decode_part_o_bytes(const attn_sink_decode_shape* s, int n_chunks) {
-  return round256((size_t)s->num_seqs * s->num_heads_kv * decode_col_groups(s) * n_chunks * kHeadDim * 32 *
+  return round256((size_t)s->num_seqs * s->num_heads_kv * decode_col_groups(s) * n_chunks * s->head_dim * 32 *
                   sizeof(float));
 }
 
@@ -302,7 +306,8 @@ int attn_sink_fwd(const void* q, const void* k, const void* v, const float* sink
   a.Hkv = shape->num_heads_kv;
   a.G = a.Hq / a.Hkv;
   a.hpw = heads_per_group_split(a.G);
-  const int fwd_rows = kFwdRowsPerWave * (4 / a.hpw);  // rows per forward workgroup
+  a.D = shape->head_dim;
+  const int fwd_rows = fwd_rows_per_wave(a.D) * (4 / a.hpw);  // rows per forward workgroup
   a.n_qblocks = (shape->max_seqlen + fwd_rows - 1) / fwd_rows;
   a.causal = causal ? 1 : 0;
   a.window = clamp_window(window, shape->max_seqlen);
@@ -393,6 +398,7 @@ int attn_sink_decode_fwd_timed(const void* q, const void* k, const void* v, cons
   a.n_cg = decode_col_groups(shape);
   a.window = clamp_window(window, shape->max_k);
   a.out_bf16 = shape->out_dtype == ATTN_SINK_BF16 ? 1 : 0;
+  a.D = shape->head_dim;
   const float scale = shape->softmax_scale > 0.0f ? shape->softmax_scale : 1.0f / sqrtf((float)shape->head_dim);
   a.scale_log2 = scale * kLog2e;
   return launch_decode(a, stream, ev) == hipSuccess ? ATTN_SINK_OK : ATTN_SINK_ERR_HIP;
@@ -437,7 +443,8 @@ const char* attn_sink_strerror(int code) {
     case ATTN_SINK_OK: return "success";
     case ATTN_SINK_ERR_NULL_PTR: return "a required pointer is NULL";
     case ATTN_SINK_ERR_BAD_SHAPE: return "invalid shape (sizes, head counts or max_seqlen)";
-    case ATTN_SINK_ERR_UNSUPPORTED: return "unsupported head_dim or output dtype (head_dim 64, float32 outputs)";
+    case ATTN_SINK_ERR_UNSUPPORTED:
+      return "unsupported head_dim or output dtype (head_dim 64 or 128; float32 outputs, bf16 also for forwards)";
     case ATTN_SINK_ERR_BAD_WINDOW: return "negative window";
     case ATTN_SINK_ERR_WORKSPACE: return "workspace missing or smaller than attn_sink_bwd_workspace_bytes()";
     case ATTN_SINK_ERR_HIP: return "a HIP launch failed";

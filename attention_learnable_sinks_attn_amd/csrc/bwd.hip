@@ -46,18 +46,25 @@ namespace {
 // ------------------------------------------------------------------------------------------
 // 2. dK, dV: column-parallel over 64-key blocks.
 // ------------------------------------------------------------------------------------------
-constexpr int kKvSub = 32;                                        // query rows per product block
-constexpr int kKvRows = 64;                                       // query rows per step (2 blocks)
-constexpr int kKvRing = 2;                                        // LDS ring slots per head stream
-constexpr int kKvTileBytes = kKvRows * kHeadDim * 2;              // one 64 x 64 bf16 row tile
-constexpr int kKvSlotBytes = 2 * kKvTileBytes + 2 * kKvRows * 4;  // Q, dO, -LSE/scale, -D
-constexpr int kKvStreamBytes = kKvRing * kKvSlotBytes;
-constexpr int kKvRedStride = kHeadDim + 4;                        // fp32 row of the final sum
+constexpr int kKvSub = 32;        // query rows per product block
+constexpr int kKvRing = 2;        // LDS ring slots per head stream
+constexpr int kKvTileBytes = 8192;  // one Q or dO row tile (64 rows at D = 64, 32 at D = 128)
 
-template <int NS>  // head streams per workgroup: 1 or 2 (waves = 2 key halves x NS)
-__global__ __launch_bounds__(128 * NS, 2) void attn_sink_bwd_dkdv_kernel(BwdArgs a) {
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[NS * kKvStreamBytes];
-  static_assert(sizeof(smem) >= (NS == 2 ? 2 * 2 * 32 * kKvRedStride * 4 : 0), "final sum fits");
+// Head dim D = 64 or 128. A step is one 8 KiB row tile: 64 rows (two product blocks) at D = 64,
+// 32 rows at D = 128, whose dK/dV accumulators and K/V operands take twice the registers; that
+// instance runs one wave per SIMD.
+template <int NS, int D>  // head streams per workgroup: 1 or 2 (waves = 2 key halves x NS)
+__global__ __launch_bounds__(128 * NS, D == 64 ? 2 : 1) void attn_sink_bwd_dkdv_kernel(BwdArgs a) {
+  using G_ = Geo<D>;
+  constexpr int kKvRows = G_::kTileRows;                            // query rows per step
+  constexpr int kSubs = kKvRows / kKvSub;                           // product blocks per step
+  constexpr int kKvSlotBytes = 2 * kKvTileBytes + 2 * kKvRows * 4;  // Q, dO, -LSE/scale, -D
+  constexpr int kKvStreamBytes = kKvRing * kKvSlotBytes;
+  constexpr int kKvRedStride = D + 4;                               // fp32 row of the final sum
+  constexpr int kRedBytes = NS == 2 ? 2 * 2 * 32 * kKvRedStride * 4 : 0;
+  constexpr int kNtr = 8 * G_::kDBlocks;                            // transposing reads per block
+  __shared__ __attribute__((aligned(1024)))
+  unsigned char smem[NS * kKvStreamBytes > kRedBytes ? NS * kKvStreamBytes : kRedBytes];
   static_assert(kKvRing == 2, "the waits below assume one step in flight");
 
   // Block order: KV group fastest (consecutive ids go to different XCDs, so each XCD works on
@@ -89,20 +96,21 @@ __global__ __launch_bounds__(128 * NS, 2) void attn_sink_bwd_dkdv_kernel(BwdArgs
   const int h0 = g * a.G + hh * heads_half + st;  // stream st takes heads h0 + NS * j
 
   // K^T and V^T as B operands (k = d, n = key): lane holds key k0 + l32, d = 16c + 8grp + 0..7.
-  bf16x8 kf[4], vf[4];
+  bf16x8 kf[G_::kChunks], vf[G_::kChunks];
   {
     const int key = min(k0 + l32, len - 1);  // keys past the end are masked
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const size_t off = ((size_t)(cs + key) * a.Hkv + g) * kHeadDim + 16 * c + 8 * grp;
+    for (int c = 0; c < G_::kChunks; ++c) {
+      const size_t off = ((size_t)(cs + key) * a.Hkv + g) * D + 16 * c + 8 * grp;
       kf[c] = load_bf16x8(a.k + off);
       vf[c] = load_bf16x8(a.v + off);
     }
   }
-  f32x16 dk[2], dv[2];  // [d block], C layout of dK^T / dV^T (rows d, columns this wave's keys)
-  dk[0] = dk[1] = dv[0] = dv[1] = zero_f32x16();
+  f32x16 dk[G_::kDBlocks], dv[G_::kDBlocks];  // [d block], C layout of dK^T / dV^T (rows d, columns keys)
+#pragma unroll
+  for (int db = 0; db < G_::kDBlocks; ++db) dk[db] = dv[db] = zero_f32x16();
 
-  // Query rows that can see a key of [kblk, kblk + 64), in 32-row steps from the last backwards
+  // Query rows that can see a key of [kblk, kblk + 64), in steps of kKvRows from the last backwards
   // (every workgroup's causal range ends at the sequence end, so the workgroups of one KV group
   // stream the same rows at about the same time and mostly hit in L2). Both key halves and both
   // streams run the same number of steps, so one barrier per step serves the whole workgroup.
@@ -117,7 +125,7 @@ __global__ __launch_bounds__(128 * NS, 2) void attn_sink_bwd_dkdv_kernel(BwdArgs
   // half 1 the dO tile (tile_copy layout). Full tiles go through buffer resources; in the last,
   // partial tile rows past the end repeat the last row (they are masked).
   unsigned char* ring = smem + st * kKvStreamBytes;
-  const int qstride = a.Hq * kHeadDim;  // elements per token row of q / dout
+  const int qstride = a.Hq * D;  // elements per token row of q / dout
   const unsigned qrow_bytes = 2u * qstride;
   unsigned coff[2];
   tile_copy_offsets(lane, qrow_bytes, coff);
@@ -133,17 +141,25 @@ __global__ __launch_bounds__(128 * NS, 2) void attn_sink_bwd_dkdv_kernel(BwdArgs
     if (i0 + kKvRows <= len) {
       const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(src, kKvRows * qrow_bytes);
 #pragma unroll
-      for (int u = 0; u < kKvTileBytes / 1024; ++u) tile_copy_full(rs, coff, qrow_bytes, dst, u);
-      if (kh == 0) {  // -LSE/scale rows, then -D rows (64 each)
-        bdma4(buffer_rsrc(nl, 4 * kKvRows), 4 * lane, 0, rows);
-        bdma4(buffer_rsrc(nd, 4 * kKvRows), 4 * lane, 0, rows + 4 * kKvRows);
+      for (int u = 0; u < kKvTileBytes / 1024; ++u) tile_copy_full_d<D>(rs, coff, qrow_bytes, dst, u);
+      if (kh == 0) {  // -LSE/scale rows, then -D rows (kKvRows each)
+        if constexpr (kKvRows == 64) {
+          bdma4(buffer_rsrc(nl, 4 * kKvRows), 4 * lane, 0, rows);
+          bdma4(buffer_rsrc(nd, 4 * kKvRows), 4 * lane, 0, rows + 4 * kKvRows);
+        } else {  // 32 rows of each: one copy, lanes 32-63 fetch the -D rows
+          dma4(lane < 32 ? nl + lane : nd + (lane - 32), rows);
+        }
       }
     } else {
 #pragma unroll
-      for (int u = 0; u < kKvTileBytes / 1024; ++u) tile_copy(src, 0, len - 1 - i0, qstride, dst, u, lane);
+      for (int u = 0; u < kKvTileBytes / 1024; ++u) tile_copy_d<D>(src, 0, len - 1 - i0, qstride, dst, u, lane);
       if (kh == 0) {
-        dma4(nl + min(lane, len - 1 - i0), rows);
-        dma4(nd + min(lane, len - 1 - i0), rows + 4 * kKvRows);
+        if constexpr (kKvRows == 64) {
+          dma4(nl + min(lane, len - 1 - i0), rows);
+          dma4(nd + min(lane, len - 1 - i0), rows + 4 * kKvRows);
+        } else {
+          dma4(lane < 32 ? nl + min(lane, len - 1 - i0) : nd + min(lane - 32, len - 1 - i0), rows);
+        }
       }
     }
   };
@@ -166,20 +182,24 @@ __global__ __launch_bounds__(128 * NS, 2) void attn_sink_bwd_dkdv_kernel(BwdArgs
     trb[db][0] = lds_addr(ring) + toff[db][0];
     trb[db][1] = lds_addr(ring) + toff[db][1];
   }
-  auto tr8 = [&](auto base_tag, auto tile_tag, int db, auto half_tag, u32x2& lo, u32x2& hi) {
-    constexpr int OFF =
-        decltype(base_tag)::value + decltype(tile_tag)::value * kKvTileBytes + 2048 * decltype(half_tag)::value;
-    lo = ds_read_tr16_b64_asm<OFF>(trb[db][0]);
-    hi = ds_read_tr16_b64_asm<OFF>(trb[db][1]);
+  // d block db lives in panel db / 2 of the tile, as d block db % 2 of that panel.
+  auto tr8 = [&](auto base_tag, auto tile_tag, auto db_tag, auto half_tag, u32x2& lo, u32x2& hi) {
+    constexpr int db = decltype(db_tag)::value;
+    constexpr int OFF = decltype(base_tag)::value + decltype(tile_tag)::value * kKvTileBytes +
+                        (db / 2) * G_::kPanelBytes + 2048 * decltype(half_tag)::value;
+    lo = ds_read_tr16_b64_asm<OFF>(trb[db % 2][0]);
+    hi = ds_read_tr16_b64_asm<OFF>(trb[db % 2][1]);
   };
-  auto tr_all = [&](auto base_tag, u32x2 (&tr)[16]) {  // [d block][query half][Q / dO][lo / hi]
-#pragma unroll
-    for (int db = 0; db < 2; ++db) {
-      tr8(base_tag, std::integral_constant<int, 0>(), db, std::integral_constant<int, 0>(), tr[8 * db], tr[8 * db + 1]);
-      tr8(base_tag, std::integral_constant<int, 1>(), db, std::integral_constant<int, 0>(), tr[8 * db + 2], tr[8 * db + 3]);
-      tr8(base_tag, std::integral_constant<int, 0>(), db, std::integral_constant<int, 1>(), tr[8 * db + 4], tr[8 * db + 5]);
-      tr8(base_tag, std::integral_constant<int, 1>(), db, std::integral_constant<int, 1>(), tr[8 * db + 6], tr[8 * db + 7]);
-    }
+  auto tr_all = [&](auto base_tag, u32x2 (&tr)[kNtr]) {  // [d block][query half][Q / dO][lo / hi]
+    static_for<G_::kDBlocks>([&](auto db_tag) {
+      constexpr int db = decltype(db_tag)::value;
+      using Z = std::integral_constant<int, 0>;
+      using O = std::integral_constant<int, 1>;
+      tr8(base_tag, Z(), db_tag, Z(), tr[8 * db], tr[8 * db + 1]);
+      tr8(base_tag, O(), db_tag, Z(), tr[8 * db + 2], tr[8 * db + 3]);
+      tr8(base_tag, Z(), db_tag, O(), tr[8 * db + 4], tr[8 * db + 5]);
+      tr8(base_tag, O(), db_tag, O(), tr[8 * db + 6], tr[8 * db + 7]);
+    });
   };
 
   // One step: S' = Q K^T - LSE/scale and dP' = dO V^T - D for the 32 rows x 32 keys (the row
@@ -197,13 +217,14 @@ __global__ __launch_bounds__(128 * NS, 2) void attn_sink_bwd_dkdv_kernel(BwdArgs
     bool again;
     do {
       f32x16 sc = load_rows16(lp, grp);
-      f32x16 dp = load_rows16(lp + kKvRows, grp);  // -D rows follow the 64 -LSE/scale rows
+      f32x16 dp = load_rows16(lp + kKvRows, grp);  // -D rows follow the kKvRows -LSE/scale rows
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        sc = mfma_32x32x16(*reinterpret_cast<const bf16x8*>(slot + aoff[c]), kf[c], sc);
-        dp = mfma_32x32x16(*reinterpret_cast<const bf16x8*>(slot + kKvTileBytes + aoff[c]), vf[c], dp);
+      for (int c = 0; c < G_::kChunks; ++c) {
+        sc = mfma_32x32x16(*reinterpret_cast<const bf16x8*>(slot + frag_off<D>(aoff, c, 0)), kf[c], sc);
+        dp = mfma_32x32x16(*reinterpret_cast<const bf16x8*>(slot + kKvTileBytes + frag_off<D>(aoff, c, 0)), vf[c],
+                           dp);
       }
-      u32x2 tr[16];
+      u32x2 tr[kNtr];
       tr_all(std::integral_constant<int, SO>(), tr);
       if (need_mask) {
         // Row of register i: i0 + 8grp + r_i with r_i = 16(i/8) + i%8. Key kj is seen by the
@@ -239,7 +260,7 @@ __global__ __launch_bounds__(128 * NS, 2) void attn_sink_bwd_dkdv_kernel(BwdArgs
       }
       wait_lds_into(tr);
 #pragma unroll
-      for (int db = 0; db < 2; ++db) {
+      for (int db = 0; db < G_::kDBlocks; ++db) {
         const u32x2* t = tr + 8 * db;
         dv[db] = mfma_32x32x16(join_tr(t[2], t[3]), pb0, dv[db]);
         dv[db] = mfma_32x32x16(join_tr(t[6], t[7]), pb1, dv[db]);
@@ -254,10 +275,10 @@ __global__ __launch_bounds__(128 * NS, 2) void attn_sink_bwd_dkdv_kernel(BwdArgs
   // The next step to issue (wave-uniform): tile index, first row and offsets.
   int nx_t = 0;
   int nx_i0 = i_begin + kKvRows * (n_sub - 1);
-  size_t nx_qoff = ((size_t)(cs + nx_i0) * a.Hq + h0) * kHeadDim;
+  size_t nx_qoff = ((size_t)(cs + nx_i0) * a.Hq + h0) * D;
   size_t nx_roff = (size_t)h0 * a.T + cs + nx_i0;
   const size_t tile_q = (size_t)kKvRows * qstride;                            // one tile back
-  const size_t head_q = (size_t)NS * kHeadDim + (size_t)(n_sub - 1) * tile_q;  // next head's last tile
+  const size_t head_q = (size_t)NS * D + (size_t)(n_sub - 1) * tile_q;  // next head's last tile
   const size_t head_r = (size_t)NS * a.T + (size_t)(n_sub - 1) * kKvRows;
   auto issue_next = [&](int slot) {
     issue(nx_i0, nx_qoff, nx_roff, slot);
@@ -289,7 +310,7 @@ __global__ __launch_bounds__(128 * NS, 2) void attn_sink_bwd_dkdv_kernel(BwdArgs
 
   int cur_i0 = nx_i0;  // first row of the current step
   issue_next(0);
-  static_assert(kKvRing == 2 && kKvRows == 2 * kKvSub, "two slots, two 32-row blocks per step");
+  static_assert(kKvRing == 2 && kKvRows % kKvSub == 0, "two slots, whole 32-row blocks per step");
   auto do_step = [&](int s, auto si_tag) {  // step s, held in slot SI = s % 2
     constexpr int SI = decltype(si_tag)::value;
     wait_own_step();
@@ -305,9 +326,11 @@ __global__ __launch_bounds__(128 * NS, 2) void attn_sink_bwd_dkdv_kernel(BwdArgs
     if (i0 >= live_lo && i0 <= live_hi) {
       step(si_tag, std::integral_constant<int, 0>(), i0, i0 < mask_lo || i0 > mask_hi);
     }
-    const int i1 = i0 + kKvSub;
-    if (i1 >= live_lo && i1 <= live_hi) {
-      step(si_tag, std::integral_constant<int, 1>(), i1, i1 < mask_lo || i1 > mask_hi);
+    if constexpr (kSubs == 2) {
+      const int i1 = i0 + kKvSub;
+      if (i1 >= live_lo && i1 <= live_hi) {
+        step(si_tag, std::integral_constant<int, 1>(), i1, i1 < mask_lo || i1 > mask_hi);
+      }
     }
   };
   for (int s = 0; s < n_steps; s += 2) {
@@ -321,7 +344,7 @@ __global__ __launch_bounds__(128 * NS, 2) void attn_sink_bwd_dkdv_kernel(BwdArgs
     __syncthreads();  // every wave is done with its ring
     if (st == 1) {
 #pragma unroll
-      for (int db = 0; db < 2; ++db) {
+      for (int db = 0; db < G_::kDBlocks; ++db) {
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
           const int d = 32 * db + 8 * r4 + 4 * grp;
@@ -339,14 +362,14 @@ __global__ __launch_bounds__(128 * NS, 2) void attn_sink_bwd_dkdv_kernel(BwdArgs
     if (key < len) {
       // With one head half these are dK (scaled here) and dV; otherwise this half's unscaled
       // partial sums, which attn_sink_bwd_finish_kernel adds and scales.
-      const size_t plane = (size_t)a.T * a.Hkv * kHeadDim;
-      const size_t row = ((size_t)(cs + key) * a.Hkv + g) * kHeadDim;
+      const size_t plane = (size_t)a.T * a.Hkv * D;
+      const size_t row = ((size_t)(cs + key) * a.Hkv + g) * D;
       const bool direct = a.n_halves == 1;
       float* dkrow = direct ? a.dk + row : a.dkv_part + hh * plane + row;
       float* dvrow = direct ? a.dv + row : a.dkv_part + (a.n_halves + hh) * plane + row;
       const float kscale = direct ? a.scale : 1.0f;
 #pragma unroll
-      for (int db = 0; db < 2; ++db) {
+      for (int db = 0; db < G_::kDBlocks; ++db) {
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
           const int d = 32 * db + 8 * r4 + 4 * grp;
@@ -367,17 +390,20 @@ __global__ __launch_bounds__(128 * NS, 2) void attn_sink_bwd_dkdv_kernel(BwdArgs
 // ------------------------------------------------------------------------------------------
 // 1. dQ, D and the dSink partials: row-parallel over 32-row query blocks.
 // ------------------------------------------------------------------------------------------
-constexpr int kDqTileKeys = 64;
-constexpr int kDqTileBytes = kDqTileKeys * kHeadDim * 2;  // one swizzled 64-key tile (K or V)
-constexpr int kDqSlotBytes = 2 * kDqTileBytes;             // K tile, then V tile
-constexpr int kDqRing = 4;                                 // LDS ring slots (two pairs of tiles)
+constexpr int kDqTileBytes = 8192;             // one swizzled K or V tile (64 keys at D = 64, 32 at D = 128)
+constexpr int kDqSlotBytes = 2 * kDqTileBytes;  // K tile, then V tile
+constexpr int kDqRing = 4;                      // LDS ring slots (two pairs of tiles)
 
 // HPW query heads of one KV group x RPW = 4 / HPW blocks of 32 rows per workgroup (four waves).
-template <int HPW>
+template <int HPW, int D>
 __global__ __launch_bounds__(256, 2) void attn_sink_bwd_dq_kernel(BwdArgs a) {
+  using G_ = Geo<D>;
+  constexpr int kDqTileKeys = G_::kTileRows;
+  constexpr int MB = G_::kRowBlocks;                    // 32-key blocks per tile
   constexpr int kRows = kDqRowsPerWave;                 // query rows per wave
   constexpr int RPW = 4 / HPW;                          // row blocks per workgroup
   constexpr int CPW = 2 * (kDqTileBytes / 1024) / 4;    // copies per wave and tile (K and V)
+  constexpr int NTR = G_::kDBlocks * MB * 4;            // transposing reads of K^T per tile
   __shared__ __attribute__((aligned(1024))) unsigned char ring[kDqRing * kDqSlotBytes];
 
   const int n_hs = a.Hq / HPW;
@@ -406,10 +432,10 @@ __global__ __launch_bounds__(256, 2) void attn_sink_bwd_dq_kernel(BwdArgs a) {
   const int qi = q0 + l32;
   const bool qok = qi < len;
   const int qc = min(qi, len - 1);  // rows past the end compute on the last row and are not stored
-  bf16x8 qf[4], df[4];
+  bf16x8 qf[G_::kChunks], df[G_::kChunks];
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    const size_t off = ((size_t)(cs + qc) * a.Hq + h) * kHeadDim + 16 * c + 8 * grp;
+  for (int c = 0; c < G_::kChunks; ++c) {
+    const size_t off = ((size_t)(cs + qc) * a.Hq + h) * D + 16 * c + 8 * grp;
     qf[c] = load_bf16x8(a.q + off);
     df[c] = load_bf16x8(a.dout + off);
   }
@@ -417,9 +443,9 @@ __global__ __launch_bounds__(256, 2) void attn_sink_bwd_dq_kernel(BwdArgs a) {
   // half of the row from lane ^ 32. -D_i and -LSE_i / scale go to the workspace for the dK/dV pass.
   float dpart = 0.0f;
   {
-    const float* orow = a.out + ((size_t)(cs + qc) * a.Hq + h) * kHeadDim + 8 * grp;
+    const float* orow = a.out + ((size_t)(cs + qc) * a.Hq + h) * D + 8 * grp;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
+    for (int c = 0; c < G_::kChunks; ++c) {
       const f32x4 o0 = *reinterpret_cast<const f32x4*>(orow + 16 * c);
       const f32x4 o1 = *reinterpret_cast<const f32x4*>(orow + 16 * c + 4);
 #pragma unroll
@@ -437,8 +463,9 @@ __global__ __launch_bounds__(256, 2) void attn_sink_bwd_dq_kernel(BwdArgs a) {
     a.nlse[(size_t)h * a.T + cs + qi] = nl;
   }
   float dsum = 0.0f;
-  f32x16 acc[2];  // dQ^T, [d block]
-  acc[0] = acc[1] = zero_f32x16();
+  f32x16 acc[G_::kDBlocks];  // dQ^T, [d block]
+#pragma unroll
+  for (int db = 0; db < G_::kDBlocks; ++db) acc[db] = zero_f32x16();
 
   // Keys a row range can see (as in the forward): the workgroup streams its whole range's tiles,
   // each wave computes only its own.
@@ -450,11 +477,11 @@ __global__ __launch_bounds__(256, 2) void attn_sink_bwd_dq_kernel(BwdArgs a) {
   const int kt_end = (key_end(qw0 + kRows * RPW) + kDqTileKeys - 1) / kDqTileKeys;
   const int kw_begin = key_begin(q0);
   const int kw_end = rows_live ? key_end(q0 + kRows) : 0;
-  const int kv_stride = a.Hkv * kHeadDim;
-  const __bf16* kbase = a.k + (size_t)cs * kv_stride + (size_t)g * kHeadDim;
-  const __bf16* vbase = a.v + (size_t)cs * kv_stride + (size_t)g * kHeadDim;
+  const int kv_stride = a.Hkv * D;
+  const __bf16* kbase = a.k + (size_t)cs * kv_stride + (size_t)g * D;
+  const __bf16* vbase = a.v + (size_t)cs * kv_stride + (size_t)g * D;
 
-  // K and V tiles of 64 keys, swizzled (see tile_swz), in a 4-slot ring filled by direct
+  // K and V tiles of kDqTileKeys keys, swizzled (see tile_swz), in a 4-slot ring filled by direct
   // global->LDS copies issued one pair of tiles ahead; the waves split each tile's 16 copies (waves 0-1
   // the K tile, 2-3 the V tile). Full tiles go through a buffer resource; in the last, partial
   // tile keys past the sequence end repeat its last key (finite data; they are masked).
@@ -474,10 +501,10 @@ __global__ __launch_bounds__(256, 2) void attn_sink_bwd_dq_kernel(BwdArgs a) {
     if (row0 + kDqTileKeys <= len) {
       const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(nx_src, kDqTileKeys * row_bytes);
 #pragma unroll
-      for (int i = 0; i < CPW; ++i) tile_copy_full(rs, coff, row_bytes, tile, (u0 + i) & 7);
+      for (int i = 0; i < CPW; ++i) tile_copy_full_d<D>(rs, coff, row_bytes, tile, (u0 + i) & 7);
     } else {
 #pragma unroll
-      for (int i = 0; i < CPW; ++i) tile_copy(nx_src, 0, len - 1 - row0, kv_stride, tile, (u0 + i) & 7, lane);
+      for (int i = 0; i < CPW; ++i) tile_copy_d<D>(nx_src, 0, len - 1 - row0, kv_stride, tile, (u0 + i) & 7, lane);
     }
     nx_src += tile_elems;
     ++nx_kt;
@@ -525,34 +552,35 @@ __global__ __launch_bounds__(256, 2) void attn_sink_bwd_dq_kernel(BwdArgs a) {
     auto tile = [&](bool residual, unsigned lds_off) -> float {
       const unsigned char* slot = ring + lds_off;
       const unsigned slot_lds = ring_lds + lds_off;
-      f32x16 s[2], dp[2];
+      f32x16 s[MB], dp[MB];
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
+      for (int mb = 0; mb < MB; ++mb) {
         s[mb] = zero_f32x16();
         dp[mb] = zero_f32x16();
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          s[mb] = mfma_32x32x16(*reinterpret_cast<const bf16x8*>(slot + 4096 * mb + aoff[c]), qf[c], s[mb]);
-          dp[mb] = mfma_32x32x16(*reinterpret_cast<const bf16x8*>(slot + kDqTileBytes + 4096 * mb + aoff[c]), df[c],
-                                 dp[mb]);
+        for (int c = 0; c < G_::kChunks; ++c) {
+          s[mb] = mfma_32x32x16(*reinterpret_cast<const bf16x8*>(slot + frag_off<D>(aoff, c, mb)), qf[c], s[mb]);
+          dp[mb] = mfma_32x32x16(*reinterpret_cast<const bf16x8*>(slot + kDqTileBytes + frag_off<D>(aoff, c, mb)),
+                                 df[c], dp[mb]);
         }
       }
-      // K^T operands for dQ^T (rows d = 32db + l32, k slots = keys 32mb + 16cc + 8grp + 0..7).
-      u32x2 tr[16];  // [d block][key block][half][lo / hi]
-#pragma unroll
-      for (int db = 0; db < 2; ++db) {
-        tr[8 * db + 0] = ds_read_tr16_b64_asm<0>(slot_lds + toff[db][0]);
-        tr[8 * db + 1] = ds_read_tr16_b64_asm<0>(slot_lds + toff[db][1]);
-        tr[8 * db + 2] = ds_read_tr16_b64_asm<2048>(slot_lds + toff[db][0]);
-        tr[8 * db + 3] = ds_read_tr16_b64_asm<2048>(slot_lds + toff[db][1]);
-        tr[8 * db + 4] = ds_read_tr16_b64_asm<4096>(slot_lds + toff[db][0]);
-        tr[8 * db + 5] = ds_read_tr16_b64_asm<4096>(slot_lds + toff[db][1]);
-        tr[8 * db + 6] = ds_read_tr16_b64_asm<6144>(slot_lds + toff[db][0]);
-        tr[8 * db + 7] = ds_read_tr16_b64_asm<6144>(slot_lds + toff[db][1]);
-      }
+      // K^T operands for dQ^T (rows d = 32db + l32, k slots = keys 32mb + 16cc + 8grp + 0..7):
+      // tr[4 (db MB + mb) + 2 cc + lo/hi], from panel db / 2 at rows 32mb + 16cc.
+      u32x2 tr[NTR];
+      static_for<G_::kDBlocks>([&](auto db_tag) {
+        constexpr int db = decltype(db_tag)::value;
+        constexpr int PO = (db / 2) * G_::kPanelBytes;
+        static_for<MB>([&](auto mb_tag) {
+          constexpr int mb = decltype(mb_tag)::value;
+          tr[4 * (db * MB + mb) + 0] = ds_read_tr16_b64_asm<PO + 4096 * mb>(slot_lds + toff[db % 2][0]);
+          tr[4 * (db * MB + mb) + 1] = ds_read_tr16_b64_asm<PO + 4096 * mb>(slot_lds + toff[db % 2][1]);
+          tr[4 * (db * MB + mb) + 2] = ds_read_tr16_b64_asm<PO + 4096 * mb + 2048>(slot_lds + toff[db % 2][0]);
+          tr[4 * (db * MB + mb) + 3] = ds_read_tr16_b64_asm<PO + 4096 * mb + 2048>(slot_lds + toff[db % 2][1]);
+        });
+      });
       float pmax = 0.0f, part = 0.0f;
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
+      for (int mb = 0; mb < MB; ++mb) {
         if (need_mask) {  // uniform: only diagonal, window-edge and ragged tiles
           const KeyBounds kb = key_bounds(qi, len, a.causal, a.window);
           const unsigned cnt = (unsigned)max(kb.hi - kb.lo, 0);  // visible keys kb.lo + 1 .. kb.hi
@@ -577,8 +605,8 @@ __global__ __launch_bounds__(256, 2) void attn_sink_bwd_dq_kernel(BwdArgs a) {
         }
         if (mb == 0) wait_lds_into(tr);
 #pragma unroll
-        for (int db = 0; db < 2; ++db) {
-          const u32x2* t = tr + 8 * db + 4 * mb;
+        for (int db = 0; db < G_::kDBlocks; ++db) {
+          const u32x2* t = tr + 4 * (db * MB + mb);
           acc[db] = mfma_32x32x16(join_tr(t[0], t[1]), d0, acc[db]);
           acc[db] = mfma_32x32x16(join_tr(t[2], t[3]), d1, acc[db]);
         }
@@ -598,9 +626,9 @@ __global__ __launch_bounds__(256, 2) void attn_sink_bwd_dq_kernel(BwdArgs a) {
   const float dtot = sum_xor32(dsum);
   float wsum = 0.0f;
   if (qok) {
-    float* qrow = a.dq + ((size_t)(cs + qi) * a.Hq + h) * kHeadDim;
+    float* qrow = a.dq + ((size_t)(cs + qi) * a.Hq + h) * D;
 #pragma unroll
-    for (int db = 0; db < 2; ++db) {
+    for (int db = 0; db < G_::kDBlocks; ++db) {
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
         f32x4 val = {acc[db][4 * r4], acc[db][4 * r4 + 1], acc[db][4 * r4 + 2], acc[db][4 * r4 + 3]};
@@ -655,7 +683,7 @@ __global__ __launch_bounds__(256) void attn_sink_bwd_finish_kernel(BwdArgs a, in
     if (threadIdx.x == 0) a.dsinks[h] = -(part[0] + part[1] + part[2] + part[3]);
     return;
   }
-  const size_t plane4 = (size_t)a.T * a.Hkv * (kHeadDim / 4);  // float4 per partial plane
+  const size_t plane4 = (size_t)a.T * a.Hkv * (a.D / 4);  // float4 per partial plane
   const f32x4* p = reinterpret_cast<const f32x4*>(a.dkv_part);
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < plane4; i += (size_t)n_sum_blocks * blockDim.x) {
     f32x4 k4 = p[i], v4 = p[a.n_halves * plane4 + i];
@@ -670,31 +698,49 @@ __global__ __launch_bounds__(256) void attn_sink_bwd_finish_kernel(BwdArgs a, in
 
 }  // namespace
 
+template <int D>
+void launch_dkdv_d(const BwdArgs& a, dim3 grid, hipStream_t stream) {
+  if (a.kv_streams == 2) {
+    hipLaunchKernelGGL((attn_sink_bwd_dkdv_kernel<2, D>), grid, dim3(256), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL((attn_sink_bwd_dkdv_kernel<1, D>), grid, dim3(128), 0, stream, a);
+  }
+}
+
 hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream) {
   const long long nblocks = (long long)a.n_kblocks * a.B * a.Hkv * a.n_halves;
   if (nblocks <= 0) return hipSuccess;
-  if (a.kv_streams == 2) {
-    hipLaunchKernelGGL(attn_sink_bwd_dkdv_kernel<2>, dim3((unsigned)nblocks), dim3(256), 0, stream, a);
+  if (a.D == 128) {
+    launch_dkdv_d<128>(a, dim3((unsigned)nblocks), stream);
   } else {
-    hipLaunchKernelGGL(attn_sink_bwd_dkdv_kernel<1>, dim3((unsigned)nblocks), dim3(128), 0, stream, a);
+    launch_dkdv_d<64>(a, dim3((unsigned)nblocks), stream);
   }
   return hipGetLastError();
+}
+
+template <int D>
+void launch_dq_d(const BwdArgs& a, dim3 grid, hipStream_t stream) {
+  const dim3 block(256);
+  switch (a.hpw) {
+    case 4: hipLaunchKernelGGL((attn_sink_bwd_dq_kernel<4, D>), grid, block, 0, stream, a); break;
+    case 2: hipLaunchKernelGGL((attn_sink_bwd_dq_kernel<2, D>), grid, block, 0, stream, a); break;
+    default: hipLaunchKernelGGL((attn_sink_bwd_dq_kernel<1, D>), grid, block, 0, stream, a); break;
+  }
 }
 
 hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream) {
   const long long nblocks = (long long)a.n_qblocks * (a.Hq / a.hpw) * a.B;
   if (nblocks <= 0) return hipSuccess;
-  const dim3 grid((unsigned)nblocks), block(256);
-  switch (a.hpw) {
-    case 4: hipLaunchKernelGGL(attn_sink_bwd_dq_kernel<4>, grid, block, 0, stream, a); break;
-    case 2: hipLaunchKernelGGL(attn_sink_bwd_dq_kernel<2>, grid, block, 0, stream, a); break;
-    default: hipLaunchKernelGGL(attn_sink_bwd_dq_kernel<1>, grid, block, 0, stream, a); break;
+  if (a.D == 128) {
+    launch_dq_d<128>(a, dim3((unsigned)nblocks), stream);
+  } else {
+    launch_dq_d<64>(a, dim3((unsigned)nblocks), stream);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_bwd_finish(const BwdArgs& a, hipStream_t stream) {
-  const long long n4 = (long long)a.T * a.Hkv * (kHeadDim / 4);
+  const long long n4 = (long long)a.T * a.Hkv * (a.D / 4);
   long long nsum = (n4 + 255) / 256;
   if (nsum > 4096) nsum = 4096;
   if (a.n_halves == 1) nsum = 0;  // the dK/dV pass wrote dK and dV itself

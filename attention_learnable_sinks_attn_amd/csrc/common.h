@@ -18,6 +18,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+#include <utility>
+
 namespace attn_sink {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -25,7 +28,6 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kHeadDim = 64;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegInf = -__builtin_inff();
@@ -284,6 +286,74 @@ __device__ __forceinline__ void tile_copy_full(__amdgpu_buffer_rsrc_t rsrc, cons
   bdma16(rsrc, off[u & 1], 8u * u * row_bytes, tile + 1024 * u);
 }
 
+// f(std::integral_constant<int, i>()) for i = 0 .. N - 1, so that i can be a template argument
+// (for instance an LDS offset folded into an instruction).
+template <int N, int I = 0, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>());
+    static_for<N, I + 1>(std::forward<F>(f));
+  }
+}
+
+// ---- Head dimensions 64 and 128 ----
+// A row of D bf16 elements is stored in LDS as D / 64 "panels" of 64 elements, each panel laid out
+// exactly like the 64-element tiles above (swizzled 128-byte rows), so every fragment and
+// transposing read of a panel uses the same offsets. A K, V, Q or dO tile is always 8 KiB: 64 rows
+// at D = 64, 32 rows at D = 128; its panels follow each other (panel p at p * kPanelBytes).
+template <int D>
+struct Geo {
+  static_assert(D == 64 || D == 128, "head_dim 64 or 128");
+  static constexpr int kPanels = D / 64;             // 64-element panels per row
+  static constexpr int kChunks = D / 16;             // 16-wide k slices of a contraction over d
+  static constexpr int kDBlocks = D / 32;            // 32-row MFMA blocks over d (outputs)
+  static constexpr int kTileRows = 4096 / D;         // rows of an 8 KiB tile
+  static constexpr int kRowBlocks = kTileRows / 32;  // 32-row MFMA blocks of a tile
+  static constexpr int kPanelBytes = kTileRows * 128;
+  static constexpr int kTileBytes = 8192;
+  static constexpr int kCopies = kTileBytes / 1024;  // 1 KiB copies per tile
+  static constexpr int kCopiesPerPanel = kTileRows / 8;
+};
+
+// Byte offset, within an 8 KiB tile, of the A-operand fragment of contraction chunk c (d = 16c +
+// 8grp + 0..7) for the 32-row block `rb` (rows swap23-permuted): panel c / 4, slice c % 4.
+template <int D>
+__device__ __forceinline__ int frag_off(const int (&aoff)[4], int c, int rb) {
+  return (c / 4) * Geo<D>::kPanelBytes + 4096 * rb + aoff[c % 4];
+}
+
+// Copy u (0 .. kCopies - 1) of an 8 KiB tile of D-element rows: panel u / kCopiesPerPanel, rows
+// 8 (u % kCopiesPerPanel) + l / 8 (global row min(row0 + that, last), `stride` elements apart),
+// into LDS tile + 1024 u. At D = 64 this is tile_copy.
+template <int D>
+__device__ __forceinline__ void tile_copy_d(const __bf16* base, int row0, int last, int stride, unsigned char* tile,
+                                            int u, int lane) {
+  const int p = u / Geo<D>::kCopiesPerPanel;
+  const int r = 8 * (u % Geo<D>::kCopiesPerPanel) + (lane >> 3);
+  dma16(base + (size_t)min(row0 + r, last) * stride + 64 * p + 8 * ((lane & 7) ^ tile_swz(r)), tile + 1024 * u);
+}
+// The same copy of a full tile through a buffer resource based at the tile's first row (offsets
+// from tile_copy_offsets). At D = 64 this is tile_copy_full.
+template <int D>
+__device__ __forceinline__ void tile_copy_full_d(__amdgpu_buffer_rsrc_t rsrc, const unsigned (&off)[2],
+                                                 unsigned row_bytes, unsigned char* tile, int u) {
+  const int p = u / Geo<D>::kCopiesPerPanel;
+  const int rb = u % Geo<D>::kCopiesPerPanel;
+  bdma16(rsrc, off[rb & 1] + 128u * p, 8u * rb * row_bytes, tile + 1024 * u);
+}
+
+// lgkmcnt(0) for 32 untracked LDS reads (asm takes at most 30 operands: the second statement
+// only orders the other 16 results after the wait).
+__device__ __forceinline__ void wait_lds_into(u32x2 (&t)[32]) {
+  u32x2(&a)[16] = *reinterpret_cast<u32x2(*)[16]>(&t[0]);
+  u32x2(&b)[16] = *reinterpret_cast<u32x2(*)[16]>(&t[16]);
+  wait_lds_into(a);
+  asm volatile(""
+               : "+v"(b[0]), "+v"(b[1]), "+v"(b[2]), "+v"(b[3]), "+v"(b[4]), "+v"(b[5]), "+v"(b[6]), "+v"(b[7]),
+                 "+v"(b[8]), "+v"(b[9]), "+v"(b[10]), "+v"(b[11]), "+v"(b[12]), "+v"(b[13]), "+v"(b[14]),
+                 "+v"(b[15]));
+}
+
 // Work descriptors (filled on the host).
 struct FwdArgs {
   const __bf16* q;
@@ -291,7 +361,7 @@ struct FwdArgs {
   const __bf16* v;
   const float* sinks;
   const int32_t* cu;
-  void* out;             // [T, Hq, 64], fp32 or bf16 (out_bf16)
+  void* out;             // [T, Hq, D], fp32 or bf16 (out_bf16)
   float* lse;
   int out_bf16;
   int T, B, Hq, Hkv, G;  // G = Hq / Hkv
@@ -299,6 +369,7 @@ struct FwdArgs {
   int n_qblocks;         // ceil(max_seqlen / rows per workgroup)
   int causal, window;
   float scale_log2;      // softmax scale * log2(e)
+  int D;                 // head_dim: 64 or 128
 };
 
 struct BwdArgs {
@@ -317,7 +388,7 @@ struct BwdArgs {
   float* nlse;       // workspace: -LSE_i / scale (score units), [Hq, T]
   float* negd;       // workspace: -D_i = -rowsum(dO * O), [Hq, T]
   float* dsink_part; // per (head, row-block slot) partial sums of P_sink * D~, [Hq, n_slots]
-  float* dkv_part;   // dK / dV partial sums per head half: [2][n_halves][T][Hkv][64] (unscaled; unused with one half)
+  float* dkv_part;   // dK / dV partial sums per head half: [2][n_halves][T][Hkv][D] (unscaled; unused with one half)
   int n_slots;
   int n_halves;      // query-head halves of a KV group processed by separate dK/dV workgroups
   int T, B, Hq, Hkv, G;
@@ -328,18 +399,19 @@ struct BwdArgs {
   int causal, window;
   float scale;        // softmax scale
   float scale_log2;   // softmax scale * log2(e)
+  int D;              // head_dim: 64 or 128
 };
 
 struct DecodeArgs {
-  const __bf16* q;     // [Tq, Hq, 64]: the new queries, packed by cu_q
-  const __bf16* k;     // [Tk, Hkv, 64]: the caches, packed by cu_k
+  const __bf16* q;     // [Tq, Hq, D]: the new queries, packed by cu_q
+  const __bf16* k;     // [Tk, Hkv, D]: the caches, packed by cu_k
   const __bf16* v;
   const float* sinks;
   const int32_t* cu_q;
   const int32_t* cu_k;
-  void* out;           // [Tq, Hq, 64], fp32 or bf16 (out_bf16)
+  void* out;           // [Tq, Hq, D], fp32 or bf16 (out_bf16)
   float* lse;          // [Hq, Tq]
-  float* part_o;       // per (sequence, KV head, column group, chunk): [32 columns][64] unnormalised outputs
+  float* part_o;       // per (sequence, KV head, column group, chunk): [32 columns][D] unnormalised outputs
   float* part_ml;      // per (sequence, KV head, column group, chunk): [2][32] running max (log2), denominator
   int Tq, B, Hq, Hkv, G;
   int n_cols;          // max_q * G: the columns any (sequence, KV head) uses
@@ -349,6 +421,7 @@ struct DecodeArgs {
   int window;
   int out_bf16;
   float scale_log2;
+  int D;               // head_dim: 64 or 128
 };
 
 }  // namespace attn_sink

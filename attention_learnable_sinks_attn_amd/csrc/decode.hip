@@ -23,12 +23,18 @@ namespace attn_sink {
 
 namespace {
 
-constexpr int kDecTileKeys = 64;
-constexpr int kDecTileBytes = kDecTileKeys * kHeadDim * 2;  // one swizzled 64-key tile (K or V)
-constexpr int kDecSlotBytes = 2 * kDecTileBytes;             // K tile, then V tile
+constexpr int kDecTileBytes = 8192;              // one swizzled K or V tile (64 keys at D = 64, 32 at D = 128)
+constexpr int kDecSlotBytes = 2 * kDecTileBytes;  // K tile, then V tile
 constexpr int kDecRing = 3;
 
+// Head dim D = 64 or 128 (rows as 64-element panels in 8 KiB tiles; see Geo in common.h). Key chunks
+// are whole numbers of 64 keys for either D.
+template <int D>
 __global__ __launch_bounds__(64) void attn_sink_decode_partial_kernel(DecodeArgs a) {
+  using G_ = Geo<D>;
+  constexpr int kDecTileKeys = G_::kTileRows;
+  constexpr int MB = G_::kRowBlocks;
+  constexpr int NTR = G_::kDBlocks * MB * 4;
   __shared__ __attribute__((aligned(1024))) unsigned char ring[kDecRing * kDecSlotBytes];
 
   // The KV heads of one chunk of keys are neighbours in the launch, so that the rows they share
@@ -56,24 +62,25 @@ __global__ __launch_bounds__(64) void attn_sink_decode_partial_kernel(DecodeArgs
   // Keys of this chunk that some column can see. Chunks tile the keys from the 64-aligned start of
   // the first one any new query sees (key 0 without a window).
   const int k_vis = a.window > 0 ? max(0, lk - nq - a.window + 1) : 0;
-  const int k_base = k_vis & ~(kDecTileKeys - 1);
+  const int k_base = k_vis & ~63;
   const int k_lo = max(k_vis, k_base + chunk * a.chunk_keys);
   const int k_hi = min(lk, k_base + (chunk + 1) * a.chunk_keys);
 
   float m = kNegInf, lsum = 0.0f;  // running max (log2 units) and denominator, without the sink
-  f32x16 o[2];
-  o[0] = o[1] = zero_f32x16();
+  f32x16 o[G_::kDBlocks];
+#pragma unroll
+  for (int db = 0; db < G_::kDBlocks; ++db) o[db] = zero_f32x16();
 
   if (nq > 0 && k_lo < k_hi) {
     // Q^T as the B operand: lane holds column l32, d = 16c + 8grp + (0..7).
-    bf16x8 qf[4];
+    bf16x8 qf[G_::kChunks];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      qf[c] = load_bf16x8(a.q + ((size_t)(cq + min(j, nq - 1)) * a.Hq + hq) * kHeadDim + 16 * c + 8 * grp);
+    for (int c = 0; c < G_::kChunks; ++c) {
+      qf[c] = load_bf16x8(a.q + ((size_t)(cq + min(j, nq - 1)) * a.Hq + hq) * D + 16 * c + 8 * grp);
     }
-    const int kv_stride = a.Hkv * kHeadDim;
-    const __bf16* kbase = a.k + (size_t)ck * kv_stride + (size_t)g * kHeadDim;
-    const __bf16* vbase = a.v + (size_t)ck * kv_stride + (size_t)g * kHeadDim;
+    const int kv_stride = a.Hkv * D;
+    const __bf16* kbase = a.k + (size_t)ck * kv_stride + (size_t)g * D;
+    const __bf16* vbase = a.v + (size_t)ck * kv_stride + (size_t)g * D;
     // Full tiles go through buffer resources; in a partial last tile, keys past the end repeat
     // the last key (finite data; they are masked).
     const unsigned row_bytes = 2u * kv_stride;
@@ -87,14 +94,14 @@ __global__ __launch_bounds__(64) void attn_sink_decode_partial_kernel(DecodeArgs
         const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(vbase + (size_t)row0 * kv_stride, kDecTileKeys * row_bytes);
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-          tile_copy_full(rk, coff, row_bytes, slot, u);
-          tile_copy_full(rv, coff, row_bytes, slot + kDecTileBytes, u);
+          tile_copy_full_d<D>(rk, coff, row_bytes, slot, u);
+          tile_copy_full_d<D>(rv, coff, row_bytes, slot + kDecTileBytes, u);
         }
       } else {
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-          tile_copy(kbase, row0, lk - 1, kv_stride, slot, u, lane);
-          tile_copy(vbase, row0, lk - 1, kv_stride, slot + kDecTileBytes, u, lane);
+          tile_copy_d<D>(kbase, row0, lk - 1, kv_stride, slot, u, lane);
+          tile_copy_d<D>(vbase, row0, lk - 1, kv_stride, slot + kDecTileBytes, u, lane);
         }
       }
     };
@@ -121,13 +128,13 @@ __global__ __launch_bounds__(64) void attn_sink_decode_partial_kernel(DecodeArgs
       const unsigned vt_lds = ring_lds + (kt % kDecRing) * kDecSlotBytes + kDecTileBytes;
       const int k0 = kt * kDecTileKeys;
 
-      f32x16 s[2];
+      f32x16 s[MB];
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
+      for (int mb = 0; mb < MB; ++mb) {
         s[mb] = zero_f32x16();
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          s[mb] = mfma_32x32x16(*reinterpret_cast<const bf16x8*>(slot + 4096 * mb + aoff[c]), qf[c], s[mb]);
+        for (int c = 0; c < G_::kChunks; ++c) {
+          s[mb] = mfma_32x32x16(*reinterpret_cast<const bf16x8*>(slot + frag_off<D>(aoff, c, mb)), qf[c], s[mb]);
         }
       }
       // Per element: the key must lie in the chunk's range, exist, and be visible from the column.
@@ -136,7 +143,7 @@ __global__ __launch_bounds__(64) void attn_sink_decode_partial_kernel(DecodeArgs
           k0 < k_lo || k0 + kDecTileKeys > k_hi || k0 + kDecTileKeys - 1 > lk - nq || a.window > 0;
       if (need_mask) {
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
+        for (int mb = 0; mb < MB; ++mb) {
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int kj = k0 + 32 * mb + c_row(i, grp);
@@ -147,7 +154,7 @@ __global__ __launch_bounds__(64) void attn_sink_decode_partial_kernel(DecodeArgs
       }
       float t = kNegInf;
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
+      for (int mb = 0; mb < MB; ++mb) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) t = fmaxf(t, s[mb][i]);
       }
@@ -156,14 +163,14 @@ __global__ __launch_bounds__(64) void attn_sink_decode_partial_kernel(DecodeArgs
         const float mnew = fmaxf(m, tmax);
         const float alpha = mnew == kNegInf ? 1.0f : fast_exp2(m - mnew);
         lsum *= alpha;
-        o[0] *= alpha;
-        o[1] *= alpha;
+#pragma unroll
+        for (int db = 0; db < G_::kDBlocks; ++db) o[db] *= alpha;
         m = mnew;
       }
       const float moff = m == kNegInf ? 0.0f : m;  // nothing visible yet: exp2(-inf) = 0
-      bf16x8 pb[2][2];
+      bf16x8 pb[MB][2];
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
+      for (int mb = 0; mb < MB; ++mb) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const float p = fast_exp2(__builtin_fmaf(s[mb][i], a.scale_log2, -moff));
@@ -173,26 +180,27 @@ __global__ __launch_bounds__(64) void attn_sink_decode_partial_kernel(DecodeArgs
         pb[mb][0] = pack8(s[mb], 0);
         pb[mb][1] = pack8(s[mb], 1);
       }
-      u32x2 tr[16];  // V^T operands: [d block][key block][half][lo / hi]
-#pragma unroll
-      for (int db = 0; db < 2; ++db) {
-        tr[8 * db + 0] = ds_read_tr16_b64_asm<0>(vt_lds + toff[db][0]);
-        tr[8 * db + 1] = ds_read_tr16_b64_asm<0>(vt_lds + toff[db][1]);
-        tr[8 * db + 2] = ds_read_tr16_b64_asm<2048>(vt_lds + toff[db][0]);
-        tr[8 * db + 3] = ds_read_tr16_b64_asm<2048>(vt_lds + toff[db][1]);
-        tr[8 * db + 4] = ds_read_tr16_b64_asm<4096>(vt_lds + toff[db][0]);
-        tr[8 * db + 5] = ds_read_tr16_b64_asm<4096>(vt_lds + toff[db][1]);
-        tr[8 * db + 6] = ds_read_tr16_b64_asm<6144>(vt_lds + toff[db][0]);
-        tr[8 * db + 7] = ds_read_tr16_b64_asm<6144>(vt_lds + toff[db][1]);
-      }
+      // V^T operands: tr[4 (db MB + mb) + 2 cc + lo/hi], from panel db / 2 at rows 32mb + 16cc.
+      u32x2 tr[NTR];
+      static_for<G_::kDBlocks>([&](auto db_tag) {
+        constexpr int db = decltype(db_tag)::value;
+        constexpr int PO = (db / 2) * G_::kPanelBytes;
+        static_for<MB>([&](auto mb_tag) {
+          constexpr int mb = decltype(mb_tag)::value;
+          tr[4 * (db * MB + mb) + 0] = ds_read_tr16_b64_asm<PO + 4096 * mb>(vt_lds + toff[db % 2][0]);
+          tr[4 * (db * MB + mb) + 1] = ds_read_tr16_b64_asm<PO + 4096 * mb>(vt_lds + toff[db % 2][1]);
+          tr[4 * (db * MB + mb) + 2] = ds_read_tr16_b64_asm<PO + 4096 * mb + 2048>(vt_lds + toff[db % 2][0]);
+          tr[4 * (db * MB + mb) + 3] = ds_read_tr16_b64_asm<PO + 4096 * mb + 2048>(vt_lds + toff[db % 2][1]);
+        });
+      });
       wait_lds_into(tr);
 #pragma unroll
-      for (int db = 0; db < 2; ++db) {
+      for (int db = 0; db < G_::kDBlocks; ++db) {
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
+        for (int mb = 0; mb < MB; ++mb) {
 #pragma unroll
           for (int cc = 0; cc < 2; ++cc) {
-            const u32x2* tt = tr + 8 * db + 4 * mb + 2 * cc;
+            const u32x2* tt = tr + 4 * (db * MB + mb) + 2 * cc;
             o[db] = mfma_32x32x16(join_tr(tt[0], tt[1]), pb[mb][cc], o[db]);
           }
         }
@@ -203,11 +211,11 @@ __global__ __launch_bounds__(64) void attn_sink_decode_partial_kernel(DecodeArgs
   // This chunk's partial: running max, denominator, unnormalised output per column. Only the
   // columns of real (query, head) pairs are stored; the combine reads no other.
   const float ltot = sum_xor32(lsum);
-  float* po = a.part_o + (size_t)pidx * 32 * kHeadDim + l32 * kHeadDim;  // [32 columns][64 d]
+  float* po = a.part_o + (size_t)pidx * 32 * D + l32 * D;  // [32 columns][D]
   float* pml = a.part_ml + (size_t)pidx * 2 * 32;                        // [max, denominator][32 columns]
   if (col_ok) {
 #pragma unroll
-    for (int db = 0; db < 2; ++db) {
+    for (int db = 0; db < G_::kDBlocks; ++db) {
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
         *reinterpret_cast<f32x4*>(po + 32 * db + 8 * r4 + 4 * grp) =
@@ -221,12 +229,15 @@ __global__ __launch_bounds__(64) void attn_sink_decode_partial_kernel(DecodeArgs
   }
 }
 
-// One workgroup per (sequence, KV head, column): lane d of each of the four waves accumulates
-// output element d over every fourth chunk; the waves' sums meet in LDS.
+// One workgroup per (sequence, KV head, column): lane l of each of the four waves accumulates
+// output elements l, l + 64, ... (D / 64 of them) over every fourth chunk; the waves' sums meet in
+// LDS.
 constexpr int kCombineWaves = 4;
 
+template <int D>
 __global__ __launch_bounds__(64 * kCombineWaves) void attn_sink_decode_combine_kernel(DecodeArgs a) {
-  __shared__ float red[kCombineWaves][kHeadDim + 1];
+  constexpr int E = D / 64;  // output elements per lane
+  __shared__ float red[kCombineWaves][D + 1];
   const int c = blockIdx.x % a.n_cols;
   const int rest = blockIdx.x / a.n_cols;  // = b * Hkv + g
   const int g = rest % a.Hkv;
@@ -249,37 +260,44 @@ __global__ __launch_bounds__(64 * kCombineWaves) void attn_sink_decode_combine_k
   for (int ch = threadIdx.x; ch < a.n_chunks; ch += 64 * kCombineWaves) M = fmaxf(M, ml[(size_t)ch * 64]);
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-  if (lane == 0) red[w][kHeadDim] = M;
+  if (lane == 0) red[w][D] = M;
   __syncthreads();
 #pragma unroll
-  for (int i = 0; i < kCombineWaves; ++i) M = fmaxf(M, red[i][kHeadDim]);
+  for (int i = 0; i < kCombineWaves; ++i) M = fmaxf(M, red[i][D]);
   const float Ms = M == kNegInf ? 0.0f : M;
-  __syncthreads();  // red[.][kHeadDim] is reused below
+  __syncthreads();  // red[.][D] is reused below
 
-  float acc = 0.0f, L = 0.0f;
-  const float* po = a.part_o + p0 * 32 * kHeadDim + (c % 32) * kHeadDim + lane;
+  float acc[E], L = 0.0f;
+#pragma unroll
+  for (int e = 0; e < E; ++e) acc[e] = 0.0f;
+  const float* po = a.part_o + p0 * 32 * D + (c % 32) * D + lane;
 #pragma unroll 4
   for (int ch = w; ch < a.n_chunks; ch += kCombineWaves) {
     const float wt = fast_exp2(ml[(size_t)ch * 64] - Ms);  // 0 for an empty chunk (max -inf)
     L += wt * ml[(size_t)ch * 64 + 32];
-    acc += wt * po[(size_t)ch * 32 * kHeadDim];
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[e] += wt * po[(size_t)ch * 32 * D + 64 * e];
   }
-  red[w][lane] = acc;
-  if (lane == 0) red[w][kHeadDim] = L;
+#pragma unroll
+  for (int e = 0; e < E; ++e) red[w][lane + 64 * e] = acc[e];
+  if (lane == 0) red[w][D] = L;
   __syncthreads();
   if (w != 0) return;
   L = fast_exp2(sink2 - Ms);
 #pragma unroll
-  for (int i = 0; i < kCombineWaves; ++i) L += red[i][kHeadDim];
-  acc = 0.0f;
-#pragma unroll
-  for (int i = 0; i < kCombineWaves; ++i) acc += red[i][lane];
+  for (int i = 0; i < kCombineWaves; ++i) L += red[i][D];
   const float inv = L > 0.0f ? 1.0f / L : 0.0f;
   const size_t row = (size_t)(cq + j) * a.Hq + hq;
-  if (a.out_bf16) {
-    static_cast<__bf16*>(a.out)[row * kHeadDim + lane] = (__bf16)(acc * inv);
-  } else {
-    static_cast<float*>(a.out)[row * kHeadDim + lane] = acc * inv;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    float x = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kCombineWaves; ++i) x += red[i][lane + 64 * e];
+    if (a.out_bf16) {
+      static_cast<__bf16*>(a.out)[row * D + lane + 64 * e] = (__bf16)(x * inv);
+    } else {
+      static_cast<float*>(a.out)[row * D + lane + 64 * e] = x * inv;
+    }
   }
   if (lane == 0) a.lse[(size_t)hq * a.Tq + cq + j] = L > 0.0f ? (Ms + fast_log2(L)) * kLn2 : kNegInf;
 }
@@ -291,11 +309,19 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream, hipEvent_t con
   if (parts <= 0) return hipSuccess;
   hipError_t e;
   if (events && events[0] && (e = hipEventRecord(events[0], stream)) != hipSuccess) return e;
-  hipLaunchKernelGGL(attn_sink_decode_partial_kernel, dim3((unsigned)parts), dim3(64), 0, stream, a);
+  if (a.D == 128) {
+    hipLaunchKernelGGL(attn_sink_decode_partial_kernel<128>, dim3((unsigned)parts), dim3(64), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL(attn_sink_decode_partial_kernel<64>, dim3((unsigned)parts), dim3(64), 0, stream, a);
+  }
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (events && events[1] && (e = hipEventRecord(events[1], stream)) != hipSuccess) return e;
-  hipLaunchKernelGGL(attn_sink_decode_combine_kernel, dim3((unsigned)(a.B * a.Hkv * a.n_cols)),
-                     dim3(64 * kCombineWaves), 0, stream, a);
+  const dim3 cgrid((unsigned)(a.B * a.Hkv * a.n_cols)), cblock(64 * kCombineWaves);
+  if (a.D == 128) {
+    hipLaunchKernelGGL(attn_sink_decode_combine_kernel<128>, cgrid, cblock, 0, stream, a);
+  } else {
+    hipLaunchKernelGGL(attn_sink_decode_combine_kernel<64>, cgrid, cblock, 0, stream, a);
+  }
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (events && events[2] && (e = hipEventRecord(events[2], stream)) != hipSuccess) return e;
   return hipSuccess;

@@ -7,8 +7,12 @@
 // and the running denominator at exp(S_h - S_h) = 1, while the output accumulator starts at 0
 // because the sink has no value row. LSE = max + log(denominator) therefore includes the sink.
 //
+// Head dim D = 64 or 128 (rows stored as 64-element panels, tiles of 8 KiB: 64 keys at D = 64, 32
+// at D = 128; see Geo in common.h). Per wave 64 query rows at D = 64, 32 at D = 128 (whose O^T
+// accumulators are twice as tall).
+//
 // Work split. A workgroup of four waves owns HPW query heads that share one KV head (GQA) and
-// 4 / HPW consecutive blocks of 64 query rows of one sequence; wave w handles head hs*HPW + w%HPW
+// 4 / HPW consecutive blocks of query rows of one sequence; wave w handles head hs*HPW + w%HPW
 // and row block w/HPW. K and V tiles of 64 keys pass in pairs through a 4-slot LDS ring shared by
 // the workgroup's waves, filled by direct global->LDS copies one pair ahead (the waves split the
 // copies); one barrier per pair of tiles; a wave skips the tiles its rows cannot see. The tiles are stored with
@@ -36,10 +40,9 @@ namespace attn_sink {
 
 namespace {
 
-constexpr int kTileKeys = 64;
-constexpr int kTileBytes = kTileKeys * kHeadDim * 2;  // one swizzled 64-key tile (K or V)
-constexpr int kSlotBytes = 2 * kTileBytes;             // K tile, then V tile
-constexpr int kRing = 4;                               // LDS ring slots (two pairs of tiles)
+constexpr int kTileBytes = 8192;              // one swizzled K or V tile (64 keys at D = 64, 32 at D = 128)
+constexpr int kSlotBytes = 2 * kTileBytes;    // K tile, then V tile
+constexpr int kRing = 4;                      // LDS ring slots (two pairs of tiles)
 // Probabilities above this share of their row get the residual P.V product (see the tile body).
 // The largest ones dominate the rounding error of O: on peaked rows a quarter already removes
 // most of it, and the rows that reach it are few, so the extra products stay rare.
@@ -49,12 +52,15 @@ constexpr float kLazyMax = 8.0f;
 
 // HPW query heads of one KV group x RPW = 4 / HPW blocks of 64 rows per workgroup (four waves),
 // so that groups of fewer than four heads still share each K/V tile among four waves.
-template <int HPW>
+template <int HPW, int D>
 __global__ __launch_bounds__(256, 2) void attn_sink_fwd_kernel(FwdArgs a) {
-  constexpr int NB = 2;                                 // 32-query column blocks per wave
+  using G_ = Geo<D>;
+  constexpr int kTileKeys = G_::kTileRows;
+  constexpr int NB = D == 64 ? 2 : 1;                   // 32-query column blocks per wave
   constexpr int kRows = 32 * NB;                        // query rows per wave
   constexpr int RPW = 4 / HPW;                          // row blocks per workgroup
   constexpr int CPW = 2 * (kTileBytes / 1024) / 4;      // copies per wave and tile (K and V)
+  constexpr int NTR = G_::kDBlocks * G_::kRowBlocks * 4;  // transposing reads of V^T per tile
   __shared__ __attribute__((aligned(1024))) unsigned char ring[kRing * kSlotBytes];
 
   const int n_hs = a.Hq / HPW;
@@ -84,27 +90,27 @@ __global__ __launch_bounds__(256, 2) void attn_sink_fwd_kernel(FwdArgs a) {
   const bool rows_live = RPW == 1 || q0 < len;  // waves past the sequence end only copy
 
   // Q^T as the B operand of S^T = K Q^T: lane holds query q0 + 32nb + l32, d = 16c + 8grp + (0..7).
-  bf16x8 qf[NB][4];
+  bf16x8 qf[NB][G_::kChunks];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     const int qi = q0 + 32 * nb + l32;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
+    for (int c = 0; c < G_::kChunks; ++c) {
       // Rows past the end compute on the last row; their results are not stored.
-      qf[nb][c] = load_bf16x8(a.q + ((size_t)(cs + min(qi, len - 1)) * a.Hq + h) * kHeadDim + 16 * c + 8 * grp);
+      qf[nb][c] = load_bf16x8(a.q + ((size_t)(cs + min(qi, len - 1)) * a.Hq + h) * D + 16 * c + 8 * grp);
     }
   }
 
   const float sink_log2 = a.sinks[h] * kLog2e;
   float m[NB], lsum[NB];
-  f32x16 o[2][NB];
+  f32x16 o[G_::kDBlocks][NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     m[nb] = sink_log2;
     // The sink contributes exp2(S_h*log2e - m) = 1 to the denominator; count it once per query.
     lsum[nb] = (grp == 0 && sink_log2 != kNegInf) ? 1.0f : 0.0f;
-    o[0][nb] = zero_f32x16();
-    o[1][nb] = zero_f32x16();
+#pragma unroll
+    for (int db = 0; db < G_::kDBlocks; ++db) o[db][nb] = zero_f32x16();
   }
 
   // Keys some row of a row range can see: up to the last row (causal), or up to W - 1 past it (a
@@ -119,11 +125,11 @@ __global__ __launch_bounds__(256, 2) void attn_sink_fwd_kernel(FwdArgs a) {
   const int kw_begin = key_begin(q0);
   const int kw_end = rows_live ? key_end(q0 + kRows) : 0;
 
-  const int kv_stride = a.Hkv * kHeadDim;
-  const __bf16* kbase = a.k + (size_t)cs * kv_stride + (size_t)g * kHeadDim;
-  const __bf16* vbase = a.v + (size_t)cs * kv_stride + (size_t)g * kHeadDim;
+  const int kv_stride = a.Hkv * D;
+  const __bf16* kbase = a.k + (size_t)cs * kv_stride + (size_t)g * D;
+  const __bf16* vbase = a.v + (size_t)cs * kv_stride + (size_t)g * D;
 
-  // K and V tiles of 64 keys, swizzled (see tile_swz), in a 4-slot ring filled by direct
+  // K and V tiles of kTileKeys keys, swizzled (see tile_swz), in a 4-slot ring filled by direct
   // global->LDS copies issued one pair of tiles ahead; the waves split each tile's 16 copies (waves 0-1
   // the K tile, 2-3 the V tile). Full tiles go through a buffer resource; in the last, partial
   // tile keys past the sequence end repeat its last key (finite data; they are masked). V^T
@@ -144,10 +150,10 @@ __global__ __launch_bounds__(256, 2) void attn_sink_fwd_kernel(FwdArgs a) {
     if (row0 + kTileKeys <= len) {
       const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(nx_src, kTileKeys * row_bytes);
 #pragma unroll
-      for (int i = 0; i < CPW; ++i) tile_copy_full(rs, coff, row_bytes, tile, (u0 + i) & 7);
+      for (int i = 0; i < CPW; ++i) tile_copy_full_d<D>(rs, coff, row_bytes, tile, (u0 + i) & 7);
     } else {
 #pragma unroll
-      for (int i = 0; i < CPW; ++i) tile_copy(nx_src, 0, len - 1 - row0, kv_stride, tile, (u0 + i) & 7, lane);
+      for (int i = 0; i < CPW; ++i) tile_copy_d<D>(nx_src, 0, len - 1 - row0, kv_stride, tile, (u0 + i) & 7, lane);
     }
     nx_src += tile_elems;
     ++nx_kt;
@@ -186,15 +192,16 @@ __global__ __launch_bounds__(256, 2) void attn_sink_fwd_kernel(FwdArgs a) {
     // Wave-uniform: skip a tile that holds none of this wave's keys.
     if (RPW > 1 && (k0 >= kw_end || k0 + kTileKeys <= kw_begin)) return;
 
-    // S^T = K Q^T for two 32-key row blocks.
-    f32x16 s[2][NB];
+    // S^T = K Q^T for the tile's 32-key row blocks.
+    constexpr int MB = G_::kRowBlocks;
+    f32x16 s[MB][NB];
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
+    for (int mb = 0; mb < MB; ++mb) {
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) s[mb][nb] = zero_f32x16();
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(slot + 4096 * mb + aoff[c]);
+      for (int c = 0; c < G_::kChunks; ++c) {
+        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(slot + frag_off<D>(aoff, c, mb));
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) s[mb][nb] = mfma_32x32x16(ka, qf[nb][c], s[mb][nb]);
       }
@@ -205,7 +212,7 @@ __global__ __launch_bounds__(256, 2) void attn_sink_fwd_kernel(FwdArgs a) {
         const KeyBounds kb = key_bounds(q0 + 32 * nb + l32, len, a.causal, a.window);
         const unsigned cnt = (unsigned)max(kb.hi - kb.lo, 0);  // visible keys kb.lo + 1 .. kb.hi
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
+        for (int mb = 0; mb < MB; ++mb) {
           const int base = k0 + 32 * mb + 8 * grp - kb.lo - 1;  // key - (kb.lo + 1) for register 0
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
@@ -221,7 +228,7 @@ __global__ __launch_bounds__(256, 2) void attn_sink_fwd_kernel(FwdArgs a) {
     for (int nb = 0; nb < NB; ++nb) {
       float t = kNegInf;
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
+      for (int mb = 0; mb < MB; ++mb) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) t = fmaxf(t, s[mb][nb][i]);
       }
@@ -236,26 +243,27 @@ __global__ __launch_bounds__(256, 2) void attn_sink_fwd_kernel(FwdArgs a) {
         const float mnew = fmaxf(m[nb], tmax[nb]);
         const float alpha = mnew == kNegInf ? 1.0f : fast_exp2(m[nb] - mnew);
         lsum[nb] *= alpha;
-        o[0][nb] *= alpha;
-        o[1][nb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < G_::kDBlocks; ++db) o[db][nb] *= alpha;
         m[nb] = mnew;
       }
     }
 
-    // V^T operands for O^T += V^T P^T (rows d = 32db + l32, k slots = keys 32mb + 16cc + 8grp + 0..7).
-    u32x2 tr[16];  // [d block][key block][half][lo / hi]
-#pragma unroll
-    for (int db = 0; db < 2; ++db) {
-      const unsigned t0 = trb[db][0] + pair_off, t1 = trb[db][1] + pair_off;
-      tr[8 * db + 0] = ds_read_tr16_b64_asm<VT + 0>(t0);
-      tr[8 * db + 1] = ds_read_tr16_b64_asm<VT + 0>(t1);
-      tr[8 * db + 2] = ds_read_tr16_b64_asm<VT + 2048>(t0);
-      tr[8 * db + 3] = ds_read_tr16_b64_asm<VT + 2048>(t1);
-      tr[8 * db + 4] = ds_read_tr16_b64_asm<VT + 4096>(t0);
-      tr[8 * db + 5] = ds_read_tr16_b64_asm<VT + 4096>(t1);
-      tr[8 * db + 6] = ds_read_tr16_b64_asm<VT + 6144>(t0);
-      tr[8 * db + 7] = ds_read_tr16_b64_asm<VT + 6144>(t1);
-    }
+    // V^T operands for O^T += V^T P^T (rows d = 32db + l32, k slots = keys 32mb + 16cc + 8grp + 0..7):
+    // tr[4 (db MB + mb) + 2 cc + lo/hi], from panel db / 2 at rows 32mb + 16cc.
+    u32x2 tr[NTR];
+    static_for<G_::kDBlocks>([&](auto db_tag) {
+      constexpr int db = decltype(db_tag)::value;
+      constexpr int PO = VT + (db / 2) * G_::kPanelBytes;
+      const unsigned t0 = trb[db % 2][0] + pair_off, t1 = trb[db % 2][1] + pair_off;
+      static_for<MB>([&](auto mb_tag) {
+        constexpr int mb = decltype(mb_tag)::value;
+        tr[4 * (db * MB + mb) + 0] = ds_read_tr16_b64_asm<PO + 4096 * mb + 0>(t0);
+        tr[4 * (db * MB + mb) + 1] = ds_read_tr16_b64_asm<PO + 4096 * mb + 0>(t1);
+        tr[4 * (db * MB + mb) + 2] = ds_read_tr16_b64_asm<PO + 4096 * mb + 2048>(t0);
+        tr[4 * (db * MB + mb) + 3] = ds_read_tr16_b64_asm<PO + 4096 * mb + 2048>(t1);
+      });
+    });
 
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
@@ -274,9 +282,9 @@ __global__ __launch_bounds__(256, 2) void attn_sink_fwd_kernel(FwdArgs a) {
       const float pm = fast_exp2(tmax[nb] - moff);  // 0 for a fully masked row
       const bool split = wave_any(pm > kFwdSplitThreshold * sum_xor32(lsum[nb]));
       float rs = 0.0f;
-      bf16x8 pb[2][2];
+      bf16x8 pb[MB][2];
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
+      for (int mb = 0; mb < MB; ++mb) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const float p = fast_exp2(__builtin_fmaf(s[mb][nb][i], a.scale_log2, -moff));
@@ -290,25 +298,25 @@ __global__ __launch_bounds__(256, 2) void attn_sink_fwd_kernel(FwdArgs a) {
       // O^T += V^T P^T for this column block, contracting over the tile's 64 keys.
       if (nb == 0) wait_lds_into(tr);
 #pragma unroll
-      for (int db = 0; db < 2; ++db) {
+      for (int db = 0; db < G_::kDBlocks; ++db) {
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
+        for (int mb = 0; mb < MB; ++mb) {
 #pragma unroll
           for (int cc = 0; cc < 2; ++cc) {
-            const u32x2* t = tr + 8 * db + 4 * mb + 2 * cc;
+            const u32x2* t = tr + 4 * (db * MB + mb) + 2 * cc;
             o[db][nb] = mfma_32x32x16(join_tr(t[0], t[1]), pb[mb][cc], o[db][nb]);
           }
         }
       }
       if (split) {
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
+        for (int mb = 0; mb < MB; ++mb) {
 #pragma unroll
           for (int cc = 0; cc < 2; ++cc) {
             const bf16x8 pl = residual8(s[mb][nb], cc, pb[mb][cc]);
 #pragma unroll
-            for (int db = 0; db < 2; ++db) {
-              const u32x2* t = tr + 8 * db + 4 * mb + 2 * cc;
+            for (int db = 0; db < G_::kDBlocks; ++db) {
+              const u32x2* t = tr + 4 * (db * MB + mb) + 2 * cc;
               o[db][nb] = mfma_32x32x16(join_tr(t[0], t[1]), pl, o[db][nb]);
             }
           }
@@ -339,9 +347,9 @@ __global__ __launch_bounds__(256, 2) void attn_sink_fwd_kernel(FwdArgs a) {
     const float inv = ltot > 0.0f ? 1.0f / ltot : 0.0f;
     const int qi = q0 + 32 * nb + l32;
     if (qi < len) {  // also false for every lane of a wave past the sequence end
-      const size_t orow = ((size_t)(cs + qi) * a.Hq + h) * kHeadDim;
+      const size_t orow = ((size_t)(cs + qi) * a.Hq + h) * D;
 #pragma unroll
-      for (int db = 0; db < 2; ++db) {
+      for (int db = 0; db < G_::kDBlocks; ++db) {
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
           f32x4 val = {o[db][nb][4 * r4] * inv, o[db][nb][4 * r4 + 1] * inv, o[db][nb][4 * r4 + 2] * inv,
@@ -364,14 +372,23 @@ __global__ __launch_bounds__(256, 2) void attn_sink_fwd_kernel(FwdArgs a) {
 
 }  // namespace
 
+template <int D>
+void launch_fwd_d(const FwdArgs& a, dim3 grid, hipStream_t stream) {
+  const dim3 block(256);
+  switch (a.hpw) {
+    case 4: hipLaunchKernelGGL((attn_sink_fwd_kernel<4, D>), grid, block, 0, stream, a); break;
+    case 2: hipLaunchKernelGGL((attn_sink_fwd_kernel<2, D>), grid, block, 0, stream, a); break;
+    default: hipLaunchKernelGGL((attn_sink_fwd_kernel<1, D>), grid, block, 0, stream, a); break;
+  }
+}
+
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
   const long long nblocks = (long long)a.n_qblocks * (a.Hq / a.hpw) * a.B;
   if (nblocks <= 0) return hipSuccess;
-  const dim3 grid((unsigned)nblocks), block(256);
-  switch (a.hpw) {
-    case 4: hipLaunchKernelGGL(attn_sink_fwd_kernel<4>, grid, block, 0, stream, a); break;
-    case 2: hipLaunchKernelGGL(attn_sink_fwd_kernel<2>, grid, block, 0, stream, a); break;
-    default: hipLaunchKernelGGL(attn_sink_fwd_kernel<1>, grid, block, 0, stream, a); break;
+  if (a.D == 128) {
+    launch_fwd_d<128>(a, dim3((unsigned)nblocks), stream);
+  } else {
+    launch_fwd_d<64>(a, dim3((unsigned)nblocks), stream);
   }
   return hipGetLastError();
 }

@@ -5,7 +5,8 @@
 
 namespace attn_sink {
 
-constexpr int kFwdRowsPerWave = 64;   // queries per wave in the forward
+// Queries per wave in the forward: 64 at head_dim 64, 32 at head_dim 128.
+constexpr int fwd_rows_per_wave(int head_dim) { return head_dim == 128 ? 32 : 64; }
 constexpr int kDqRowsPerWave = 32;    // queries per wave in the row-parallel dQ / dSink pass
 constexpr int kKvKeysPerBlock = 64;   // keys per workgroup in the column-parallel dK / dV pass
 

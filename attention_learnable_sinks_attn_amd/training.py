@@ -50,8 +50,8 @@ def sink_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, sinks: tor
                    softmax_scale: Optional[float] = None, return_lse: bool = False):
     """Differentiable sink attention over a packed batch.
 
-    q [T, Hq, 64], k / v [T, Hkv, 64] bf16 (CUDA); sinks [Hq] fp32; cu_seqlens [B+1] int32 on the
-    same device. Returns out [T, Hq, 64] fp32 (and lse [Hq, T] fp32 if ``return_lse``).
+    q [T, Hq, D], k / v [T, Hkv, D] bf16 (CUDA; D = 64 or 128); sinks [Hq] fp32; cu_seqlens [B+1] int32 on the
+    same device. Returns out [T, Hq, D] fp32 (and lse [Hq, T] fp32 if ``return_lse``).
     """
     out, lse = _SinkAttentionFn.apply(q.contiguous(), k.contiguous(), v.contiguous(), sinks.contiguous(),
                                       cu_seqlens, int(max_seqlen), bool(causal), int(window), softmax_scale)

@@ -19,13 +19,14 @@
  *    cu_seqlens[b+1]-1 belong to sequence b. Attention never crosses a sequence boundary
  *    (same page, section "结合Flash Attention V3的序列并行技术": padding removed, tokens
  *    packed into one list). A fixed-shape batch is B = 1, cu_seqlens = {0, N}.
- *  - Tensors (device pointers, contiguous, row-major, base 16-byte aligned):
- *      q, dout   [T, Hq, 64]  bfloat16
- *      k, v      [T, Hkv, 64] bfloat16
+ *  - Tensors (device pointers, contiguous, row-major, base 16-byte aligned); D = head_dim, 64 or
+ *    128 (the pages' GPT-OSS layers use 64; 128 is the other common head size):
+ *      q, dout   [T, Hq, D]   bfloat16
+ *      k, v      [T, Hkv, D]  bfloat16
  *      sinks     [Hq]         float32 (one logit per query head, natural-log units, NOT scaled)
- *      out       [T, Hq, 64]  float32 (attn_sink_fwd may store bf16 instead: out_dtype)
+ *      out       [T, Hq, D]   float32 (attn_sink_fwd may store bf16 instead: out_dtype)
  *      lse       [Hq, T]      float32, natural log of the full denominator (sink included)
- *      dq        [T, Hq, 64]  float32;  dk, dv [T, Hkv, 64] float32;  dsinks [Hq] float32
+ *      dq        [T, Hq, D]   float32;  dk, dv [T, Hkv, D] float32;  dsinks [Hq] float32
  *      cu_seqlens [B+1] int32 on the device, cu[0] = 0, non-decreasing, cu[B] = T
  *  - GQA: query head h reads KV head h / (Hq / Hkv); Hq must be a multiple of Hkv.
  *  - Masks: causal != 0 lets query i see keys j <= i of its own sequence. window = W > 0 with
@@ -59,9 +60,9 @@ enum {
   ATTN_SINK_OK = 0,
   ATTN_SINK_ERR_NULL_PTR = -1,    /* a required pointer (or the shape struct) is NULL */
   ATTN_SINK_ERR_BAD_SHAPE = -2,   /* T < 0, B < 1, Hq < 1, Hkv < 1, Hq % Hkv != 0, max_seqlen < 0
-                                     or max_seqlen > T, max_seqlen * Hq * 64 >= 2^31 (offsets
+                                     or max_seqlen > T, max_seqlen * Hq * D >= 2^31 (offsets
                                      inside one sequence are 32-bit), or T * Hq > 2^34 (grid size) */
-  ATTN_SINK_ERR_UNSUPPORTED = -3, /* head_dim != 64, or out_dtype not ATTN_SINK_F32 (attn_sink_bwd)
+  ATTN_SINK_ERR_UNSUPPORTED = -3, /* head_dim not 64 or 128, or out_dtype not ATTN_SINK_F32 (attn_sink_bwd)
                                      or not ATTN_SINK_F32 / ATTN_SINK_BF16 (attn_sink_fwd) */
   ATTN_SINK_ERR_BAD_WINDOW = -4,  /* window < 0 (attn_sink_decode_fwd only) */
   ATTN_SINK_ERR_WORKSPACE = -5,   /* workspace NULL or smaller than attn_sink_bwd_workspace_bytes() */
@@ -80,7 +81,7 @@ typedef struct attn_sink_shape {
   int32_t max_seqlen;    /* >= every cu[b+1]-cu[b]; sizes the grid (a larger value only adds idle blocks) */
   int32_t num_heads_q;   /* Hq */
   int32_t num_heads_kv;  /* Hkv, divides Hq */
-  int32_t head_dim;      /* must be 64 */
+  int32_t head_dim;      /* D: 64 or 128 */
   float softmax_scale;   /* <= 0 selects 1/sqrt(head_dim) */
   int32_t out_dtype;     /* ATTN_SINK_F32; attn_sink_fwd also takes ATTN_SINK_BF16 (out rounded to
                             bf16, nearest even, e.g. for inference prefill). attn_sink_bwd needs the
@@ -88,7 +89,7 @@ typedef struct attn_sink_shape {
 } attn_sink_shape;
 
 /*
- * Forward: writes out [T, Hq, 64] (float32) and lse [Hq, T] (float32, natural log, sink included:
+ * Forward: writes out [T, Hq, D] (float32) and lse [Hq, T] (float32, natural log, sink included:
  * lse_i = log(sum_j exp(S_ij) + exp(S_h))). Rows of zero-length sequences are not touched (there
  * are none). Inputs are read only.
  */
@@ -101,14 +102,14 @@ int attn_sink_fwd(const void* q, const void* k, const void* v, const float* sink
  * (head, row), one dSink partial sum per (head, 32-row block), and, when the dK/dV pass splits a
  * KV group's query heads over two workgroups (even Hq/Hkv and fewer than 2048 key blocks of 64
  * over all sequences and KV heads, counted as num_seqs * ceil(max_seqlen / 64) * Hkv), fp32
- * dK/dV partial sums for each half (2 * 2 * T * Hkv * 64 floats); each region 256-byte aligned.
+ * dK/dV partial sums for each half (2 * 2 * T * Hkv * D floats); each region 256-byte aligned.
  * Returns 0 if `shape` is NULL or invalid.
  */
 size_t attn_sink_bwd_workspace_bytes(const attn_sink_shape* shape);
 
 /*
  * Backward of L with upstream gradient dout = dL/dO, given the forward's out and lse:
- *   dq [T, Hq, 64], dk / dv [T, Hkv, 64] (float32, summed over the query heads of each KV group),
+ *   dq [T, Hq, D], dk / dv [T, Hkv, D] (float32, summed over the query heads of each KV group),
  *   dsinks [Hq] (float32, dL/dS_h summed over every row of every sequence).
  * workspace: caller-owned device memory of at least attn_sink_bwd_workspace_bytes(shape) bytes;
  * its contents on entry do not matter and are clobbered. The result is deterministic: no atomics
@@ -164,8 +165,8 @@ int attn_sink_bwd_timed(const void* q, const void* k, const void* v, const float
  * "GPT-OSS中的带注意力槽的注意力机制"); results agree with attn_sink_fwd's rows to rounding, not
  * bitwise (the keys are summed in another order).
  *
- *   q      [Tq, Hq, 64] bf16;  k, v [Tk, Hkv, 64] bf16;  sinks [Hq] fp32
- *   out    [Tq, Hq, 64] fp32 (out_dtype ATTN_SINK_F32) or bf16 (ATTN_SINK_BF16)
+ *   q      [Tq, Hq, D] bf16;  k, v [Tk, Hkv, D] bf16;  sinks [Hq] fp32 (D = head_dim, 64 or 128)
+ *   out    [Tq, Hq, D] fp32 (out_dtype ATTN_SINK_F32) or bf16 (ATTN_SINK_BF16)
  *   lse    [Hq, Tq] fp32, natural log, sink included
  *   cu_seqlens_q / cu_seqlens_k  [B+1] int32 on the device, non-decreasing, Nq_b <= Lk_b (trusted)
  * Requires max_q * (Hq / Hkv) <= 1024 (the (new token, query head) pairs of one KV head, taken 32
@@ -181,7 +182,7 @@ typedef struct attn_sink_decode_shape {
   int32_t max_k;        /* >= every Lk_b, >= 0 (sizes the key chunks) */
   int32_t num_heads_q;  /* Hq */
   int32_t num_heads_kv; /* Hkv, divides Hq */
-  int32_t head_dim;     /* must be 64 */
+  int32_t head_dim;     /* 64 or 128 */
   float softmax_scale;  /* <= 0 selects 1/sqrt(head_dim) */
   int32_t out_dtype;    /* ATTN_SINK_F32 or ATTN_SINK_BF16 */
 } attn_sink_decode_shape;

@@ -84,7 +84,8 @@ def test_forward_argument_errors():
     assert fwd(lib, shape(hkv=0)) == -2
     assert fwd(lib, shape(maxlen=-1)) == -2
     assert fwd(lib, shape(maxlen=129)) == -2
-    assert fwd(lib, shape(d=128)) == -3
+    assert fwd(lib, shape(d=96)) == -3   # head_dim 64 and 128 only
+    assert fwd(lib, shape(d=32)) == -3
     assert fwd(lib, shape(dtype=2)) == -3  # bf16 (1) is a valid forward output dtype
     assert fwd(lib, shape(), q=PM) == -7
     assert fwd(lib, shape(), out=PM) == -7
@@ -166,7 +167,7 @@ def test_decode_argument_errors():
     assert decode(lib, dshape(max_q=9)) == -2    # above total_q
     assert decode(lib, dshape(max_k=301)) == -2  # above total_k
     assert decode(lib, dshape(max_q=0)) == -2    # new tokens but max_q = 0
-    assert decode(lib, dshape(d=128)) == -3
+    assert decode(lib, dshape(d=96)) == -3
     assert decode(lib, dshape(dtype=2)) == -3
     # at most 1024 (new token, query head) pairs per KV head
     assert decode(lib, dshape(tq=300, max_q=129, hq=8, hkv=1)) == -3

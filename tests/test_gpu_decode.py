@@ -90,6 +90,32 @@ def test_decode_small(name):
     check_against_oracle(d, out, lse, scale)
 
 
+D128_SMALL = ["g8_nq1", "g4_mixed_nq", "g2_window50", "neg_inf_sinks", "g8_nq4_bf16", "g1_nq32", "all_new_tokens"]
+
+
+@pytest.mark.parametrize("name", D128_SMALL)
+def test_decode_small_d128(name):
+    lengths, nq, hq, hkv, window, kw = SMALL[name]
+    kw = dict(kw)
+    out_dtype = kw.pop("out_dtype", torch.float32)
+    sink_value = kw.pop("sinks", None)
+    d = make_decode_inputs(lengths, nq, hq, hkv, 128, window=window, seed=12, **kw)
+    if sink_value is not None:
+        d.sinks.fill_(sink_value)
+    say(f"decode {name} d=128: Lk={lengths} nq={nq} heads {hq}/{hkv} window={window} out={out_dtype}")
+    out, lse = run_decode(d, out_dtype)
+    assert out.shape[2] == 128
+    check_against_oracle(d, out, lse)
+
+
+def test_decode_full_size_d128():
+    lengths = np.random.default_rng(0).integers(16384, 32768, 8, endpoint=True)
+    d = make_decode_inputs(lengths, 1, 64, 8, 128, seed=0)
+    say(f"decode 8 x 16k-32k cached tokens, d=128: Lk={[int(x) for x in lengths]}")
+    out, lse = run_decode(d, torch.bfloat16)
+    check_against_oracle(d, out, lse)
+
+
 def test_decode_empty_batch():
     d = make_decode_inputs((10, 20), 0, 8, 1, seed=1)
     say("decode: no new tokens")
@@ -122,16 +148,16 @@ def test_decode_full_size(name):
     check_against_oracle(d, out, lse)
 
 
-@pytest.mark.parametrize("window", [0, 128])
-def test_train_inference_consistency(window):
+@pytest.mark.parametrize("window,d", [(0, 64), (128, 64), (0, 128)])
+def test_train_inference_consistency(window, d):
     """Training forward over whole packed sequences vs the decode forward over their last tokens."""
     lengths = (1000, 3000, 517, 64, 2049)
     nq = (1, 4, 3, 2, 4)
-    inp = make_inputs(lengths, 64, 8, causal=True, window=window, seed=5)
+    inp = make_inputs(lengths, 64, 8, d, causal=True, window=window, seed=5)
     dev = torch.device("cuda:0")
     q, k, v = (t.to(dev).contiguous() for t in (inp.q, inp.k, inp.v))
     sinks, cu = inp.sinks.to(dev), inp.cu_seqlens.to(dev)
-    say(f"consistency: lengths {lengths} new tokens {nq} window {window}")
+    say(f"consistency: lengths {lengths} new tokens {nq} window {window} d={d}")
     out_t, lse_t = asa.fwd(q, k, v, sinks, cu, inp.max_seqlen, True, window)
     rows, cu_q = last_rows(inp.cu_seqlens, nq)
     rows_t = torch.tensor(rows, device=dev)

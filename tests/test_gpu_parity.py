@@ -120,15 +120,31 @@ SMALL_CASES = {
 }
 
 
-@pytest.mark.parametrize("name", list(SMALL_CASES))
-def test_small_parity(name):
+def _small(name, d):
     lengths, hq, hkv, causal, window, extra = SMALL_CASES[name]
-    inp = make_inputs(lengths, hq, hkv, 64, causal=causal, window=window, seed=7,
+    inp = make_inputs(lengths, hq, hkv, d, causal=causal, window=window, seed=7,
                       sink_scale=extra.get("sink_scale", 1.0), sinks_override=extra.get("sinks"))
     scale = extra.get("scale")
-    say(f"[gpu] small case {name}: lengths={lengths} hq={hq} hkv={hkv} causal={causal} window={window}")
+    say(f"[gpu] small case {name}: lengths={lengths} hq={hq} hkv={hkv} causal={causal} window={window} d={d}")
     g = run_gpu(inp, scale)
     check_full(inp, g, scale)
+
+
+@pytest.mark.parametrize("name", list(SMALL_CASES))
+def test_small_parity(name):
+    _small(name, 64)
+
+
+# head_dim 128: rows of two 64-element panels, 32-key tiles, and the dK/dV pass at one wave per SIMD
+D128_CASES = ["mha_causal_ragged", "gqa8_varlen_causal", "varlen_empty_ends", "gqa2_window37", "gqa8_window128",
+              "gqa4_noncausal", "mha_single_tokens", "window_int_max", "sink_neg_inf_window", "sink_plus20",
+              "sinks_x3", "scale_0p07", "gqa3_causal", "gqa6_window50", "band_gqa4_w40", "band_exact_tiles",
+              "exact_tiles", "one_half_window", "one_half_causal", "one_half_band"]
+
+
+@pytest.mark.parametrize("name", D128_CASES)
+def test_small_parity_d128(name):
+    _small(name, 128)
 
 
 def test_tiny_workload_full_parity():
@@ -145,9 +161,10 @@ def test_empty_input():
     assert torch.all(g["dsinks"] == 0)
 
 
-def test_backward_is_deterministic():
-    inp = make_inputs((700, 333), 16, 2, 64, causal=True, window=0, seed=2)
-    say("[gpu] determinism: two backward calls on the same inputs")
+@pytest.mark.parametrize("d", [64, 128])
+def test_backward_is_deterministic(d):
+    inp = make_inputs((700, 333), 16, 2, d, causal=True, window=0, seed=2)
+    say(f"[gpu] determinism: two backward calls on the same inputs, d={d}")
     g = run_gpu(inp, repeat_bwd=True)
     for a, b in zip((g["dq"], g["dk"], g["dv"], g["dsinks"]), g["again"]):
         assert torch.equal(a, b)
@@ -173,7 +190,7 @@ def _oracle_row_block(inp):
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("name", ["causal4k", "window4k", "band4k", "varlen_window"])
+@pytest.mark.parametrize("name", ["causal4k", "window4k", "band4k", "varlen_window", "causal4k_d128"])
 def test_full_size_every_element(name):
     inp = make_workload_inputs(name)
     say(f"[gpu] full-size workload {name}, every element: T={inp.total_tokens} B={len(inp.lengths)} "

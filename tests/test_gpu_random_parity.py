@@ -4,7 +4,8 @@ Each case draws a packed batch with a mix of empty, single-token, ragged and mul
 sequences; a GQA ratio from 1 to 8; causal, causal-window, non-causal or band masks; an optional
 softmax scale; and sinks that are ordinary, scaled x3, very large, or -inf on some heads. Every
 element of O, LSE, dQ, dK, dV and dSink is compared, to the same tolerances as the fixed cases.
-The draw depends only on the case index, so a failing case can be rerun by itself.
+The draw depends only on the case index, so a failing case can be rerun by itself. The first 24
+indices run at head_dim 64, twelve more at head_dim 128.
 """
 import math
 
@@ -61,11 +62,23 @@ def draw_case(idx: int) -> dict:
                 sinks=sinks, sink_scale=sink_scale, seed=100 + idx)
 
 
-@pytest.mark.parametrize("idx", range(N_CASES))
-def test_random_parity(idx):
+def _run_case(idx, d):
     c = draw_case(idx)
     say(f"[gpu] random case {idx}: lengths={c['lengths']} hq={c['hq']} hkv={c['hkv']} causal={c['causal']} "
-        f"window={c['window']} scale={c['scale']} sink_scale={c['sink_scale']} sinks={c['sinks']}")
-    inp = make_inputs(c["lengths"], c["hq"], c["hkv"], 64, causal=c["causal"], window=c["window"], seed=c["seed"],
+        f"window={c['window']} scale={c['scale']} sink_scale={c['sink_scale']} sinks={c['sinks']} d={d}")
+    inp = make_inputs(c["lengths"], c["hq"], c["hkv"], d, causal=c["causal"], window=c["window"], seed=c["seed"],
                       sink_scale=c["sink_scale"], sinks_override=c["sinks"])
     check_full(inp, run_gpu(inp, c["scale"]), c["scale"])
+
+
+@pytest.mark.parametrize("idx", range(N_CASES))
+def test_random_parity(idx):
+    _run_case(idx, 64)
+
+
+N_CASES_D128 = 12
+
+
+@pytest.mark.parametrize("idx", range(1000, 1000 + N_CASES_D128))
+def test_random_parity_d128(idx):
+    _run_case(idx, 128)

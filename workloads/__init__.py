@@ -71,10 +71,14 @@ def workload(name: str, seed: int = 0) -> Workload:
     if name == "long32k":
         return Workload(name, (32768,), 64, 8, sink_scale=3.0,
                         description="32768 tokens, GQA 64/8, causal, sinks x3")
+    if name == "causal4k_d128":
+        return Workload(name, (4096,), 64, 8, d=128,
+                        description="4096 tokens, GQA 64/8, head_dim 128, causal (beyond the pages' d = 64)")
     raise KeyError(name)
 
 
-WORKLOAD_NAMES = ("tiny", "causal4k", "window4k", "varlen_causal", "varlen_window", "long32k", "band4k")
+WORKLOAD_NAMES = ("tiny", "causal4k", "window4k", "varlen_causal", "varlen_window", "long32k", "band4k",
+                  "causal4k_d128")
 
 
 @dataclass
