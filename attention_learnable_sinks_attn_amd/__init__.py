@@ -16,7 +16,7 @@ from typing import Optional, Sequence
 
 import torch
 
-__all__ = ["fwd", "bwd", "bwd_noalloc", "decode_fwd", "bwd_workspace_bytes", "decode_workspace_bytes", "bwd_kernel_names",
+__all__ = ["fwd", "bwd", "bwd_noalloc", "decode_fwd", "decode_fwd_ordered", "bwd_workspace_bytes", "decode_workspace_bytes", "bwd_kernel_names",
            "decode_kernel_names", "check_cu_seqlens", "library_path", "load_library", "AttnSinkError",
            "ERROR_CODES", "HEAD_DIMS"]
 
@@ -91,6 +91,8 @@ def load_library() -> ctypes.CDLL:
     lib.attn_sink_decode_fwd_timed.argtypes = [vp, vp, vp, vp, i32, vp, vp, dshp, vp, sz, vp, vp, vp,
                                                ctypes.POINTER(ctypes.c_void_p), i32]
     lib.attn_sink_decode_fwd_timed.restype = i32
+    lib.attn_sink_decode_fwd_ordered.argtypes = [vp, vp, vp, vp, i32, vp, vp, dshp, vp, vp, vp]
+    lib.attn_sink_decode_fwd_ordered.restype = i32
     lib.attn_sink_decode_num_kernels.restype = i32
     lib.attn_sink_decode_kernel_name.argtypes = [i32]
     lib.attn_sink_decode_kernel_name.restype = ctypes.c_char_p
@@ -370,4 +372,42 @@ def decode_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, sinks: torch.T
         rc = lib.attn_sink_decode_fwd_timed(*args, arr, len(events))
     if rc != 0:
         raise AttnSinkError(rc, "attn_sink_decode_fwd")
+    return out, lse
+
+
+def decode_fwd_ordered(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, sinks: torch.Tensor,
+                       cu_seqlens_q: torch.Tensor, cu_seqlens_k: torch.Tensor, max_q: int, max_k: int,
+                       window: int = 0, softmax_scale: Optional[float] = None, out_dtype: torch.dtype = torch.float32,
+                       out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                       validate_seqlens: bool = False):
+    """Decode forward through attn_sink_decode_fwd_ordered: the same arguments and outputs as
+    ``decode_fwd`` (no workspace), with results equal bit for bit to ``fwd``'s rows for the same
+    tokens (causal, same window, scale and out_dtype); slower on long caches."""
+    lib = load_library()
+    dev = q.device
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _check(t, n, torch.bfloat16, dev)
+    _check(sinks, "sinks", torch.float32, dev)
+    _check(cu_seqlens_q, "cu_seqlens_q", torch.int32, dev)
+    _check(cu_seqlens_k, "cu_seqlens_k", torch.int32, dev)
+    _check_qkv(q, k, v, sinks, cu_seqlens_q, total_k=int(k.shape[0]))
+    if cu_seqlens_k.shape != cu_seqlens_q.shape:
+        raise ValueError(f"cu_seqlens_k {tuple(cu_seqlens_k.shape)} and cu_seqlens_q {tuple(cu_seqlens_q.shape)} differ")
+    Tq, Hq, d = q.shape
+    if out is None:
+        out = torch.empty((Tq, Hq, d), dtype=out_dtype, device=dev)
+    if lse is None:
+        lse = torch.empty((Hq, Tq), dtype=torch.float32, device=dev)
+    _check(out, "out", out_dtype, dev)
+    _check(lse, "lse", torch.float32, dev)
+    _shape_of(out, "out", (Tq, Hq, d))
+    _shape_of(lse, "lse", (Hq, Tq))
+    if validate_seqlens:
+        check_cu_seqlens(cu_seqlens_q, Tq, max_q, "cu_seqlens_q")
+        check_cu_seqlens(cu_seqlens_k, int(k.shape[0]), max_k, "cu_seqlens_k")
+    shape = make_decode_shape(q, k, cu_seqlens_q, max_q, max_k, softmax_scale, out_dtype)
+    rc = lib.attn_sink_decode_fwd_ordered(_ptr(q), _ptr(k), _ptr(v), _ptr(sinks), int(window), _ptr(cu_seqlens_q),
+                                          _ptr(cu_seqlens_k), ctypes.byref(shape), _ptr(out), _ptr(lse), _stream(dev))
+    if rc != 0:
+        raise AttnSinkError(rc, "attn_sink_decode_fwd_ordered")
     return out, lse

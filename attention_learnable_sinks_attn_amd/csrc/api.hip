@@ -166,6 +166,10 @@ int bwd_impl(const void* q, const void* k, const void* v, const float* sinks, co
 }
 
 // ---- decode ----
+float resolve_decode_scale(const attn_sink_decode_shape* s) {
+  return s->softmax_scale > 0.0f ? s->softmax_scale : 1.0f / sqrtf((float)s->head_dim);
+}
+
 int check_decode_shape(const attn_sink_decode_shape* s) {
   if (s == nullptr) return ATTN_SINK_ERR_NULL_PTR;
   if (s->total_q < 0 || s->total_k < 0 || s->num_seqs < 1 || s->max_q < 0 || s->max_k < 0 ||
@@ -399,8 +403,7 @@ int attn_sink_decode_fwd_timed(const void* q, const void* k, const void* v, cons
   a.window = clamp_window(window, shape->max_k);
   a.out_bf16 = shape->out_dtype == ATTN_SINK_BF16 ? 1 : 0;
   a.D = shape->head_dim;
-  const float scale = shape->softmax_scale > 0.0f ? shape->softmax_scale : 1.0f / sqrtf((float)shape->head_dim);
-  a.scale_log2 = scale * kLog2e;
+  a.scale_log2 = resolve_decode_scale(shape) * kLog2e;
   return launch_decode(a, stream, ev) == hipSuccess ? ATTN_SINK_OK : ATTN_SINK_ERR_HIP;
 }
 
@@ -409,6 +412,41 @@ int attn_sink_decode_fwd(const void* q, const void* k, const void* v, const floa
                          void* workspace, size_t workspace_bytes, void* out, float* lse, hipStream_t stream) {
   return attn_sink_decode_fwd_timed(q, k, v, sinks, window, cu_seqlens_q, cu_seqlens_k, shape, workspace,
                                     workspace_bytes, out, lse, stream, nullptr, 0);
+}
+
+int attn_sink_decode_fwd_ordered(const void* q, const void* k, const void* v, const float* sinks, int window,
+                                 const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                 const attn_sink_decode_shape* shape, void* out, float* lse, hipStream_t stream) {
+  int rc = check_decode_shape(shape);
+  if (rc) return rc;
+  if (window < 0) return ATTN_SINK_ERR_BAD_WINDOW;
+  if (sinks == nullptr || cu_seqlens_q == nullptr || cu_seqlens_k == nullptr) return ATTN_SINK_ERR_NULL_PTR;
+  if (shape->total_q > 0 && (!q || !out || !lse)) return ATTN_SINK_ERR_NULL_PTR;
+  if (shape->total_k > 0 && (!k || !v)) return ATTN_SINK_ERR_NULL_PTR;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return ATTN_SINK_ERR_ALIGN;
+  if (shape->total_q == 0) return ATTN_SINK_OK;
+
+  DecodeArgs a = {};
+  a.q = static_cast<const __bf16*>(q);
+  a.k = static_cast<const __bf16*>(k);
+  a.v = static_cast<const __bf16*>(v);
+  a.sinks = sinks;
+  a.cu_q = cu_seqlens_q;
+  a.cu_k = cu_seqlens_k;
+  a.out = out;
+  a.lse = lse;
+  a.Tq = shape->total_q;
+  a.B = shape->num_seqs;
+  a.Hq = shape->num_heads_q;
+  a.Hkv = shape->num_heads_kv;
+  a.G = a.Hq / a.Hkv;
+  a.n_cols = shape->max_q * a.G;
+  a.n_cg = decode_col_groups(shape);
+  a.window = clamp_window(window, shape->max_k);
+  a.out_bf16 = shape->out_dtype == ATTN_SINK_BF16 ? 1 : 0;
+  a.D = shape->head_dim;
+  a.scale_log2 = resolve_decode_scale(shape) * kLog2e;
+  return launch_decode_ordered(a, stream) == hipSuccess ? ATTN_SINK_OK : ATTN_SINK_ERR_HIP;
 }
 
 int attn_sink_decode_num_kernels(void) { return kDecodeNumKernels; }

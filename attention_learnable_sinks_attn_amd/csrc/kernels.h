@@ -25,4 +25,8 @@ hipError_t launch_bwd_finish(const BwdArgs& a, hipStream_t stream);  // dK, dV =
 // (a NULL entry records nothing at that point).
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream, hipEvent_t const* events);
 
+// Decode forward in the training forward's key order (no split over the keys, no workspace); uses
+// q, k, v, sinks, cu_q, cu_k, out, lse, B, Hq, Hkv, G, n_cg, window, out_bf16, scale_log2, D.
+hipError_t launch_decode_ordered(const DecodeArgs& a, hipStream_t stream);
+
 }  // namespace attn_sink

@@ -224,6 +224,23 @@ const char* attn_sink_decode_kernel_name(int i);
 int attn_sink_check_cu_seqlens(const int32_t* cu_seqlens_host, int32_t num_seqs, int32_t total_tokens,
                                int32_t max_seqlen);
 
+/*
+ * Decode forward whose results equal the training forward's, bit for bit: out and lse of new
+ * query j of sequence b are exactly attn_sink_fwd's (causal, same window, scale and out_dtype) for
+ * row Lk_b - Nq_b + j of that sequence run over its whole cached K/V. Same arguments, shapes and
+ * limits as attn_sink_decode_fwd (max_q * (Hq / Hkv) <= 1024), but no workspace: each (sequence,
+ * KV head, group of 32 (new token, query head) pairs) is one wave that streams every key its
+ * queries see in the training forward's tile order, with the training forward's own tile
+ * arithmetic, instead of splitting the keys over waves; it is correspondingly slower on long
+ * caches. For rollout engines that must reproduce the trainer's log-probabilities exactly: the
+ * pages trace their RL training instability to the inference engine's sink forward and the
+ * training kernel disagreeing (nmedialink.com "惊爆！GPT-OSS-20B强化学习…", section
+ * "纠正训练与推理不一致问题", Fig. 4). Errors as attn_sink_decode_fwd (no ATTN_SINK_ERR_WORKSPACE).
+ */
+int attn_sink_decode_fwd_ordered(const void* q, const void* k, const void* v, const float* sinks, int window,
+                                 const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                 const attn_sink_decode_shape* shape, void* out, float* lse, hipStream_t stream);
+
 /* Number of kernels attn_sink_bwd enqueues, and the name of kernel i (static string, or NULL). */
 int attn_sink_bwd_num_kernels(void);
 const char* attn_sink_bwd_kernel_name(int i);

@@ -170,6 +170,64 @@ def test_train_inference_consistency(window, d):
     assert do <= CONSIST_TOL["out"] and dl <= CONSIST_TOL["lse"]
 
 
+ORDERED_CASES = {
+    # name: (lengths, new tokens per sequence, Hq, Hkv, d, window, sinks kwargs, out dtype)
+    "g8_causal": ((1000, 3000, 517, 64, 2049), (1, 4, 3, 2, 4), 64, 8, 64, 0, {}, torch.float32),
+    "g8_window128": ((1000, 3000, 517, 64, 2049), (1, 4, 3, 2, 4), 64, 8, 64, 128, {}, torch.float32),
+    "g8_sinks_x3_bf16": ((700, 33, 1500), (2, 1, 5), 16, 2, 64, 0, {"sink_scale": 3.0}, torch.bfloat16),
+    "g4_window7_neg_inf": ((300, 129, 64), (3, 2, 1), 8, 2, 64, 7, {"sinks_override": [float("-inf")] * 8},
+                           torch.float32),
+    "g1_many_tokens": ((200, 90), (40, 17), 2, 2, 64, 0, {}, torch.float32),
+    "d128_causal": ((1000, 3000, 517, 64, 2049), (1, 4, 3, 2, 4), 64, 8, 128, 0, {}, torch.float32),
+    "d128_window50": ((900, 77), (3, 2), 16, 2, 128, 50, {}, torch.float32),
+}
+
+
+@pytest.mark.parametrize("name", sorted(ORDERED_CASES))
+def test_ordered_decode_equals_training_forward_bitwise(name):
+    """attn_sink_decode_fwd_ordered reproduces the training forward's rows bit for bit (the opt-in
+    answer to the train/inference mismatch); the default split-KV decode agrees to rounding."""
+    lengths, nq, hq, hkv, d, window, kw, out_dtype = ORDERED_CASES[name]
+    inp = make_inputs(lengths, hq, hkv, d, causal=True, window=window, seed=6, **kw)
+    dev = torch.device("cuda:0")
+    q, k, v = (t.to(dev).contiguous() for t in (inp.q, inp.k, inp.v))
+    sinks, cu = inp.sinks.to(dev), inp.cu_seqlens.to(dev)
+    say(f"ordered decode {name}: lengths {lengths} new tokens {nq} heads {hq}/{hkv} d={d} window {window}")
+    out_t, lse_t = asa.fwd(q, k, v, sinks, cu, inp.max_seqlen, True, window, out_dtype=out_dtype)
+    rows, cu_q = last_rows(inp.cu_seqlens, nq)
+    rows_t = torch.tensor(rows, device=dev)
+    out_d, lse_d = asa.decode_fwd_ordered(q[rows_t].contiguous(), k, v, sinks, cu_q.to(dev), cu, max(nq),
+                                          inp.max_seqlen, window=window, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    ref_o, ref_l = out_t[rows_t], lse_t[:, rows_t]
+    diff = (out_d.float() - ref_o.float()).abs().max().item()
+    say(f"  ordered decode vs training forward: out max-abs diff {diff:.3e}, "
+        f"equal: out {torch.equal(out_d, ref_o)}, lse {torch.equal(lse_d, ref_l)}")
+    assert torch.equal(out_d, ref_o)
+    assert torch.equal(lse_d, ref_l)
+    # and against the oracle, like the split-KV decode
+    dd = make_decode_inputs(tuple(lengths), nq, hq, hkv, d, window=window, seed=0)
+    dd.q, dd.k, dd.v, dd.sinks = inp.q[torch.tensor(rows)], inp.k, inp.v, inp.sinks
+    dd.cu_q, dd.cu_k = cu_q, inp.cu_seqlens
+    check_against_oracle(dd, out_d, lse_d)
+
+
+def test_ordered_decode_handles_empty_sequences():
+    inp = make_inputs((0, 300, 1, 0, 70), 8, 2, 64, causal=True, seed=9)
+    dev = torch.device("cuda:0")
+    q, k, v = (t.to(dev).contiguous() for t in (inp.q, inp.k, inp.v))
+    sinks, cu = inp.sinks.to(dev), inp.cu_seqlens.to(dev)
+    say("ordered decode with empty sequences and sequences without new tokens")
+    out_t, lse_t = asa.fwd(q, k, v, sinks, cu, inp.max_seqlen, True, 0)
+    nq = (0, 3, 1, 0, 0)
+    rows, cu_q = last_rows(inp.cu_seqlens, nq)
+    rows_t = torch.tensor(rows, device=dev)
+    out_d, lse_d = asa.decode_fwd_ordered(q[rows_t].contiguous(), k, v, sinks, cu_q.to(dev), cu, max(nq),
+                                          inp.max_seqlen)
+    torch.cuda.synchronize()
+    assert torch.equal(out_d, out_t[rows_t]) and torch.equal(lse_d, lse_t[:, rows_t])
+
+
 def test_decode_timed_records_only_the_given_events():
     """attn_sink_decode_fwd_timed with a NULL entry: results unchanged, the given events bracket the
     partial kernel."""
