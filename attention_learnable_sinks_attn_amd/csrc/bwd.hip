@@ -205,71 +205,76 @@ __global__ __launch_bounds__(128 * NS, D == 64 ? 2 : 1) void attn_sink_bwd_dkdv_
   // One step: S' = Q K^T - LSE/scale and dP' = dO V^T - D for the 32 rows x 32 keys (the row
   // values preloaded as the accumulators; C: lane = key, registers = rows 16(i/8) + 8grp + i%8),
   // P = exp2(S' * scale * log2e), dS = P dP'; then dV^T += dO^T P and dK^T += Q^T dS. When some
-  // probability of the step exceeds kSplitThreshold, the step runs a second time in residual
-  // mode, multiplying the bf16 rounding residuals of P and dS instead (same instructions, so the
-  // accumulators are not split over two code paths).
+  // probability of the step exceeds kSplitThresholdDk (kSplitThreshold), the bf16 rounding
+  // residuals of dS (and of P) are multiplied too, right after the main products.
   auto step = [&](auto si_tag, auto sub_tag, int i0, bool need_mask) {
     constexpr int SI = decltype(si_tag)::value, SUB = decltype(sub_tag)::value;
     constexpr int SO = SI * kKvSlotBytes + 4096 * SUB;  // 32-row block SUB of slot SI's tiles
     const unsigned char* slot = ring + SO;
     const float* lp = reinterpret_cast<const float*>(ring + SI * kKvSlotBytes + 2 * kKvTileBytes) + kKvSub * SUB;
-    bool residual = false;
-    bool again;
-    do {
-      f32x16 sc = load_rows16(lp, grp);
-      f32x16 dp = load_rows16(lp + kKvRows, grp);  // -D rows follow the kKvRows -LSE/scale rows
+    f32x16 sc = load_rows16(lp, grp);
+    f32x16 dp = load_rows16(lp + kKvRows, grp);  // -D rows follow the kKvRows -LSE/scale rows
 #pragma unroll
-      for (int c = 0; c < G_::kChunks; ++c) {
-        sc = mfma_32x32x16(*reinterpret_cast<const bf16x8*>(slot + frag_off<D>(aoff, c, 0)), kf[c], sc);
-        dp = mfma_32x32x16(*reinterpret_cast<const bf16x8*>(slot + kKvTileBytes + frag_off<D>(aoff, c, 0)), vf[c],
-                           dp);
-      }
-      u32x2 tr[kNtr];
-      tr_all(std::integral_constant<int, SO>(), tr);
-      if (need_mask) {
-        // Row of register i: i0 + 8grp + r_i with r_i = 16(i/8) + i%8. Key kj is seen by the
-        // rows lo .. hi: from the key itself (causal) or W - 1 rows before it (a non-causal
-        // window), up to W - 1 rows after it (any window), within the sequence; none if the key
-        // is past the end. (The empty asm keeps the arithmetic in this branch.)
-        int kj = k0 + l32;
-        asm volatile("" : "+v"(kj));
-        const int lo = a.causal ? kj : (a.window > 0 ? kj - a.window + 1 : 0);
-        const int hi = kj >= len ? lo - 1 : (a.window > 0 ? min(len - 1, kj + a.window - 1) : len - 1);
-        const unsigned cnt = (unsigned)max(hi - lo + 1, 0);
-        const int base = i0 + 8 * grp - lo;  // row - lo for r_i = 0
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          sc[i] = in_span(base + 16 * (i >> 3) + (i & 7), cnt) ? sc[i] : kNegInf;
-        }
-      }
-      float pmax = 0.0f;
+    for (int c = 0; c < G_::kChunks; ++c) {
+      sc = mfma_32x32x16(*reinterpret_cast<const bf16x8*>(slot + frag_off<D>(aoff, c, 0)), kf[c], sc);
+      dp = mfma_32x32x16(*reinterpret_cast<const bf16x8*>(slot + kKvTileBytes + frag_off<D>(aoff, c, 0)), vf[c],
+                         dp);
+    }
+    u32x2 tr[kNtr];
+    tr_all(std::integral_constant<int, SO>(), tr);
+    if (need_mask) {
+      // Row of register i: i0 + 8grp + r_i with r_i = 16(i/8) + i%8. Key kj is seen by the
+      // rows lo .. hi: from the key itself (causal) or W - 1 rows before it (a non-causal
+      // window), up to W - 1 rows after it (any window), within the sequence; none if the key
+      // is past the end. (The empty asm keeps the arithmetic in this branch.)
+      int kj = k0 + l32;
+      asm volatile("" : "+v"(kj));
+      const int lo = a.causal ? kj : (a.window > 0 ? kj - a.window + 1 : 0);
+      const int hi = kj >= len ? lo - 1 : (a.window > 0 ? min(len - 1, kj + a.window - 1) : len - 1);
+      const unsigned cnt = (unsigned)max(hi - lo + 1, 0);
+      const int base = i0 + 8 * grp - lo;  // row - lo for r_i = 0
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const float p = fast_exp2(sc[i] * a.scale_log2);
-        pmax = fmaxf(pmax, p);
-        sc[i] = p;
-        dp[i] *= p;
+        sc[i] = in_span(base + 16 * (i >> 3) + (i & 7), cnt) ? sc[i] : kNegInf;
       }
-      bf16x8 pb0 = pack8(sc, 0), pb1 = pack8(sc, 1);
-      bf16x8 sb0 = pack8(dp, 0), sb1 = pack8(dp, 1);
-      if (residual) {
-        pb0 = residual8(sc, 0, pb0);
-        pb1 = residual8(sc, 1, pb1);
-        sb0 = residual8(dp, 0, sb0);
-        sb1 = residual8(dp, 1, sb1);
-      }
-      wait_lds_into(tr);
+    }
+    float pmax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float p = fast_exp2(sc[i] * a.scale_log2);
+      pmax = fmaxf(pmax, p);
+      sc[i] = p;
+      dp[i] *= p;
+    }
+    const bf16x8 pb0 = pack8(sc, 0), pb1 = pack8(sc, 1);
+    const bf16x8 sb0 = pack8(dp, 0), sb1 = pack8(dp, 1);
+    wait_lds_into(tr);
+#pragma unroll
+    for (int db = 0; db < G_::kDBlocks; ++db) {
+      const u32x2* t = tr + 8 * db;
+      dv[db] = mfma_32x32x16(join_tr(t[2], t[3]), pb0, dv[db]);
+      dv[db] = mfma_32x32x16(join_tr(t[6], t[7]), pb1, dv[db]);
+      dk[db] = mfma_32x32x16(join_tr(t[0], t[1]), sb0, dk[db]);
+      dk[db] = mfma_32x32x16(join_tr(t[4], t[5]), sb1, dk[db]);
+    }
+    if (wave_any(pmax > kSplitThresholdDk)) {
+      const bf16x8 sl0 = residual8(dp, 0, sb0), sl1 = residual8(dp, 1, sb1);
 #pragma unroll
       for (int db = 0; db < G_::kDBlocks; ++db) {
         const u32x2* t = tr + 8 * db;
-        dv[db] = mfma_32x32x16(join_tr(t[2], t[3]), pb0, dv[db]);
-        dv[db] = mfma_32x32x16(join_tr(t[6], t[7]), pb1, dv[db]);
-        dk[db] = mfma_32x32x16(join_tr(t[0], t[1]), sb0, dk[db]);
-        dk[db] = mfma_32x32x16(join_tr(t[4], t[5]), sb1, dk[db]);
+        dk[db] = mfma_32x32x16(join_tr(t[0], t[1]), sl0, dk[db]);
+        dk[db] = mfma_32x32x16(join_tr(t[4], t[5]), sl1, dk[db]);
       }
-      again = !residual && wave_any(pmax > kSplitThreshold);
-      residual = true;
-    } while (again);
+      if (wave_any(pmax > kSplitThreshold)) {
+        const bf16x8 pl0 = residual8(sc, 0, pb0), pl1 = residual8(sc, 1, pb1);
+#pragma unroll
+        for (int db = 0; db < G_::kDBlocks; ++db) {
+          const u32x2* t = tr + 8 * db;
+          dv[db] = mfma_32x32x16(join_tr(t[2], t[3]), pl0, dv[db]);
+          dv[db] = mfma_32x32x16(join_tr(t[6], t[7]), pl1, dv[db]);
+        }
+      }
+    }
   };
 
   // The next step to issue (wave-uniform): tile index, first row and offsets.
@@ -458,10 +463,7 @@ __global__ __launch_bounds__(256, 2) void attn_sink_bwd_dq_kernel(BwdArgs a) {
   const float nd = -sum_xor32(dpart);                              // -D_i
   const float nl = -a.lse[(size_t)h * a.T + cs + qc] / a.scale;   // -LSE_i / scale
   const float lse2 = -nl * a.scale_log2;                           // LSE_i * log2(e)
-  if (qok && grp == 0) {
-    a.negd[(size_t)h * a.T + cs + qi] = nd;
-    a.nlse[(size_t)h * a.T + cs + qi] = nl;
-  }
+  if (qok && grp == 0) a.nlse[(size_t)h * a.T + cs + qi] = nl;
   float dsum = 0.0f;
   f32x16 acc[G_::kDBlocks];  // dQ^T, [d block]
 #pragma unroll
@@ -545,11 +547,10 @@ __global__ __launch_bounds__(256, 2) void attn_sink_bwd_dq_kernel(BwdArgs a) {
     const bool need_mask = k0 > mask_hi || k0 < mask_lo;
     // One tile: S^T = K Q^T and dP^T = V dO^T (rows = keys, loaded with the swap23 permutation),
     // P = exp2(S*scale*log2e - LSE*log2e), dS = P (dP - D), dQ^T += K^T dS^T, one 32-key block
-    // after the other so that block 1's softmax overlaps block 0's dQ products. Returns the
-    // tile's largest probability. When it exceeds kSplitThreshold, the tile runs a second time in
-    // residual mode, multiplying the bf16 rounding residual of dS instead (its LDS offset goes
-    // through an empty asm, so that none of the first pass's loads are kept for it).
-    auto tile = [&](bool residual, unsigned lds_off) -> float {
+    // after the other so that block 1's softmax overlaps block 0's dQ products. A block whose
+    // largest probability exceeds kSplitThreshold also multiplies the bf16 rounding residual of
+    // its dS.
+    auto tile = [&](unsigned lds_off) {
       const unsigned char* slot = ring + lds_off;
       const unsigned slot_lds = ring_lds + lds_off;
       f32x16 s[MB], dp[MB];
@@ -578,9 +579,10 @@ __global__ __launch_bounds__(256, 2) void attn_sink_bwd_dq_kernel(BwdArgs a) {
           tr[4 * (db * MB + mb) + 3] = ds_read_tr16_b64_asm<PO + 4096 * mb + 2048>(slot_lds + toff[db % 2][1]);
         });
       });
-      float pmax = 0.0f, part = 0.0f;
+      float part = 0.0f;
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
+        float pmax = 0.0f;
         if (need_mask) {  // uniform: only diagonal, window-edge and ragged tiles
           const KeyBounds kb = key_bounds(qi, len, a.causal, a.window);
           const unsigned cnt = (unsigned)max(kb.hi - kb.lo, 0);  // visible keys kb.lo + 1 .. kb.hi
@@ -598,11 +600,7 @@ __global__ __launch_bounds__(256, 2) void attn_sink_bwd_dq_kernel(BwdArgs a) {
           part += pdp;
           dp[mb][i] = __builtin_fmaf(p, nd, pdp);
         }
-        bf16x8 d0 = pack8(dp[mb], 0), d1 = pack8(dp[mb], 1);
-        if (residual) {
-          d0 = residual8(dp[mb], 0, d0);
-          d1 = residual8(dp[mb], 1, d1);
-        }
+        const bf16x8 d0 = pack8(dp[mb], 0), d1 = pack8(dp[mb], 1);
         if (mb == 0) wait_lds_into(tr);
 #pragma unroll
         for (int db = 0; db < G_::kDBlocks; ++db) {
@@ -610,20 +608,24 @@ __global__ __launch_bounds__(256, 2) void attn_sink_bwd_dq_kernel(BwdArgs a) {
           acc[db] = mfma_32x32x16(join_tr(t[0], t[1]), d0, acc[db]);
           acc[db] = mfma_32x32x16(join_tr(t[2], t[3]), d1, acc[db]);
         }
+        if (wave_any(pmax > kSplitThreshold)) {
+          const bf16x8 d0l = residual8(dp[mb], 0, d0), d1l = residual8(dp[mb], 1, d1);
+#pragma unroll
+          for (int db = 0; db < G_::kDBlocks; ++db) {
+            const u32x2* t = tr + 4 * (db * MB + mb);
+            acc[db] = mfma_32x32x16(join_tr(t[0], t[1]), d0l, acc[db]);
+            acc[db] = mfma_32x32x16(join_tr(t[2], t[3]), d1l, acc[db]);
+          }
+        }
       }
-      if (!residual) dsum += part;
-      return pmax;
+      dsum += part;
     };
-    const unsigned off = (j % kDqRing) * kDqSlotBytes;
-    if (wave_any(tile(false, off) > kSplitThreshold)) {
-      unsigned off2 = off;
-      asm volatile("" : "+v"(off2));
-      tile(true, off2);
-    }
+    tile((j % kDqRing) * kDqSlotBytes);
   }
 
-  // dQ row, and this wave's share of sum_i P_{i,h} D~_i.
+  // dQ row, -D~_i for the dK/dV pass, and this wave's share of sum_i P_{i,h} D~_i.
   const float dtot = sum_xor32(dsum);
+  if (qok && grp == 0) a.negd[(size_t)h * a.T + cs + qi] = -dtot;
   float wsum = 0.0f;
   if (qok) {
     float* qrow = a.dq + ((size_t)(cs + qi) * a.Hq + h) * D;

@@ -64,8 +64,11 @@ __device__ __forceinline__ bf16x8 residual8(const f32x16& c, int chunk, const bf
 }
 
 // Probabilities above this value make the bf16 rounding of P and dS visible in the sums over
-// query rows and heads (dK, dV) and over keys (dQ); tiles that hold one get the residual product.
+// query rows and heads (dV) and over keys (dQ); blocks that hold one get the residual product.
 constexpr float kSplitThreshold = 0.0625f;
+// dK sums dS Q over rows and heads, and on sharp rows (large |Q|) the rounding of dS shows from
+// smaller probabilities on: its residual product starts at this one.
+constexpr float kSplitThresholdDk = 0.03125f;
 
 // Wave index within the workgroup, as a value the compiler knows to be wave-uniform (SGPR), so
 // that branches and addresses derived from it stay scalar.

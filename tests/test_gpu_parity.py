@@ -190,7 +190,8 @@ def _oracle_row_block(inp):
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("name", ["causal4k", "window4k", "band4k", "varlen_window", "causal4k_d128"])
+@pytest.mark.parametrize("name", ["causal4k", "window4k", "band4k", "varlen_window", "causal4k_d128",
+                                  "causal4k_sharp"])
 def test_full_size_every_element(name):
     inp = make_workload_inputs(name)
     say(f"[gpu] full-size workload {name}, every element: T={inp.total_tokens} B={len(inp.lengths)} "

@@ -9,7 +9,8 @@ Recipe (every config, one seed per run):
   * then a ``torch.Generator().manual_seed(seed)`` draws float32 N(0, 1) in the order
     q [T, Hq, d], k [T, Hkv, d], v [T, Hkv, d], dout [T, Hq, d], sinks [Hq];
   * q, k, v, dout are rounded to bfloat16 (round-to-nearest-even); sinks stay float32 and are
-    multiplied by ``sink_scale`` (3 for the 32k long-context workload).
+    multiplied by ``sink_scale`` (3 for the 32k long-context workload); ``q_scale`` (4 for the
+    sharp-attention variant of the 4k workload) multiplies q before its rounding.
 
 The pages' own workloads are GPT-OSS-20B RL runs (GSM8K, ReTool, VerifyIf) on packed
 rollouts; no dataset or weight is used here. These GPT-OSS-shaped N(0, 1) tensors stand in
@@ -35,6 +36,7 @@ class Workload:
     causal: bool = True
     window: int = 0
     sink_scale: float = 1.0
+    q_scale: float = 1.0
     description: str = ""
 
     @property
@@ -71,6 +73,9 @@ def workload(name: str, seed: int = 0) -> Workload:
     if name == "long32k":
         return Workload(name, (32768,), 64, 8, sink_scale=3.0,
                         description="32768 tokens, GQA 64/8, causal, sinks x3")
+    if name == "causal4k_sharp":
+        return Workload(name, (4096,), 64, 8, q_scale=4.0,
+                        description="causal4k with q x4 (score std 4: peaked rows, like a trained layer's)")
     if name == "causal4k_d128":
         return Workload(name, (4096,), 64, 8, d=128,
                         description="4096 tokens, GQA 64/8, head_dim 128, causal (beyond the pages' d = 64)")
@@ -78,7 +83,7 @@ def workload(name: str, seed: int = 0) -> Workload:
 
 
 WORKLOAD_NAMES = ("tiny", "causal4k", "window4k", "varlen_causal", "varlen_window", "long32k", "band4k",
-                  "causal4k_d128")
+                  "causal4k_d128", "causal4k_sharp")
 
 
 @dataclass
@@ -108,9 +113,10 @@ def cu_from_lengths(lengths) -> torch.Tensor:
 
 def make_inputs(lengths, hq: int, hkv: int, d: int = 64, *, causal: bool = True, window: int = 0,
                 seed: int = 0, sink_scale: float = 1.0, sinks_override: Optional[List[float]] = None,
-                zero_q: bool = False) -> Inputs:
+                zero_q: bool = False, q_scale: float = 1.0) -> Inputs:
     """Draw one batch following the recipe above. ``zero_q`` / ``sinks_override`` build the
-    special inputs some pins need (uniform scores, S_h = -inf); they only replace drawn values."""
+    special inputs some pins need (uniform scores, S_h = -inf); they only replace drawn values.
+    ``q_scale`` multiplies q before its bf16 rounding (sharper softmax rows)."""
     lengths = tuple(int(x) for x in lengths)
     T = int(sum(lengths))
     g = torch.Generator().manual_seed(seed)
@@ -119,6 +125,8 @@ def make_inputs(lengths, hq: int, hkv: int, d: int = 64, *, causal: bool = True,
     v = torch.randn((T, hkv, d), generator=g, dtype=torch.float32)
     dout = torch.randn((T, hq, d), generator=g, dtype=torch.float32)
     sinks = torch.randn((hq,), generator=g, dtype=torch.float32) * float(sink_scale)
+    if q_scale != 1.0:
+        q = q * float(q_scale)
     if sinks_override is not None:
         sinks = torch.tensor(list(sinks_override), dtype=torch.float32)
         assert sinks.shape == (hq,)
@@ -128,13 +136,13 @@ def make_inputs(lengths, hq: int, hkv: int, d: int = 64, *, causal: bool = True,
                   dout=dout.to(torch.bfloat16), sinks=sinks.contiguous(), cu_seqlens=cu_from_lengths(lengths),
                   lengths=lengths, causal=bool(causal), window=int(window),
                   max_seqlen=max(lengths) if lengths else 0,
-                  meta=dict(hq=hq, hkv=hkv, d=d, seed=seed, sink_scale=sink_scale))
+                  meta=dict(hq=hq, hkv=hkv, d=d, seed=seed, sink_scale=sink_scale, q_scale=q_scale))
 
 
 def make_workload_inputs(name: str, seed: int = 0) -> Inputs:
     w = workload(name, seed)
     inp = make_inputs(w.lengths, w.hq, w.hkv, w.d, causal=w.causal, window=w.window, seed=seed,
-                      sink_scale=w.sink_scale)
+                      sink_scale=w.sink_scale, q_scale=w.q_scale)
     inp.meta["workload"] = name
     return inp
 
