@@ -109,7 +109,7 @@ int bwd_impl(const void* q, const void* k, const void* v, const float* sinks, co
   if (workspace == nullptr || ws_bytes < need || !aligned16(workspace)) return ATTN_SINK_ERR_WORKSPACE;
   if (events != nullptr && num_events != kBwdNumKernels + 1) return ATTN_SINK_ERR_BAD_SHAPE;
 
-  BwdArgs a;
+  BwdArgs a = {};
   a.q = static_cast<const __bf16*>(q);
   a.k = static_cast<const __bf16*>(k);
   a.v = static_cast<const __bf16*>(v);
@@ -141,6 +141,14 @@ int bwd_impl(const void* q, const void* k, const void* v, const float* sinks, co
   a.G = a.Hq / a.Hkv;
   a.hpw = heads_per_group_split(a.G);
   a.kv_streams = (a.G / a.n_halves) % 2 == 0 ? 2 : 1;  // two key halves x (two head streams if possible)
+  if (shape->head_dim == 64 && a.G % 4 == 0 && window > 0) {
+    // With a window a key block's rows are few (the window plus 64): all of a group's heads in one
+    // 8-wave workgroup (four head streams, one workgroup per CU) pay the per-block set-up once and
+    // share each block's rows in L2; measured 10-15% faster than two 4-wave workgroups per CU on
+    // the window-128 workloads, and 3-13% slower without a window.
+    a.n_halves = 1;
+    a.kv_streams = 4;
+  }
   const int dq_rows = kDqRowsPerWave * (4 / a.hpw);  // rows per dQ workgroup
   a.n_qblocks = (shape->max_seqlen + dq_rows - 1) / dq_rows;
   a.n_kblocks = (shape->max_seqlen + kKvKeysPerBlock - 1) / kKvKeysPerBlock;
@@ -295,7 +303,7 @@ int attn_sink_fwd(const void* q, const void* k, const void* v, const float* sink
   if (T > 0 && (!q || !k || !v || !out || !lse)) return ATTN_SINK_ERR_NULL_PTR;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return ATTN_SINK_ERR_ALIGN;
 
-  FwdArgs a;
+  FwdArgs a = {};
   a.q = static_cast<const __bf16*>(q);
   a.k = static_cast<const __bf16*>(k);
   a.v = static_cast<const __bf16*>(v);
@@ -381,7 +389,7 @@ int attn_sink_decode_fwd_timed(const void* q, const void* k, const void* v, cons
     return ATTN_SINK_OK;
   }
 
-  DecodeArgs a;
+  DecodeArgs a = {};
   a.q = static_cast<const __bf16*>(q);
   a.k = static_cast<const __bf16*>(k);
   a.v = static_cast<const __bf16*>(v);

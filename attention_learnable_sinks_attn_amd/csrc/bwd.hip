@@ -22,8 +22,8 @@
 //            does not carry the bf16 rounding of the forward's P.V product, which matters
 //            because the terms of dL/dS_h cancel heavily.
 //  2. dkdv:  column-parallel. A workgroup owns 64 keys of one KV head and all, or one half, of
-//            the group's query heads: two key halves of 32 (one per wave) times one or two "head
-//            streams". Each stream walks its query rows 64 at a time through a 2-slot LDS ring
+//            the group's query heads: two key halves of 32 (one per wave) times one, two or (with
+//            a window, head_dim 64) four "head streams". Each stream walks its query rows 64 at a time through a 2-slot LDS ring
 //            filled by direct global->LDS copies issued one step ahead (the two key halves of a
 //            stream split the copies and share the tiles); one barrier per step. The row tiles
 //            are stored with an XOR swizzle of their 16-byte chunks, which keeps both the
@@ -53,15 +53,15 @@ constexpr int kKvTileBytes = 8192;  // one Q or dO row tile (64 rows at D = 64, 
 // Head dim D = 64 or 128. A step is one 8 KiB row tile: 64 rows (two product blocks) at D = 64,
 // 32 rows at D = 128, whose dK/dV accumulators and K/V operands take twice the registers; that
 // instance runs one wave per SIMD.
-template <int NS, int D>  // head streams per workgroup: 1 or 2 (waves = 2 key halves x NS)
-__global__ __launch_bounds__(128 * NS, D == 64 ? 2 : 1) void attn_sink_bwd_dkdv_kernel(BwdArgs a) {
+template <int NS, int D>  // head streams per workgroup: 1, 2 or 4 (waves = 2 key halves x NS)
+__global__ __launch_bounds__(128 * NS, (D == 64 && NS <= 2) ? 2 : 1) void attn_sink_bwd_dkdv_kernel(BwdArgs a) {
   using G_ = Geo<D>;
   constexpr int kKvRows = G_::kTileRows;                            // query rows per step
   constexpr int kSubs = kKvRows / kKvSub;                           // product blocks per step
   constexpr int kKvSlotBytes = 2 * kKvTileBytes + 2 * kKvRows * 4;  // Q, dO, -LSE/scale, -D
   constexpr int kKvStreamBytes = kKvRing * kKvSlotBytes;
   constexpr int kKvRedStride = D + 4;                               // fp32 row of the final sum
-  constexpr int kRedBytes = NS == 2 ? 2 * 2 * 32 * kKvRedStride * 4 : 0;
+  constexpr int kRedBytes = (NS - 1) * 2 * 2 * 32 * kKvRedStride * 4;  // partials of streams 1 .. NS-1
   constexpr int kNtr = 8 * G_::kDBlocks;                            // transposing reads per block
   __shared__ __attribute__((aligned(1024)))
   unsigned char smem[NS * kKvStreamBytes > kRedBytes ? NS * kKvStreamBytes : kRedBytes];
@@ -343,19 +343,22 @@ __global__ __launch_bounds__(128 * NS, D == 64 ? 2 : 1) void attn_sink_bwd_dkdv_
     if (s + 1 < n_steps) do_step(s + 1, std::integral_constant<int, 1>());
   }
 
-  // Add the second stream's partial sums (LDS, [key][d] fp32 per key half), then store rows.
-  float* red = reinterpret_cast<float*>(smem) + kh * 2 * 32 * kKvRedStride;
-  if (NS == 2) {
+  // Streams 1 .. NS-1 leave their partial sums in LDS ([dk, dv][key][d] fp32 per (stream, key
+  // half)); stream 0 adds them in stream order and stores the rows.
+  float* red = reinterpret_cast<float*>(smem);
+  constexpr int kRedPlane = 2 * 32 * kKvRedStride;
+  if (NS > 1) {
     __syncthreads();  // every wave is done with its ring
-    if (st == 1) {
+    if (st > 0) {
+      float* r = red + ((st - 1) * 2 + kh) * kRedPlane;
 #pragma unroll
       for (int db = 0; db < G_::kDBlocks; ++db) {
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
           const int d = 32 * db + 8 * r4 + 4 * grp;
-          *reinterpret_cast<f32x4*>(&red[l32 * kKvRedStride + d]) =
+          *reinterpret_cast<f32x4*>(&r[l32 * kKvRedStride + d]) =
               (f32x4){dk[db][4 * r4], dk[db][4 * r4 + 1], dk[db][4 * r4 + 2], dk[db][4 * r4 + 3]};
-          *reinterpret_cast<f32x4*>(&red[(32 + l32) * kKvRedStride + d]) =
+          *reinterpret_cast<f32x4*>(&r[(32 + l32) * kKvRedStride + d]) =
               (f32x4){dv[db][4 * r4], dv[db][4 * r4 + 1], dv[db][4 * r4 + 2], dv[db][4 * r4 + 3]};
         }
       }
@@ -380,9 +383,11 @@ __global__ __launch_bounds__(128 * NS, D == 64 ? 2 : 1) void attn_sink_bwd_dkdv_
           const int d = 32 * db + 8 * r4 + 4 * grp;
           f32x4 kv = {dk[db][4 * r4], dk[db][4 * r4 + 1], dk[db][4 * r4 + 2], dk[db][4 * r4 + 3]};
           f32x4 vv = {dv[db][4 * r4], dv[db][4 * r4 + 1], dv[db][4 * r4 + 2], dv[db][4 * r4 + 3]};
-          if (NS == 2) {
-            kv += *reinterpret_cast<const f32x4*>(&red[l32 * kKvRedStride + d]);
-            vv += *reinterpret_cast<const f32x4*>(&red[(32 + l32) * kKvRedStride + d]);
+#pragma unroll
+          for (int o = 0; o < NS - 1; ++o) {
+            const float* r = red + (o * 2 + kh) * kRedPlane;
+            kv += *reinterpret_cast<const f32x4*>(&r[l32 * kKvRedStride + d]);
+            vv += *reinterpret_cast<const f32x4*>(&r[(32 + l32) * kKvRedStride + d]);
           }
           *reinterpret_cast<f32x4*>(dkrow + d) = kv * kscale;
           *reinterpret_cast<f32x4*>(dvrow + d) = vv;
@@ -702,7 +707,9 @@ __global__ __launch_bounds__(256) void attn_sink_bwd_finish_kernel(BwdArgs a, in
 
 template <int D>
 void launch_dkdv_d(const BwdArgs& a, dim3 grid, hipStream_t stream) {
-  if (a.kv_streams == 2) {
+  if (D == 64 && a.kv_streams == 4) {
+    hipLaunchKernelGGL((attn_sink_bwd_dkdv_kernel<4, 64>), grid, dim3(512), 0, stream, a);
+  } else if (a.kv_streams == 2) {
     hipLaunchKernelGGL((attn_sink_bwd_dkdv_kernel<2, D>), grid, dim3(256), 0, stream, a);
   } else {
     hipLaunchKernelGGL((attn_sink_bwd_dkdv_kernel<1, D>), grid, dim3(128), 0, stream, a);
