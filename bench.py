@@ -75,14 +75,16 @@ KERNEL_FLOPS_PER_PAIR_D = {
 # (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch) scaled by what the same counters read for the
 # copy probe; valid only for kernel sources with the recorded digest.
 TRAFFIC = {
-    ("causal4k", "attn_sink_bwd_dkdv_kernel"): {"bytes": 146899847, "digest": "beedb3e3d3ae39ef"},
-    ("window4k", "attn_sink_bwd_dkdv_kernel"): {"bytes": 106394479, "digest": "beedb3e3d3ae39ef"},
-    ("window4k", "attn_sink_bwd_dq_kernel"): {"bytes": 213271453, "digest": "beedb3e3d3ae39ef"},
-    ("varlen_window", "attn_sink_bwd_dkdv_kernel"): {"bytes": 1718894312, "digest": "beedb3e3d3ae39ef"},
-    ("varlen_window", "attn_sink_bwd_dq_kernel"): {"bytes": 3792490999, "digest": "beedb3e3d3ae39ef"},
-    ("band4k", "attn_sink_bwd_dkdv_kernel"): {"bytes": 126190898, "digest": "beedb3e3d3ae39ef"},
-    ("band4k", "attn_sink_bwd_dq_kernel"): {"bytes": 213320343, "digest": "beedb3e3d3ae39ef"},
-    ("decode32k", "attn_sink_decode_partial_kernel"): {"bytes": 368464234, "digest": "beedb3e3d3ae39ef"},
+    ("causal4k", "attn_sink_bwd_dkdv_kernel"): {"bytes": 146757055, "digest": "640069b1385d2501"},
+    ("causal4k", "attn_sink_fwd_kernel"): {"bytes": 114531482, "digest": "640069b1385d2501"},
+    ("causal4k", "attn_sink_bwd_dq_kernel"): {"bytes": 221250988, "digest": "640069b1385d2501"},
+    ("window4k", "attn_sink_bwd_dkdv_kernel"): {"bytes": 96773515, "digest": "640069b1385d2501"},
+    ("window4k", "attn_sink_bwd_dq_kernel"): {"bytes": 213303233, "digest": "640069b1385d2501"},
+    ("varlen_window", "attn_sink_bwd_dkdv_kernel"): {"bytes": 1667213280, "digest": "640069b1385d2501"},
+    ("varlen_window", "attn_sink_bwd_dq_kernel"): {"bytes": 3792827391, "digest": "640069b1385d2501"},
+    ("band4k", "attn_sink_bwd_dkdv_kernel"): {"bytes": 99699534, "digest": "640069b1385d2501"},
+    ("band4k", "attn_sink_bwd_dq_kernel"): {"bytes": 213352550, "digest": "640069b1385d2501"},
+    ("decode32k", "attn_sink_decode_partial_kernel"): {"bytes": 368461185, "digest": "640069b1385d2501"},
 }
 
 
