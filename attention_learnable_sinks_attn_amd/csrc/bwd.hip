@@ -68,18 +68,20 @@ __global__ __launch_bounds__(128 * NS, (D == 64 && NS <= 2) ? 2 : 1) void attn_s
   static_assert(kKvRing == 2, "the waits below assume one step in flight");
 
   // Block order: KV group fastest (consecutive ids go to different XCDs, so each XCD works on
-  // few groups and their query rows stay in its L2), then head half. Then, with a window, the key
-  // blocks of one sequence back to back: neighbouring blocks share most of their query rows,
-  // which stay in L2 between them. Otherwise sequences, then key blocks ascending: under a
-  // causal mask the first key blocks see the most query rows, so the longest workgroups start
-  // first and the short ones fill in.
+  // few groups and their query rows stay in its L2), then head half, then the key blocks of one
+  // sequence back to back, sequence after sequence. The workgroups in flight then stream the rows
+  // of one or two sequences, which stay in L2 and the last-level cache between them; interleaving
+  // the sequences (key block 0 of every sequence, then key block 1, ...) made the pass fetch
+  // about 31 times its algorithmic bytes on 16 packed sequences of up to 8k tokens, against 5
+  // times in this order, and took 40% longer. Under a causal mask the first key blocks of a
+  // sequence see the most query rows, so each sequence's longest workgroups start first.
   const int bid = blockIdx.x;
   const int g = bid % a.Hkv;
   int rest = bid / a.Hkv;
   const int hh = rest % a.n_halves;
   rest /= a.n_halves;
-  const int b = a.window > 0 ? rest / a.n_kblocks : rest % a.B;
-  const int kblk = (a.window > 0 ? rest % a.n_kblocks : rest / a.B) * kKvKeysPerBlock;
+  const int b = rest / a.n_kblocks;
+  const int kblk = (rest % a.n_kblocks) * kKvKeysPerBlock;
   const int cs = a.cu[b];
   const int len = a.cu[b + 1] - cs;
   if (kblk >= len) return;  // uniform over the workgroup
@@ -422,10 +424,12 @@ __global__ __launch_bounds__(256, 2) void attn_sink_bwd_dq_kernel(BwdArgs a) {
   const int rest = bid / n_hs;
   const int spg = a.G / HPW;
   const int hs = (inner % a.Hkv) * spg + inner / a.Hkv;
-  const int b = rest % a.B;
+  // Row blocks of one sequence back to back (its K/V tiles stay in L2), the last (longest under
+  // a causal mask) first; sequence after sequence.
+  const int b = rest / a.n_qblocks;
   const int cs = a.cu[b];
   const int len = a.cu[b + 1] - cs;
-  const int qw0 = (a.n_qblocks - 1 - rest / a.B) * kRows * RPW;  // longest causal rows first
+  const int qw0 = (a.n_qblocks - 1 - rest % a.n_qblocks) * kRows * RPW;  // longest causal rows first
   if (qw0 >= len) return;
 
   const int wave = wave_id();

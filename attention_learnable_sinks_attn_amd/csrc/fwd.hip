@@ -268,8 +268,10 @@ __global__ __launch_bounds__(256, 2) void attn_sink_fwd_kernel(FwdArgs a) {
   // workgroups on the 8 XCDs keeps each group's K/V in few L2s.
   const int spg = a.G / HPW;
   const int hs = (inner % a.Hkv) * spg + inner / a.Hkv;
-  const int b = rest % a.B;
-  const int qb = a.n_qblocks - 1 - rest / a.B;  // longest causal rows first
+  // Row blocks of one sequence back to back (its K/V tiles stay in L2 and the last-level cache),
+  // the last (longest under a causal mask) first; sequence after sequence.
+  const int b = rest / a.n_qblocks;
+  const int qb = a.n_qblocks - 1 - rest % a.n_qblocks;  // longest causal rows first
 
   const int cs = a.cu[b];
   const int len = a.cu[b + 1] - cs;
