@@ -140,15 +140,13 @@ int bwd_impl(const void* q, const void* k, const void* v, const float* sinks, co
   a.Hkv = shape->num_heads_kv;
   a.G = a.Hq / a.Hkv;
   a.hpw = heads_per_group_split(a.G);
-  a.kv_streams = (a.G / a.n_halves) % 2 == 0 ? 2 : 1;  // two key halves x (two head streams if possible)
-  if (shape->head_dim == 64 && a.G % 4 == 0 && window > 0) {
-    // With a window a key block's rows are few (the window plus 64): all of a group's heads in one
-    // 8-wave workgroup (four head streams, one workgroup per CU) pay the per-block set-up once and
-    // share each block's rows in L2; measured 10-15% faster than two 4-wave workgroups per CU on
-    // the window-128 workloads, and 3-13% slower without a window.
-    a.n_halves = 1;
-    a.kv_streams = 4;
-  }
+  // Two key halves x two head streams per workgroup where the heads split evenly, two workgroups
+  // per CU. (With a window, an 8-wave workgroup holding all of a group's heads as four streams, one
+  // per CU, lost 37% of its step loop at the per-step barrier: at the window's edges the two key
+  // halves of a stream have different numbers of live row blocks in a step, and with one
+  // workgroup per CU nothing fills the wait. Two 4-wave workgroups per CU hide it: the pass took
+  // 9-23% less time on the window-128 workloads.)
+  a.kv_streams = (a.G / a.n_halves) % 2 == 0 ? 2 : 1;
   const int dq_rows = kDqRowsPerWave * (4 / a.hpw);  // rows per dQ workgroup
   a.n_qblocks = (shape->max_seqlen + dq_rows - 1) / dq_rows;
   a.n_kblocks = (shape->max_seqlen + kKvKeysPerBlock - 1) / kKvKeysPerBlock;
