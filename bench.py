@@ -75,20 +75,19 @@ KERNEL_FLOPS_PER_PAIR_D = {
 # (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch) scaled by what the same counters read for the
 # copy probe; valid only for kernel sources with the recorded digest.
 TRAFFIC = {
-    ("causal4k", "attn_sink_bwd_dkdv_kernel"): {"bytes": 146655957, "digest": "20f1104edb695b09"},
-    ("window4k", "attn_sink_bwd_dkdv_kernel"): {"bytes": 96766897, "digest": "20f1104edb695b09"},
-    ("window4k", "attn_sink_bwd_dq_kernel"): {"bytes": 213374385, "digest": "20f1104edb695b09"},
-    ("varlen_window", "attn_sink_bwd_dkdv_kernel"): {"bytes": 1671564751, "digest": "20f1104edb695b09"},
-    ("varlen_window", "attn_sink_bwd_dq_kernel"): {"bytes": 3648269712, "digest": "20f1104edb695b09"},
-    ("band4k", "attn_sink_bwd_dkdv_kernel"): {"bytes": 99638874, "digest": "20f1104edb695b09"},
-    ("band4k", "attn_sink_bwd_dq_kernel"): {"bytes": 213371277, "digest": "20f1104edb695b09"},
-    ("decode32k", "attn_sink_decode_partial_kernel"): {"bytes": 368472194, "digest": "20f1104edb695b09"},
-    ("causal4k", "attn_sink_fwd_kernel"): {"bytes": 114513881, "digest": "20f1104edb695b09"},
-    ("causal4k", "attn_sink_bwd_dq_kernel"): {"bytes": 221260094, "digest": "20f1104edb695b09"},
-    ("varlen_causal", "attn_sink_bwd_dkdv_kernel"): {"bytes": 8723074081, "digest": "20f1104edb695b09"},
-    ("long32k", "attn_sink_bwd_dkdv_kernel"): {"bytes": 35508242603, "digest": "20f1104edb695b09"},
+    ("causal4k", "attn_sink_bwd_dkdv_kernel"): {"bytes": 146638394, "digest": "c3738a9bd6683083"},
+    ("window4k", "attn_sink_bwd_dkdv_kernel"): {"bytes": 107057304, "digest": "c3738a9bd6683083"},
+    ("window4k", "attn_sink_bwd_dq_kernel"): {"bytes": 213318171, "digest": "c3738a9bd6683083"},
+    ("varlen_window", "attn_sink_bwd_dkdv_kernel"): {"bytes": 1708413064, "digest": "c3738a9bd6683083"},
+    ("varlen_window", "attn_sink_bwd_dq_kernel"): {"bytes": 3648282113, "digest": "c3738a9bd6683083"},
+    ("band4k", "attn_sink_bwd_dkdv_kernel"): {"bytes": 120642347, "digest": "c3738a9bd6683083"},
+    ("band4k", "attn_sink_bwd_dq_kernel"): {"bytes": 213365493, "digest": "c3738a9bd6683083"},
+    ("decode32k", "attn_sink_decode_partial_kernel"): {"bytes": 368460878, "digest": "c3738a9bd6683083"},
+    ("causal4k", "attn_sink_fwd_kernel"): {"bytes": 114516139, "digest": "c3738a9bd6683083"},
+    ("causal4k", "attn_sink_bwd_dq_kernel"): {"bytes": 221266072, "digest": "c3738a9bd6683083"},
+    ("varlen_causal", "attn_sink_bwd_dkdv_kernel"): {"bytes": 8735592386, "digest": "c3738a9bd6683083"},
+    ("long32k", "attn_sink_bwd_dkdv_kernel"): {"bytes": 35426477783, "digest": "c3738a9bd6683083"},
 }
-
 def kernel_source_digest() -> str:
     """sha256 over the HIP sources and headers the library is built from."""
     h = hashlib.sha256()
