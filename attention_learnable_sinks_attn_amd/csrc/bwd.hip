@@ -52,7 +52,7 @@ constexpr int kKvTileBytes = 8192;  // one Q or dO row tile (64 rows at D = 64, 
 
 // Head dim D = 64 or 128. A step is one 8 KiB row tile: 64 rows (two product blocks) at D = 64,
 // 32 rows at D = 128, whose dK/dV accumulators and K/V operands take twice the registers; that
-// instance runs one wave per SIMD.
+// instance runs one wave per SIMD and one head stream per workgroup (two workgroups per CU).
 template <int NS, int D>  // head streams per workgroup: 1 or 2 (waves = 2 key halves x NS)
 __global__ __launch_bounds__(128 * NS, D == 64 ? 2 : 1) void attn_sink_bwd_dkdv_kernel(BwdArgs a) {
   using G_ = Geo<D>;
@@ -711,8 +711,8 @@ __global__ __launch_bounds__(256) void attn_sink_bwd_finish_kernel(BwdArgs a, in
 
 template <int D>
 void launch_dkdv_d(const BwdArgs& a, dim3 grid, hipStream_t stream) {
-  if (a.kv_streams == 2) {
-    hipLaunchKernelGGL((attn_sink_bwd_dkdv_kernel<2, D>), grid, dim3(256), 0, stream, a);
+  if (D == 64 && a.kv_streams == 2) {  // head_dim 128 always runs one stream per workgroup
+    hipLaunchKernelGGL((attn_sink_bwd_dkdv_kernel<2, 64>), grid, dim3(256), 0, stream, a);
   } else {
     hipLaunchKernelGGL((attn_sink_bwd_dkdv_kernel<1, D>), grid, dim3(128), 0, stream, a);
   }
