@@ -75,18 +75,18 @@ KERNEL_FLOPS_PER_PAIR_D = {
 # (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch) scaled by what the same counters read for the
 # copy probe; valid only for kernel sources with the recorded digest.
 TRAFFIC = {
-    ("causal4k", "attn_sink_bwd_dkdv_kernel"): {"bytes": 146638394, "digest": "c3738a9bd6683083"},
-    ("window4k", "attn_sink_bwd_dkdv_kernel"): {"bytes": 107057304, "digest": "c3738a9bd6683083"},
-    ("window4k", "attn_sink_bwd_dq_kernel"): {"bytes": 213318171, "digest": "c3738a9bd6683083"},
-    ("varlen_window", "attn_sink_bwd_dkdv_kernel"): {"bytes": 1708413064, "digest": "c3738a9bd6683083"},
-    ("varlen_window", "attn_sink_bwd_dq_kernel"): {"bytes": 3648282113, "digest": "c3738a9bd6683083"},
-    ("band4k", "attn_sink_bwd_dkdv_kernel"): {"bytes": 120642347, "digest": "c3738a9bd6683083"},
-    ("band4k", "attn_sink_bwd_dq_kernel"): {"bytes": 213365493, "digest": "c3738a9bd6683083"},
-    ("decode32k", "attn_sink_decode_partial_kernel"): {"bytes": 368460878, "digest": "c3738a9bd6683083"},
-    ("causal4k", "attn_sink_fwd_kernel"): {"bytes": 114516139, "digest": "c3738a9bd6683083"},
-    ("causal4k", "attn_sink_bwd_dq_kernel"): {"bytes": 221266072, "digest": "c3738a9bd6683083"},
-    ("varlen_causal", "attn_sink_bwd_dkdv_kernel"): {"bytes": 8735592386, "digest": "c3738a9bd6683083"},
-    ("long32k", "attn_sink_bwd_dkdv_kernel"): {"bytes": 35426477783, "digest": "c3738a9bd6683083"},
+    ("causal4k", "attn_sink_bwd_dkdv_kernel"): {"bytes": 146635407, "digest": "b89f69c0a57cce8d"},
+    ("window4k", "attn_sink_bwd_dkdv_kernel"): {"bytes": 105775258, "digest": "b89f69c0a57cce8d"},
+    ("window4k", "attn_sink_bwd_dq_kernel"): {"bytes": 213342372, "digest": "b89f69c0a57cce8d"},
+    ("varlen_window", "attn_sink_bwd_dkdv_kernel"): {"bytes": 1707937222, "digest": "b89f69c0a57cce8d"},
+    ("varlen_window", "attn_sink_bwd_dq_kernel"): {"bytes": 3648356079, "digest": "b89f69c0a57cce8d"},
+    ("band4k", "attn_sink_bwd_dkdv_kernel"): {"bytes": 119695941, "digest": "b89f69c0a57cce8d"},
+    ("band4k", "attn_sink_bwd_dq_kernel"): {"bytes": 213405152, "digest": "b89f69c0a57cce8d"},
+    ("decode32k", "attn_sink_decode_partial_kernel"): {"bytes": 368461589, "digest": "b89f69c0a57cce8d"},
+    ("causal4k", "attn_sink_fwd_kernel"): {"bytes": 114511996, "digest": "b89f69c0a57cce8d"},
+    ("causal4k", "attn_sink_bwd_dq_kernel"): {"bytes": 221271538, "digest": "b89f69c0a57cce8d"},
+    ("varlen_causal", "attn_sink_bwd_dkdv_kernel"): {"bytes": 8715513372, "digest": "b89f69c0a57cce8d"},
+    ("long32k", "attn_sink_bwd_dkdv_kernel"): {"bytes": 35534154722, "digest": "b89f69c0a57cce8d"},
 }
 def kernel_source_digest() -> str:
     """sha256 over the HIP sources and headers the library is built from."""
