@@ -6,8 +6,10 @@ head_dim 64, causal, bf16 inputs (the headline configuration).
 
     python bench.py [--gpus 1] [--steps 50] [--warmup 50] [--workload causal4k] [--no-cpu-baseline]
 
-The default 50 warm-up steps let the GPU's clocks settle: from idle, the first 20-40 steps of the
-4k workload run up to 8% slower than the rest.
+From idle, the first 20-40 steps of the 4k workload run up to 8% slower than the rest while the
+GPU's clocks settle. So before the ``--warmup`` steps the script runs untimed steps for
+``--settle-ms`` of wall time (300 by default; reported as ``settle`` in the output line); the timed
+region is still exactly ``--steps`` steps.
 
 ``--workload decode32k`` (or decode32k_nq4, decode32k_window) times the inference-shaped decode
 forward instead: a few new tokens per sequence against 16k-32k-token KV caches, reported as
@@ -16,9 +18,10 @@ algorithmic HBM GB/s (q, every cached K/V row a new token sees, out and LSE, eac
 Prints one JSON line. ``value`` is algorithmic TFLOP/s over the timed steps: 4*d FLOPs per visible
 (query, key, head) in the forward (QK^T and PV) plus 10*d in the backward (S, dP, dV, dK, dQ);
 recomputation and masked tile work are not counted. ``roofline`` describes the kernel with the
-largest share of the step time (in the per-kernel breakdown ``kernel_ms``, taken in a pass between
-the warm-up and the timed steps, each of its steps with events around one kernel only), timed with
-HIP events recorded around it, on the stream the kernels run on, in every timed step: against the
+largest share of the step time (picked in a short pass between the warm-up and the timed steps,
+each of its steps with events around one kernel only), timed with HIP events recorded around it,
+on the stream the kernels run on, in every timed step; the per-kernel breakdown ``kernel_ms`` comes
+from a pass of the same kind after the timed steps. The roofline is taken against the
 bf16 MFMA peak for the causal workloads, and against HBM bandwidth (algorithmic bytes: each tensor
 the kernel needs read or written once at its ABI dtype) for the banded window ones.
 ``measured_peaks`` gives a bf16 GEMM's and a device copy's rates on the same GPU, measured after the
@@ -200,6 +203,20 @@ def breakdown_source(n_kernels: int) -> str:
             f"around kernel j % {n_kernels} only")
 
 
+def settle(step, settle_ms: float) -> int:
+    """Untimed steps for `settle_ms` of wall time (the host waits for the GPU every 8 steps, so it
+    does not queue far ahead of it); returns how many ran."""
+    n = 0
+    t_end = time.perf_counter() + settle_ms / 1000.0
+    while time.perf_counter() < t_end:
+        step(None)
+        n += 1
+        if n % 8 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    return n
+
+
 def run_timed(step, names, hip, warmup: int, steps: int):
     """`warmup` untimed steps; a short pass that picks the dominant kernel; exactly `steps` timed
     steps; then the breakdown pass.
@@ -335,6 +352,7 @@ def bench_decode(args):
         asa.decode_fwd(q, k, v, sinks, cu_q, cu_k, d.max_q, d.max_k, window=window, out_dtype=torch.bfloat16,
                        out=out, lse=lse, workspace=ws, events=evs)
 
+    n_settle = settle(step, args.settle_ms)
     ms_step, wall, per_kernel, dom, dom_ms = run_timed(step, names, hip, args.warmup, args.steps)
     kb = decode_bytes(d, hq, hkv, 2)
     total = sum(kb.values())
@@ -349,7 +367,8 @@ def bench_decode(args):
         roofline["traffic_unit"] = "bytes per launch (HBM fetch + write)"
     res = {
         "metric": "sink-attention decode forward HBM GB/s (GQA 64/8, d=64, bf16 KV cache)", "value": round(gbs, 1),
-        "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "settle": {"ms": args.settle_ms, "steps": n_settle}, "ms_per_step": round(ms_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": args.workload, "seqs": B, "new_tokens": int(Tq), "cached_tokens": int(k.shape[0]),
                    "heads_q": hq, "heads_kv": hkv, "head_dim": 64, "window": window, "out_dtype": "bf16",
@@ -378,6 +397,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--settle-ms", type=float, default=300.0,
+                    help="untimed steps for this much wall time before the warm-up steps (clocks settle)")
     ap.add_argument("--workload", default="causal4k", choices=list(WORKLOAD_NAMES) + list(DECODE_WORKLOADS))
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -437,6 +458,7 @@ def main():
         asa.bwd(q, k, v, sinks, out, lse, dout, cu, inp.max_seqlen, inp.causal, inp.window, dq=dq, dk=dk, dv=dv,
                 dsinks=dsinks, workspace=ws, events=bwd_ev)
 
+    n_settle = settle(step, args.settle_ms)
     ms_step, wall, per_kernel, dom, dom_ms = run_timed(step, names, hip, args.warmup, args.steps)
 
     pairs = visible_pairs(inp.lengths, inp.causal, inp.window) * Hq
@@ -462,7 +484,8 @@ def main():
     metric = METRIC if w.name == "causal4k" else f"sink-attention fwd+bwd bf16 TFLOP/s ({w.name}: {w.description})"
     res = {
         "metric": metric, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+        "warmup": args.warmup, "settle": {"ms": args.settle_ms, "steps": n_settle}, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": w.name, "tokens": int(T), "seqs": len(inp.lengths), "heads_q": int(Hq),
                    "heads_kv": int(Hkv), "head_dim": int(d), "causal": inp.causal, "window": inp.window,
@@ -554,6 +577,7 @@ def bench_table(args):
             asa.bwd(q, k, v, sinks, out, lse, dout, cu, inp.max_seqlen, inp.causal, inp.window, dq=dq, dk=dk, dv=dv,
                     dsinks=ds, workspace=ws)
 
+        settle(lambda _evs: (f(), b()), args.settle_ms)
         for _ in range(args.warmup):
             f()
             b()
