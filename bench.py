@@ -78,18 +78,18 @@ KERNEL_FLOPS_PER_PAIR_D = {
 # (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch) scaled by what the same counters read for the
 # copy probe; valid only for kernel sources with the recorded digest.
 TRAFFIC = {
-    ("causal4k", "attn_sink_bwd_dkdv_kernel"): {"bytes": 146635407, "digest": "b89f69c0a57cce8d"},
-    ("window4k", "attn_sink_bwd_dkdv_kernel"): {"bytes": 105775258, "digest": "b89f69c0a57cce8d"},
-    ("window4k", "attn_sink_bwd_dq_kernel"): {"bytes": 213342372, "digest": "b89f69c0a57cce8d"},
-    ("varlen_window", "attn_sink_bwd_dkdv_kernel"): {"bytes": 1707937222, "digest": "b89f69c0a57cce8d"},
-    ("varlen_window", "attn_sink_bwd_dq_kernel"): {"bytes": 3648356079, "digest": "b89f69c0a57cce8d"},
-    ("band4k", "attn_sink_bwd_dkdv_kernel"): {"bytes": 119695941, "digest": "b89f69c0a57cce8d"},
-    ("band4k", "attn_sink_bwd_dq_kernel"): {"bytes": 213405152, "digest": "b89f69c0a57cce8d"},
-    ("decode32k", "attn_sink_decode_partial_kernel"): {"bytes": 368461589, "digest": "b89f69c0a57cce8d"},
-    ("causal4k", "attn_sink_fwd_kernel"): {"bytes": 114511996, "digest": "b89f69c0a57cce8d"},
-    ("causal4k", "attn_sink_bwd_dq_kernel"): {"bytes": 221271538, "digest": "b89f69c0a57cce8d"},
-    ("varlen_causal", "attn_sink_bwd_dkdv_kernel"): {"bytes": 8715513372, "digest": "b89f69c0a57cce8d"},
-    ("long32k", "attn_sink_bwd_dkdv_kernel"): {"bytes": 35534154722, "digest": "b89f69c0a57cce8d"},
+    ("causal4k", "attn_sink_bwd_dkdv_kernel"): {"bytes": 146633428, "digest": "b89f69c0a57cce8d"},
+    ("window4k", "attn_sink_bwd_dkdv_kernel"): {"bytes": 105772827, "digest": "b89f69c0a57cce8d"},
+    ("window4k", "attn_sink_bwd_dq_kernel"): {"bytes": 213329835, "digest": "b89f69c0a57cce8d"},
+    ("varlen_window", "attn_sink_bwd_dkdv_kernel"): {"bytes": 1707646133, "digest": "b89f69c0a57cce8d"},
+    ("varlen_window", "attn_sink_bwd_dq_kernel"): {"bytes": 3648384318, "digest": "b89f69c0a57cce8d"},
+    ("band4k", "attn_sink_bwd_dkdv_kernel"): {"bytes": 119648156, "digest": "b89f69c0a57cce8d"},
+    ("band4k", "attn_sink_bwd_dq_kernel"): {"bytes": 213371607, "digest": "b89f69c0a57cce8d"},
+    ("decode32k", "attn_sink_decode_partial_kernel"): {"bytes": 368459570, "digest": "b89f69c0a57cce8d"},
+    ("causal4k", "attn_sink_fwd_kernel"): {"bytes": 114517828, "digest": "b89f69c0a57cce8d"},
+    ("causal4k", "attn_sink_bwd_dq_kernel"): {"bytes": 221265699, "digest": "b89f69c0a57cce8d"},
+    ("varlen_causal", "attn_sink_bwd_dkdv_kernel"): {"bytes": 8702002983, "digest": "b89f69c0a57cce8d"},
+    ("long32k", "attn_sink_bwd_dkdv_kernel"): {"bytes": 35421619970, "digest": "b89f69c0a57cce8d"},
 }
 def kernel_source_digest() -> str:
     """sha256 over the HIP sources and headers the library is built from."""
