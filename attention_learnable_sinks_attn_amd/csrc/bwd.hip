@@ -22,8 +22,8 @@
 //            does not carry the bf16 rounding of the forward's P.V product, which matters
 //            because the terms of dL/dS_h cancel heavily.
 //  2. dkdv:  column-parallel. A workgroup owns 64 keys of one KV head and all, or one half, of
-//            the group's query heads: two key halves of 32 (one per wave) times one, two or (with
-//            a window, head_dim 64) four "head streams". Each stream walks its query rows 64 at a time through a 2-slot LDS ring
+//            the group's query heads: two key halves of 32 (one per wave) times one or two "head
+//            streams". Each stream walks its query rows 64 at a time through a 2-slot LDS ring
 //            filled by direct global->LDS copies issued one step ahead (the two key halves of a
 //            stream split the copies and share the tiles); one barrier per step. The row tiles
 //            are stored with an XOR swizzle of their 16-byte chunks, which keeps both the

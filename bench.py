@@ -47,6 +47,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -78,27 +79,35 @@ KERNEL_FLOPS_PER_PAIR_D = {
 # (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch) scaled by what the same counters read for the
 # copy probe; valid only for kernel sources with the recorded digest.
 TRAFFIC = {
-    ("causal4k", "attn_sink_bwd_dkdv_kernel"): {"bytes": 146633428, "digest": "b89f69c0a57cce8d"},
-    ("window4k", "attn_sink_bwd_dkdv_kernel"): {"bytes": 105772827, "digest": "b89f69c0a57cce8d"},
-    ("window4k", "attn_sink_bwd_dq_kernel"): {"bytes": 213329835, "digest": "b89f69c0a57cce8d"},
-    ("varlen_window", "attn_sink_bwd_dkdv_kernel"): {"bytes": 1707646133, "digest": "b89f69c0a57cce8d"},
-    ("varlen_window", "attn_sink_bwd_dq_kernel"): {"bytes": 3648384318, "digest": "b89f69c0a57cce8d"},
-    ("band4k", "attn_sink_bwd_dkdv_kernel"): {"bytes": 119648156, "digest": "b89f69c0a57cce8d"},
-    ("band4k", "attn_sink_bwd_dq_kernel"): {"bytes": 213371607, "digest": "b89f69c0a57cce8d"},
-    ("decode32k", "attn_sink_decode_partial_kernel"): {"bytes": 368459570, "digest": "b89f69c0a57cce8d"},
-    ("causal4k", "attn_sink_fwd_kernel"): {"bytes": 114517828, "digest": "b89f69c0a57cce8d"},
-    ("causal4k", "attn_sink_bwd_dq_kernel"): {"bytes": 221265699, "digest": "b89f69c0a57cce8d"},
-    ("varlen_causal", "attn_sink_bwd_dkdv_kernel"): {"bytes": 8702002983, "digest": "b89f69c0a57cce8d"},
-    ("long32k", "attn_sink_bwd_dkdv_kernel"): {"bytes": 35421619970, "digest": "b89f69c0a57cce8d"},
+    ("causal4k", "attn_sink_bwd_dkdv_kernel"): {"bytes": 146633428, "digest": "11aa62ecc2a37a29"},
+    ("window4k", "attn_sink_bwd_dkdv_kernel"): {"bytes": 105772827, "digest": "11aa62ecc2a37a29"},
+    ("window4k", "attn_sink_bwd_dq_kernel"): {"bytes": 213329835, "digest": "11aa62ecc2a37a29"},
+    ("varlen_window", "attn_sink_bwd_dkdv_kernel"): {"bytes": 1707646133, "digest": "11aa62ecc2a37a29"},
+    ("varlen_window", "attn_sink_bwd_dq_kernel"): {"bytes": 3648384318, "digest": "11aa62ecc2a37a29"},
+    ("band4k", "attn_sink_bwd_dkdv_kernel"): {"bytes": 119648156, "digest": "11aa62ecc2a37a29"},
+    ("band4k", "attn_sink_bwd_dq_kernel"): {"bytes": 213371607, "digest": "11aa62ecc2a37a29"},
+    ("decode32k", "attn_sink_decode_partial_kernel"): {"bytes": 368459570, "digest": "11aa62ecc2a37a29"},
+    ("causal4k", "attn_sink_fwd_kernel"): {"bytes": 114517828, "digest": "11aa62ecc2a37a29"},
+    ("causal4k", "attn_sink_bwd_dq_kernel"): {"bytes": 221265699, "digest": "11aa62ecc2a37a29"},
+    ("varlen_causal", "attn_sink_bwd_dkdv_kernel"): {"bytes": 8702002983, "digest": "11aa62ecc2a37a29"},
+    ("long32k", "attn_sink_bwd_dkdv_kernel"): {"bytes": 35421619970, "digest": "11aa62ecc2a37a29"},
 }
+def _code_only(text: str) -> str:
+    """C/C++ source without its comments and with whitespace runs collapsed (string literals kept)."""
+    out = re.sub(r'"(?:\\.|[^"\\\n])*"|//[^\n]*|/\*.*?\*/',
+                 lambda m: m.group(0) if m.group(0).startswith('"') else " ", text, flags=re.S)
+    return " ".join(out.split())
+
+
 def kernel_source_digest() -> str:
-    """sha256 over the HIP sources and headers the library is built from."""
+    """sha256 over the code (comments and layout ignored) of the HIP sources and headers the library
+    is built from."""
     h = hashlib.sha256()
     for d in (os.path.join(ROOT, "attention_learnable_sinks_attn_amd", "csrc"), os.path.join(ROOT, "include")):
         for name in sorted(os.listdir(d)):
             if name.endswith((".hip", ".h")):
-                with open(os.path.join(d, name), "rb") as f:
-                    h.update(name.encode() + b"\0" + f.read())
+                with open(os.path.join(d, name), encoding="utf-8") as f:
+                    h.update(name.encode() + b"\0" + _code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 
