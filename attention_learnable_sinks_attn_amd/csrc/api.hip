@@ -210,15 +210,15 @@ void split_keys(long long pairs, long long tiles, long long* per, long long* n) 
   *n = tiles <= 0 ? 1 : (tiles + *per - 1) / *per;
 }
 
-// Chunks for a call with the given window. The workspace is sized for window 0; a window only
-// shortens the span to chunk (the keys from the 64-aligned start of the first visible one), and the
-// chunk count never exceeds the workspace's.
 // Groups of 32 (new token, query head) columns per (sequence, KV head).
 int decode_col_groups(const attn_sink_decode_shape* s) {
   const long long cols = (long long)s->max_q * (s->num_heads_q / s->num_heads_kv);
   return (int)std::max<long long>(1, (cols + 31) / 32);
 }
 
+// Chunks for a call with the given window. The workspace is sized for window 0; a window only
+// shortens the span to chunk (the keys from the 64-aligned start of the first visible one), and the
+// chunk count never exceeds the workspace's.
 void decode_chunks(const attn_sink_decode_shape* s, int window, int* n_chunks, int* chunk_keys) {
   const long long pairs = (long long)s->num_seqs * s->num_heads_kv * decode_col_groups(s);
   long long per, n;
@@ -494,7 +494,9 @@ const char* attn_sink_strerror(int code) {
     case ATTN_SINK_ERR_UNSUPPORTED:
       return "unsupported head_dim or output dtype (head_dim 64 or 128; float32 outputs, bf16 also for forwards)";
     case ATTN_SINK_ERR_BAD_WINDOW: return "negative window";
-    case ATTN_SINK_ERR_WORKSPACE: return "workspace missing or smaller than attn_sink_bwd_workspace_bytes()";
+    case ATTN_SINK_ERR_WORKSPACE:
+      return "workspace missing, not 16-byte aligned, or smaller than attn_sink_bwd_workspace_bytes() "
+             "(attn_sink_decode_workspace_bytes() for the decode forward)";
     case ATTN_SINK_ERR_HIP: return "a HIP launch failed";
     case ATTN_SINK_ERR_ALIGN: return "a tensor base pointer is not 16-byte aligned";
     case ATTN_SINK_ERR_SCRATCH:

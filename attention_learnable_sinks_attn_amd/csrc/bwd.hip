@@ -124,7 +124,7 @@ __global__ __launch_bounds__(128 * NS, D == 64 ? 2 : 1) void attn_sink_bwd_dkdv_
 
   // Each stream owns a ring of 2 slots; step s lives in slot s % 2. The two key halves of a
   // stream split the copies of a step: half 0 copies the Q tile and the -LSE/scale, -D rows,
-  // half 1 the dO tile (tile_copy layout). Full tiles go through buffer resources; in the last,
+  // half 1 the dO tile (tile_copy_d layout). Full tiles go through buffer resources; in the last,
   // partial tile rows past the end repeat the last row (they are masked).
   unsigned char* ring = smem + st * kKvStreamBytes;
   const int qstride = a.Hq * D;  // elements per token row of q / dout
@@ -174,7 +174,7 @@ __global__ __launch_bounds__(128 * NS, D == 64 ? 2 : 1) void attn_sink_bwd_dkdv_
   for (int c = 0; c < 4; ++c) aoff[c] = tile_frag_off(l32, grp, c);
   int toff[2][2];  // [d block][+0 / +4 rows]
   tile_tr_offsets(lane, toff);
-  // Transposed operands (see load_tr8): Q^T (tile 0) or dO^T (tile 1) rows d = 32db + l32, k
+  // Transposed operands (see ds_read_tr16_b64_asm): Q^T (tile 0) or dO^T (tile 1) rows d = 32db + l32, k
   // slots = query rows 16*half + 8grp + 0..7 of the slot at LDS address `slot_lds`.
   // The slot and the 32-row block are compile-time constants below (the step loop is unrolled
   // over the two ring slots), so their LDS offset goes into the reads' offset fields.

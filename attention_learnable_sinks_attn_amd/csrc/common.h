@@ -78,23 +78,6 @@ __device__ __forceinline__ bool wave_any(bool pred) { return __builtin_amdgcn_ba
 
 __device__ __forceinline__ bf16x8 load_bf16x8(const __bf16* p) { return *reinterpret_cast<const bf16x8*>(p); }
 
-// Operand fragment of a TRANSPOSED tile, read from X stored row-major in LDS (`stride` bf16 per
-// row) with two ds_read_b64_tr_b16: lane l receives X[k0 + 8*(l/32) + e][m0 + l%32], e = 0..7,
-// i.e. the MFMA operand whose row (or column) index runs along X's columns and whose k slots run
-// along X's rows. ds_read_b64_tr_b16 works on 16-lane groups: when the group's lanes address a
-// 4-row x 16-column block (lane s at row s/4, columns 4*(s%4)..+3), lane t of the group gets
-// column t of the block, rows 0..3.
-__device__ __forceinline__ bf16x8 load_tr8(const __bf16* lds, int stride, int k0, int m0) {
-  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-  typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
-  const int l = threadIdx.x & 63;
-  const int s = l & 15;
-  const __bf16* p = lds + (k0 + 8 * (l >> 5) + (s >> 2)) * stride + m0 + 16 * ((l >> 4) & 1) + 4 * (s & 3);
-  const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p));
-  const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p + 4 * stride));
-  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-}
-
 __device__ __forceinline__ bf16x8 zero_bf16x8() {
   bf16x8 z;
 #pragma unroll
@@ -108,8 +91,6 @@ __device__ __forceinline__ f32x16 zero_f32x16() {
   for (int i = 0; i < 16; ++i) z[i] = 0.0f;
   return z;
 }
-
-__device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32); }
 
 // Reductions over the lane pair (l, l ^ 32) with one v_permlane32_swap: the swap leaves the
 // low-half values in both halves of one register and the high-half values in the other.
@@ -142,20 +123,6 @@ __device__ __forceinline__ KeyBounds key_bounds(int i, int len, int causal, int 
 // Membership of x in the interval first .. first + count - 1 as one unsigned comparison:
 // in_span(x - first, count) (a negative offset wraps to a large unsigned value).
 __device__ __forceinline__ bool in_span(int offset, unsigned count) { return (unsigned)offset < count; }
-
-// Makes a register value opaque to the optimiser (no instruction is emitted). Used at the top of
-// rarely taken branches so that their arithmetic is not speculated onto the common path.
-__device__ __forceinline__ void opaque(f32x16& x) {
-#pragma unroll
-  for (int i = 0; i < 16; ++i) asm volatile("" : "+v"(x[i]));
-}
-__device__ __forceinline__ void opaque(bf16x8& x) {
-  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-  u32x4 u = __builtin_bit_cast(u32x4, x);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(u[i]));
-  x = __builtin_bit_cast(bf16x8, u);
-}
 
 // Direct global -> LDS copies (gfx950): lane l's 16 (or 4) bytes at `src` land at LDS byte
 // offset lds_dst + 16 * l (or 4 * l). `lds_dst` must be wave-uniform. The copy completes
@@ -198,10 +165,17 @@ __device__ __forceinline__ unsigned lds_addr(const void* p) {
   return (unsigned)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
-// ds_read_b64_tr_b16 (see load_tr8) issued through inline asm. The compiler makes every
-// transposing LDS read it knows about wait for all outstanding direct global->LDS copies
-// (vmcnt(0)), which would serialise a kernel that keeps copies in flight into other LDS slots.
-// The result is not tracked either: wait_lds_into must follow before any use.
+// Operand fragments of TRANSPOSED tiles come from ds_read_b64_tr_b16, which works on 16-lane
+// groups: when the group's lanes address a 4-row x 16-column block of a row-major bf16 array X in
+// LDS (lane s at row s/4, columns 4*(s%4)..+3), lane t of the group receives column t of the
+// block, rows 0..3. Two such reads, 4 rows apart, give lane l the eight elements
+// X[k0 + 8*(l/32) + e][m0 + l%32], e = 0..7: the MFMA operand whose row (or column) index runs
+// along X's columns and whose k slots run along X's rows.
+//
+// The read is issued through inline asm: the compiler makes every transposing LDS read it knows
+// about wait for all outstanding direct global->LDS copies (vmcnt(0)), which would serialise a
+// kernel that keeps copies in flight into other LDS slots. The result is not tracked either:
+// wait_lds_into must follow before any use.
 template <int OFF>
 __device__ __forceinline__ u32x2 ds_read_tr16_b64_asm(unsigned addr) {
   static_assert(OFF >= 0 && OFF < 65536, "16-bit DS offset");
@@ -249,7 +223,7 @@ __device__ __forceinline__ int tile_frag_off(int l32, int grp, int c) {
   return r * 128 + (((2 * c + grp) ^ tile_swz(r)) << 4);
 }
 
-// Per-lane byte offsets of the transposing reads (see load_tr8) of a swizzled tile:
+// Per-lane byte offsets of the transposing reads (see ds_read_tr16_b64_asm) of a swizzled tile:
 // off[mb][h] addresses rows 8grp + (l%16)/4 + 4h, logical columns 32mb + 16((l>>4)&1) + 4(l%4).
 // Rows k0 + ... (k0 a multiple of 16) add 128 * k0, which fits the instruction's offset field.
 __device__ __forceinline__ void tile_tr_offsets(int lane, int (&off)[2][2]) {
@@ -266,27 +240,14 @@ __device__ __forceinline__ void tile_tr_offsets(int lane, int (&off)[2][2]) {
   }
 }
 
-// Copy u of a swizzled tile: lane l fetches tile row 8u + l/8 (global row min(row0 + 8u + l/8,
-// last), `stride` elements apart), logical chunk (l % 8) ^ tile_swz(row), into LDS tile + 1024u +
-// 16l, i.e. physical chunk l % 8 of that row.
-__device__ __forceinline__ void tile_copy(const __bf16* base, int row0, int last, int stride, unsigned char* tile,
-                                          int u, int lane) {
-  const int r = 8 * u + (lane >> 3);
-  dma16(base + (size_t)min(row0 + r, last) * stride + 8 * ((lane & 7) ^ tile_swz(r)), tile + 1024 * u);
-}
-
-// Copies of a full tile (all 64 rows inside the sequence) through a buffer resource based at the
-// tile's first row, rows `row_bytes` apart. Copy u moves the same bytes as tile_copy(u): lane l's
-// offset is off[u % 2] (row l/8 and its swizzled chunk; the swizzle of row 8u + l/8 depends on u
-// only through u % 2) plus the uniform 8u rows.
+// Per-lane offsets for copies of a full tile through a buffer resource based at the tile's first
+// row, rows `row_bytes` apart (tile_copy_full_d): off[h] is lane l's row l/8 and its swizzled
+// chunk for the copies whose first row is 8h mod 16 (the swizzle of row 8u + l/8 depends on u only
+// through u % 2); the uniform 8u rows are added per copy.
 __device__ __forceinline__ void tile_copy_offsets(int lane, unsigned row_bytes, unsigned (&off)[2]) {
   const int r = lane >> 3;
   off[0] = r * row_bytes + 16 * ((lane & 7) ^ tile_swz(r));
   off[1] = r * row_bytes + 16 * ((lane & 7) ^ tile_swz(r + 8));
-}
-__device__ __forceinline__ void tile_copy_full(__amdgpu_buffer_rsrc_t rsrc, const unsigned (&off)[2],
-                                               unsigned row_bytes, unsigned char* tile, int u) {
-  bdma16(rsrc, off[u & 1], 8u * u * row_bytes, tile + 1024 * u);
 }
 
 // f(std::integral_constant<int, i>()) for i = 0 .. N - 1, so that i can be a template argument
@@ -325,9 +286,10 @@ __device__ __forceinline__ int frag_off(const int (&aoff)[4], int c, int rb) {
   return (c / 4) * Geo<D>::kPanelBytes + 4096 * rb + aoff[c % 4];
 }
 
-// Copy u (0 .. kCopies - 1) of an 8 KiB tile of D-element rows: panel u / kCopiesPerPanel, rows
-// 8 (u % kCopiesPerPanel) + l / 8 (global row min(row0 + that, last), `stride` elements apart),
-// into LDS tile + 1024 u. At D = 64 this is tile_copy.
+// Copy u (0 .. kCopies - 1) of an 8 KiB swizzled tile of D-element rows: lane l fetches panel
+// u / kCopiesPerPanel of tile row r = 8 (u % kCopiesPerPanel) + l / 8 (global row min(row0 + r,
+// last), `stride` elements apart), logical 16-byte chunk (l % 8) ^ tile_swz(r), into LDS
+// tile + 1024 u + 16 l, i.e. physical chunk l % 8 of that row.
 template <int D>
 __device__ __forceinline__ void tile_copy_d(const __bf16* base, int row0, int last, int stride, unsigned char* tile,
                                             int u, int lane) {
@@ -335,8 +297,8 @@ __device__ __forceinline__ void tile_copy_d(const __bf16* base, int row0, int la
   const int r = 8 * (u % Geo<D>::kCopiesPerPanel) + (lane >> 3);
   dma16(base + (size_t)min(row0 + r, last) * stride + 64 * p + 8 * ((lane & 7) ^ tile_swz(r)), tile + 1024 * u);
 }
-// The same copy of a full tile through a buffer resource based at the tile's first row (offsets
-// from tile_copy_offsets). At D = 64 this is tile_copy_full.
+// The same copy of a full tile (every row inside the sequence) through a buffer resource based at
+// the tile's first row (offsets from tile_copy_offsets).
 template <int D>
 __device__ __forceinline__ void tile_copy_full_d(__amdgpu_buffer_rsrc_t rsrc, const unsigned (&off)[2],
                                                  unsigned row_bytes, unsigned char* tile, int u) {

@@ -11,7 +11,7 @@
 // column c = j * G + (query head - g * G) for new token j, taken 32 at a time as the wave's MFMA
 // columns, so the G query heads of a KV head share every K and V tile: S^T = K Q^T (32x32x16 MFMA, keys on the C
 // rows), a sink-free online softmax per column (lane), O^T += V^T P^T, with K and V tiles of 64
-// keys streamed through a 3-slot LDS ring of swizzled tiles (direct global->LDS copies two tiles
+// keys (32 at head_dim 128) streamed through a 3-slot LDS ring of swizzled tiles (direct global->LDS copies two tiles
 // ahead, transposing reads for V^T; see common.h). It writes the chunk's running max (log2
 // units), denominator and unnormalised output per column. attn_sink_decode_combine_kernel merges
 // the chunks of a (sequence, KV head, column) and adds the sink once: with M = max(S_h log2e, m_c),

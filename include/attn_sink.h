@@ -36,8 +36,9 @@
  *    from every row, is never masked and does not count toward W. The sink is added after
  *    scaling: it is never multiplied by scale.
  *  - Outputs are overwritten, never accumulated into. The caller owns every buffer; the library
- *    allocates nothing, keeps no global state, and only enqueues work on `stream` (NULL = the
- *    default stream). Calls return before the GPU work finishes; errors raised by the device
+ *    allocates nothing, keeps no state between calls (apart from attn_sink_bwd_noalloc's static
+ *    scratch array, described there), and only enqueues work on `stream` (NULL = the default
+ *    stream). Calls return before the GPU work finishes; errors raised by the device
  *    surface at the caller's next synchronisation.
  *  - Errors: 0 on success, a negative ATTN_SINK_ERR_* code otherwise. All argument checks run on
  *    the host before anything is enqueued; a failing call enqueues nothing. The contents of
@@ -61,11 +62,13 @@ enum {
   ATTN_SINK_ERR_NULL_PTR = -1,    /* a required pointer (or the shape struct) is NULL */
   ATTN_SINK_ERR_BAD_SHAPE = -2,   /* T < 0, B < 1, Hq < 1, Hkv < 1, Hq % Hkv != 0, max_seqlen < 0
                                      or max_seqlen > T, max_seqlen * Hq * D >= 2^31 (offsets
-                                     inside one sequence are 32-bit), or T * Hq > 2^34 (grid size) */
+                                     inside one sequence are 32-bit), T * Hq > 2^34, or
+                                     ceil(max_seqlen / 64) * Hq * B >= 2^31 (grid size) */
   ATTN_SINK_ERR_UNSUPPORTED = -3, /* head_dim not 64 or 128, or out_dtype not ATTN_SINK_F32 (attn_sink_bwd)
                                      or not ATTN_SINK_F32 / ATTN_SINK_BF16 (attn_sink_fwd) */
   ATTN_SINK_ERR_BAD_WINDOW = -4,  /* window < 0 (attn_sink_decode_fwd only) */
-  ATTN_SINK_ERR_WORKSPACE = -5,   /* workspace NULL or smaller than attn_sink_bwd_workspace_bytes() */
+  ATTN_SINK_ERR_WORKSPACE = -5,   /* workspace NULL, not 16-byte aligned, or smaller than
+                                     attn_sink_bwd_workspace_bytes() (attn_sink_decode_workspace_bytes()) */
   ATTN_SINK_ERR_HIP = -6,         /* a HIP launch failed (hipGetLastError after the launch) */
   ATTN_SINK_ERR_ALIGN = -7,       /* a tensor base pointer is not 16-byte aligned */
   ATTN_SINK_ERR_BAD_SEQLENS = -8, /* attn_sink_check_cu_seqlens: offsets inconsistent with the shape */
