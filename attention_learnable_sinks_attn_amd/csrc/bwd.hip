@@ -636,17 +636,33 @@ __global__ __launch_bounds__(256, 2) void attn_sink_bwd_dq_kernel(BwdArgs a) {
   const float dtot = sum_xor32(dsum);
   if (qok && grp == 0) a.negd[(size_t)h * a.T + cs + qi] = -dtot;
   float wsum = 0.0f;
-  if (qok) {
-    float* qrow = a.dq + ((size_t)(cs + qi) * a.Hq + h) * D;
+  if (qok && grp == 0) wsum = fast_exp2(__builtin_fmaf(a.sinks[h], kLog2e, -lse2)) * dtot;
+  // dQ goes through LDS: a lane holds 4-float pieces of one row, so direct stores would put
+  // 32-byte pieces of 32 rows in each store instruction; from LDS each instruction writes whole
+  // rows. Each wave stages its kRows x D tile in its part of the ring (free once every wave is
+  // done with the last tile), 16-byte chunk k of row r at chunk k ^ (r % kCpr).
+  {
+    constexpr int kCpr = D / 4;      // 16-byte chunks per dQ row
+    constexpr int kRpi = 64 / kCpr;  // rows per store instruction
+    static_assert(4 * kRows * D * 4 <= kDqRing * kDqSlotBytes, "four staged tiles fit in the ring");
+    __syncthreads();
+    float* stage = reinterpret_cast<float*>(ring) + wave * kRows * D;
 #pragma unroll
     for (int db = 0; db < G_::kDBlocks; ++db) {
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
-        f32x4 val = {acc[db][4 * r4], acc[db][4 * r4 + 1], acc[db][4 * r4 + 2], acc[db][4 * r4 + 3]};
-        *reinterpret_cast<f32x4*>(qrow + 32 * db + 8 * r4 + 4 * grp) = val * a.scale;
+        const int k = 8 * db + 2 * r4 + grp;  // d = 4k .. 4k + 3
+        const f32x4 val = {acc[db][4 * r4], acc[db][4 * r4 + 1], acc[db][4 * r4 + 2], acc[db][4 * r4 + 3]};
+        *reinterpret_cast<f32x4*>(stage + l32 * D + 4 * (k ^ (l32 % kCpr))) = val * a.scale;
       }
     }
-    if (grp == 0) wsum = fast_exp2(__builtin_fmaf(a.sinks[h], kLog2e, -lse2)) * dtot;
+    const int k = lane % kCpr;
+#pragma unroll
+    for (int it = 0; it < kRows / kRpi; ++it) {
+      const int r = kRpi * it + lane / kCpr;
+      const f32x4 val = *reinterpret_cast<const f32x4*>(stage + r * D + 4 * (k ^ (r % kCpr)));
+      if (q0 + r < len) *reinterpret_cast<f32x4*>(a.dq + ((size_t)(cs + q0 + r) * a.Hq + h) * D + 4 * k) = val;
+    }
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) wsum += __shfl_xor(wsum, off);

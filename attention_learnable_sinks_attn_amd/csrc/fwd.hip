@@ -401,12 +401,53 @@ __global__ __launch_bounds__(256, 2) void attn_sink_fwd_kernel(FwdArgs a) {
   }
 
   // Epilogue: combine the two lane halves' partial denominators, normalise, store.
+  if (a.out_bf16) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int qi = q0 + 32 * nb + l32;
+      if (qi < len) {  // also false for every lane of a wave past the sequence end
+        cols.store(nb, a.out, a.out_bf16, ((size_t)(cs + qi) * a.Hq + h) * D, a.lse + (size_t)h * a.T + cs + qi, grp);
+      }
+    }
+    return;
+  }
+  // fp32 O goes through LDS: a lane holds 4-float pieces of one row, so direct stores would put
+  // 32-byte pieces of 32 rows in each store instruction; from LDS each instruction writes whole
+  // rows. Each wave stages its kRows x D tile in its quarter of the ring (free once every wave is
+  // done with the last tile), 16-byte chunk k of row r at chunk k ^ (r % kCpr), which spreads the
+  // writes of the 32 lanes of a register (32 rows, one chunk) over the banks.
+  constexpr int kCpr = D / 4;         // 16-byte chunks per O row
+  constexpr int kRpi = 64 / kCpr;     // rows per store instruction
+  static_assert(kRows * D * 4 * 4 <= kRing * kSlotBytes, "four staged tiles fit in the ring");
+  __syncthreads();
+  float* stage = reinterpret_cast<float*>(ring) + wave * kRows * D;
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
-    const int qi = q0 + 32 * nb + l32;
-    if (qi < len) {  // also false for every lane of a wave past the sequence end
-      cols.store(nb, a.out, a.out_bf16, ((size_t)(cs + qi) * a.Hq + h) * D, a.lse + (size_t)h * a.T + cs + qi, grp);
+    const int r = 32 * nb + l32;
+    const float ltot = sum_xor32(cols.lsum[nb]);
+    const float inv = ltot > 0.0f ? 1.0f / ltot : 0.0f;
+#pragma unroll
+    for (int db = 0; db < G_::kDBlocks; ++db) {
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int k = 8 * db + 2 * r4 + grp;  // d = 4k .. 4k + 3
+        const f32x4 val = {cols.o[db][nb][4 * r4] * inv, cols.o[db][nb][4 * r4 + 1] * inv,
+                           cols.o[db][nb][4 * r4 + 2] * inv, cols.o[db][nb][4 * r4 + 3] * inv};
+        *reinterpret_cast<f32x4*>(stage + r * D + 4 * (k ^ (r % kCpr))) = val;
+      }
     }
+    const int qi = q0 + r;
+    if (grp == 0 && qi < len) {
+      a.lse[(size_t)h * a.T + cs + qi] = ltot > 0.0f ? (cols.m[nb] + fast_log2(ltot)) * kLn2 : kNegInf;
+    }
+  }
+  const int k = lane % kCpr;
+#pragma unroll
+  for (int it = 0; it < kRows / kRpi; ++it) {
+    const int r = kRpi * it + lane / kCpr;
+    const f32x4 val = *reinterpret_cast<const f32x4*>(stage + r * D + 4 * (k ^ (r % kCpr)));
+    const int qi = q0 + r;
+    if (qi < len) *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + ((size_t)(cs + qi) * a.Hq + h) * D + 4 * k) = val;
   }
 }
 
