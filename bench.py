@@ -79,18 +79,18 @@ KERNEL_FLOPS_PER_PAIR_D = {
 # (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch) scaled by what the same counters read for the
 # copy probe; valid only for kernel sources with the recorded digest.
 TRAFFIC = {
-    ("causal4k", "attn_sink_bwd_dkdv_kernel"): {"bytes": 146633428, "digest": "49011181511ba2f2"},
-    ("window4k", "attn_sink_bwd_dkdv_kernel"): {"bytes": 105772827, "digest": "49011181511ba2f2"},
-    ("window4k", "attn_sink_bwd_dq_kernel"): {"bytes": 213329835, "digest": "49011181511ba2f2"},
-    ("varlen_window", "attn_sink_bwd_dkdv_kernel"): {"bytes": 1707646133, "digest": "49011181511ba2f2"},
-    ("varlen_window", "attn_sink_bwd_dq_kernel"): {"bytes": 3648384318, "digest": "49011181511ba2f2"},
-    ("band4k", "attn_sink_bwd_dkdv_kernel"): {"bytes": 119648156, "digest": "49011181511ba2f2"},
-    ("band4k", "attn_sink_bwd_dq_kernel"): {"bytes": 213371607, "digest": "49011181511ba2f2"},
-    ("decode32k", "attn_sink_decode_partial_kernel"): {"bytes": 368459570, "digest": "49011181511ba2f2"},
-    ("causal4k", "attn_sink_fwd_kernel"): {"bytes": 114517828, "digest": "49011181511ba2f2"},
-    ("causal4k", "attn_sink_bwd_dq_kernel"): {"bytes": 221265699, "digest": "49011181511ba2f2"},
-    ("varlen_causal", "attn_sink_bwd_dkdv_kernel"): {"bytes": 8702002983, "digest": "49011181511ba2f2"},
-    ("long32k", "attn_sink_bwd_dkdv_kernel"): {"bytes": 35421619970, "digest": "49011181511ba2f2"},
+    ("causal4k", "attn_sink_bwd_dkdv_kernel"): {"bytes": 146626429, "digest": "782483b013869cc1"},
+    ("window4k", "attn_sink_bwd_dkdv_kernel"): {"bytes": 105203660, "digest": "782483b013869cc1"},
+    ("window4k", "attn_sink_bwd_dq_kernel"): {"bytes": 213173250, "digest": "782483b013869cc1"},
+    ("varlen_window", "attn_sink_bwd_dkdv_kernel"): {"bytes": 1706627600, "digest": "782483b013869cc1"},
+    ("varlen_window", "attn_sink_bwd_dq_kernel"): {"bytes": 3648226776, "digest": "782483b013869cc1"},
+    ("band4k", "attn_sink_bwd_dkdv_kernel"): {"bytes": 120149332, "digest": "782483b013869cc1"},
+    ("band4k", "attn_sink_bwd_dq_kernel"): {"bytes": 213304683, "digest": "782483b013869cc1"},
+    ("decode32k", "attn_sink_decode_partial_kernel"): {"bytes": 368462427, "digest": "782483b013869cc1"},
+    ("causal4k", "attn_sink_fwd_kernel"): {"bytes": 114529091, "digest": "782483b013869cc1"},
+    ("causal4k", "attn_sink_bwd_dq_kernel"): {"bytes": 221294545, "digest": "782483b013869cc1"},
+    ("varlen_causal", "attn_sink_bwd_dkdv_kernel"): {"bytes": 8753615109, "digest": "782483b013869cc1"},
+    ("long32k", "attn_sink_bwd_dkdv_kernel"): {"bytes": 36592952243, "digest": "782483b013869cc1"},
 }
 def _code_only(text: str) -> str:
     """C/C++ source without its comments and with whitespace runs collapsed (string literals kept)."""
