@@ -229,3 +229,59 @@ def test_workspace_without_head_halves():
     s = shape(T=4096, maxlen=4096, hq=24, hkv=8)
     dsink = 24 * (4096 // 32 + 2) * 4
     assert lib.attn_sink_bwd_workspace_bytes(ctypes.byref(s)) == 2 * 24 * 4096 * 4 + (dsink + 255) // 256 * 256
+
+
+C_CALLER = r"""
+#include <stdio.h>
+#include "attn_sink.h"
+int main(void) {
+  const int32_t cu[3] = {0, 3000, 4096};
+  attn_sink_shape s = {.total_tokens = 4096, .num_seqs = 2, .max_seqlen = 3000, .num_heads_q = 64,
+                       .num_heads_kv = 8, .head_dim = 64, .softmax_scale = 0.0f, .out_dtype = ATTN_SINK_F32};
+  printf("%d %d %zu %d %s\n", attn_sink_check_cu_seqlens(cu, 2, 4096, 3000),
+         attn_sink_check_cu_seqlens(cu, 2, 4096, 2999), attn_sink_bwd_workspace_bytes(&s),
+         attn_sink_bwd_num_kernels(), attn_sink_strerror(ATTN_SINK_ERR_BAD_SEQLENS));
+  return 0;
+}
+"""
+
+
+def _compiler(name):
+    import shutil
+    path = shutil.which(name)
+    if path is None:
+        pytest.skip(f"{name} not found")
+    return path
+
+
+@pytest.mark.parametrize("cc,std,suffix", [("gcc", "-std=c99", ".c"), ("g++", "-std=c++17", ".cpp")])
+def test_header_compiles_alone(tmp_path, cc, std, suffix):
+    # plain C and C++ callers need no HIP headers
+    src = tmp_path / ("use" + suffix)
+    src.write_text('#include "attn_sink.h"\nint f(void) { return ATTN_SINK_OK + (int)sizeof(attn_sink_shape); }\n')
+    import subprocess
+    r = subprocess.run([_compiler(cc), std, "-Wall", "-Wextra", "-Werror", "-fsyntax-only", "-I",
+                        os.path.join(ROOT, "include"), str(src)], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+
+
+@needs_lib
+def test_c_program_links_and_calls_host_entry_points(tmp_path):
+    import subprocess
+    src = tmp_path / "caller.c"
+    src.write_text(C_CALLER)
+    exe = tmp_path / "caller"
+    libdir = os.path.dirname(asa.library_path())
+    r = subprocess.run([_compiler("gcc"), "-std=c99", "-Wall", "-Werror", "-I", os.path.join(ROOT, "include"),
+                        str(src), "-o", str(exe), f"-L{libdir}", "-l:libattn_sink.so", f"-Wl,-rpath,{libdir}"],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stderr
+    fields = r.stdout.split(" ", 4)
+    lib = asa.load_library()
+    s = asa.Shape(4096, 2, 3000, 64, 8, 64, 0.0, 0)
+    assert int(fields[0]) == 0 and int(fields[1]) == -8
+    assert int(fields[2]) == lib.attn_sink_bwd_workspace_bytes(ctypes.byref(s))
+    assert int(fields[3]) == lib.attn_sink_bwd_num_kernels()
+    assert fields[4].startswith("cu_seqlens")
