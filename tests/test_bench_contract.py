@@ -44,18 +44,18 @@ def test_source_digest_ignores_comments_but_not_code():
 
 @pytest.mark.gpu
 def test_bench_line(monkeypatch, capsys):
-    print("[gpu] bench.py --steps 3 --warmup 1 --settle-ms 0 --no-cpu-baseline --no-peaks (causal4k)", flush=True)
-    monkeypatch.setattr(sys, "argv", ["bench.py", "--steps", "3", "--warmup", "1", "--settle-ms", "0",
+    print("[gpu] bench.py --steps 10 --warmup 5 --settle-ms 100 --no-cpu-baseline --no-peaks (causal4k)", flush=True)
+    monkeypatch.setattr(sys, "argv", ["bench.py", "--steps", "10", "--warmup", "5", "--settle-ms", "100",
                                       "--no-cpu-baseline", "--no-peaks"])
     bench.main()
     lines = [l for l in capsys.readouterr().out.splitlines() if l.startswith("{")]
     assert len(lines) == 1
     r = json.loads(lines[0])
     assert r["metric"] == bench.METRIC and r["unit"] == "TFLOP/s" and r["higher_is_better"] is True
-    assert r["n_gpus"] == 1 and r["steps"] == 3 and r["warmup"] == 1
+    assert r["n_gpus"] == 1 and r["steps"] == 10 and r["warmup"] == 5
     assert r["dtype"] == "bf16" and r["data"] == "synthetic" and r["vs_baseline"] is None
     assert r["config"]["workload"] == "causal4k" and r["config"]["heads_q"] == 64 and r["config"]["heads_kv"] == 8
-    assert r["settle"] == {"ms": 0.0, "steps": 0}
+    assert r["settle"]["ms"] == 100.0 and r["settle"]["steps"] > 0
     inp = make_workload_inputs("causal4k", 0)
     flops = visible_pairs(inp.lengths, inp.causal, inp.window) * 64 * 14 * 64
     assert r["ms_per_step"] > 0
