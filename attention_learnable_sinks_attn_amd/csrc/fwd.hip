@@ -30,7 +30,7 @@
 // The reference max is lazy: the sum and the accumulator are only rescaled when some row of a
 // 32-query block sees a score more than 2^8 above its reference, so the unnormalised values
 // exp2(s - m) stay below 256 and most tiles skip the rescale. Their bf16 rounding is then not
-// exact for a row's largest value, and tiles where a value can reach a quarter of its row's
+// exact for a row's largest value, and tiles where a value can reach an eighth of its row's
 // probability mass also multiply the rounding residuals (see the tile body).
 #include <type_traits>
 
@@ -44,9 +44,11 @@ constexpr int kTileBytes = 8192;              // one swizzled K or V tile (64 ke
 constexpr int kSlotBytes = 2 * kTileBytes;    // K tile, then V tile
 constexpr int kRing = 4;                      // LDS ring slots (two pairs of tiles)
 // Probabilities above this share of their row get the residual P.V product (see the tile body).
-// The largest ones dominate the rounding error of O: on peaked rows a quarter already removes
-// most of it, and the rows that reach it are few, so the extra products stay rare.
-constexpr float kFwdSplitThreshold = 0.25f;
+// The largest ones dominate the rounding error of O, and through D = dO . O that of every dS of
+// the row in the dQ pass, which grows with head_dim and the softmax scale: at a quarter, a
+// head_dim-128 batch with three times the default scale put dQ at 1.08e-2; at an eighth, 3.7e-3.
+// On N(0,1) inputs at the default scale about a tenth of the (row block, tile) units take it.
+constexpr float kFwdSplitThreshold = 0.125f;
 // Growth of a row's maximum (log2 units) that forces a rescale of its sum and accumulator.
 constexpr float kLazyMax = 8.0f;
 
@@ -172,7 +174,8 @@ struct FwdCols {
       // residuals of its P: O then carries about 16 significant bits of its largest
       // probabilities, which matters twice downstream, in O itself and in D = dO . O of the
       // backward, where an error in D scales every dS of the row (dQ of peaked rows crossed 1e-2
-      // through it without this product). The test needs only values known before the softmax,
+      // through it without this product, and at head_dim 128 with a large scale with it at a
+      // threshold of a quarter). The test needs only values known before the softmax,
       // which keeps it off the common path's critical chain; on N(0,1) inputs it is mostly a row
       // block's first tile that takes the extra products, and rows that a large sink dominates
       // never do.
