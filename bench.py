@@ -79,18 +79,18 @@ KERNEL_FLOPS_PER_PAIR_D = {
 # (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch) scaled by what the same counters read for the
 # copy probe; valid only for kernel sources with the recorded digest.
 TRAFFIC = {
-    ("causal4k", "attn_sink_bwd_dkdv_kernel"): {"bytes": 146626429, "digest": "782483b013869cc1"},
-    ("window4k", "attn_sink_bwd_dkdv_kernel"): {"bytes": 105203660, "digest": "782483b013869cc1"},
-    ("window4k", "attn_sink_bwd_dq_kernel"): {"bytes": 213173250, "digest": "782483b013869cc1"},
-    ("varlen_window", "attn_sink_bwd_dkdv_kernel"): {"bytes": 1706627600, "digest": "782483b013869cc1"},
-    ("varlen_window", "attn_sink_bwd_dq_kernel"): {"bytes": 3648226776, "digest": "782483b013869cc1"},
-    ("band4k", "attn_sink_bwd_dkdv_kernel"): {"bytes": 120149332, "digest": "782483b013869cc1"},
-    ("band4k", "attn_sink_bwd_dq_kernel"): {"bytes": 213304683, "digest": "782483b013869cc1"},
-    ("decode32k", "attn_sink_decode_partial_kernel"): {"bytes": 368462427, "digest": "782483b013869cc1"},
-    ("causal4k", "attn_sink_fwd_kernel"): {"bytes": 114529091, "digest": "782483b013869cc1"},
-    ("causal4k", "attn_sink_bwd_dq_kernel"): {"bytes": 221294545, "digest": "782483b013869cc1"},
-    ("varlen_causal", "attn_sink_bwd_dkdv_kernel"): {"bytes": 8753615109, "digest": "782483b013869cc1"},
-    ("long32k", "attn_sink_bwd_dkdv_kernel"): {"bytes": 36592952243, "digest": "782483b013869cc1"},
+    ("causal4k", "attn_sink_bwd_dkdv_kernel"): {"bytes": 146634536, "digest": "44f8c43fa5eb5433"},
+    ("window4k", "attn_sink_bwd_dkdv_kernel"): {"bytes": 105793227, "digest": "44f8c43fa5eb5433"},
+    ("window4k", "attn_sink_bwd_dq_kernel"): {"bytes": 213175578, "digest": "44f8c43fa5eb5433"},
+    ("varlen_window", "attn_sink_bwd_dkdv_kernel"): {"bytes": 1706812248, "digest": "44f8c43fa5eb5433"},
+    ("varlen_window", "attn_sink_bwd_dq_kernel"): {"bytes": 3648308856, "digest": "44f8c43fa5eb5433"},
+    ("band4k", "attn_sink_bwd_dkdv_kernel"): {"bytes": 119770026, "digest": "44f8c43fa5eb5433"},
+    ("band4k", "attn_sink_bwd_dq_kernel"): {"bytes": 213320701, "digest": "44f8c43fa5eb5433"},
+    ("decode32k", "attn_sink_decode_partial_kernel"): {"bytes": 368462096, "digest": "44f8c43fa5eb5433"},
+    ("causal4k", "attn_sink_fwd_kernel"): {"bytes": 114545573, "digest": "44f8c43fa5eb5433"},
+    ("causal4k", "attn_sink_bwd_dq_kernel"): {"bytes": 221308528, "digest": "44f8c43fa5eb5433"},
+    ("varlen_causal", "attn_sink_bwd_dkdv_kernel"): {"bytes": 8740251349, "digest": "44f8c43fa5eb5433"},
+    ("long32k", "attn_sink_bwd_dkdv_kernel"): {"bytes": 35438920660, "digest": "44f8c43fa5eb5433"},
 }
 def _code_only(text: str) -> str:
     """C/C++ source without its comments and with whitespace runs collapsed (string literals kept)."""
