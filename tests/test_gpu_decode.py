@@ -1,8 +1,9 @@
 """Parity of the HIP decode (inference-shaped) forward, through the C ABI, against the fp64 oracle,
 and its consistency with the training forward.
 
-Tolerances against the oracle are those of the training forward: max-abs 1e-2 on O (fp32 or bf16
-output) and 1e-3 on the fp32 LSE. Small cases compare every element and cover several key chunks
+Tolerances against the oracle are those of the training forward: max-abs 1e-2 on O and 1e-3 on the
+fp32 LSE; a bf16 O may differ by half a bf16 ulp more (its own rounding, which alone exceeds 1e-2
+where |O| >= 4). Small cases compare every element and cover several key chunks
 with ragged tails, GQA groups of 1 to 8, per-sequence numbers of new tokens (0 included), a
 sliding window, sinks at -inf, sequences made only of new tokens and an empty batch. The
 full-size cases run the 8-sequence, 16k-32k-key GPT-OSS-shaped caches in the launch
@@ -43,17 +44,28 @@ def run_decode(d, out_dtype=torch.float32, scale=None):
     return out, lse
 
 
+def bf16_half_ulp(x):
+    """Half the bf16 spacing at |x| (8 significant bits): what storing x in bf16 may cost."""
+    e = np.floor(np.log2(np.maximum(np.abs(x), np.finfo(np.float32).tiny)))
+    return np.ldexp(1.0, (e - 8).astype(np.int64))
+
+
 def check_against_oracle(d, out, lse, scale=None):
     ro, rl = oracle.decode_forward(d.q, d.k, d.v, d.sinks, d.cu_q, d.cu_k, d.window, scale)
     o = out.double().cpu().numpy()
     l = lse.double().cpu().numpy()
     assert np.isfinite(o).all(), "out has non-finite values"
     eo = float(np.max(np.abs(o - ro))) if o.size else 0.0
+    # A bf16 output also carries its own rounding of the fp32 value y it was made from, at most half
+    # a bf16 ulp of y, which is at most half an ulp of the stored output (7.8e-3 for |O| in [2, 4),
+    # more above): the tolerance bounds the error beyond it.
+    slack = bf16_half_ulp(o) if out.dtype == torch.bfloat16 else np.zeros_like(ro)
+    eo_beyond = float(np.max(np.abs(o - ro) - slack)) if o.size else 0.0
     fin = np.isfinite(rl)
     assert (np.isfinite(l) == fin).all(), "LSE -inf pattern differs"
     el = float(np.max(np.abs(l[fin] - rl[fin]))) if fin.any() else 0.0
-    say(f"  out: max-abs err {eo:.3e}   lse: max-abs err {el:.3e}")
-    assert eo <= TOL_OUT, f"out: max-abs err {eo:.3e} > {TOL_OUT}"
+    say(f"  out: max-abs err {eo:.3e} ({eo_beyond:.3e} beyond the output's own rounding)   lse: max-abs err {el:.3e}")
+    assert eo_beyond <= TOL_OUT, f"out: max-abs err {eo_beyond:.3e} beyond the output rounding > {TOL_OUT}"
     assert el <= TOL_LSE, f"lse: max-abs err {el:.3e} > {TOL_LSE}"
 
 
