@@ -33,8 +33,11 @@
 //            workgroup it writes dK and dV; with head halves each half writes its own fp32
 //            partial. Halves double the number of workgroups, so that (launched longest first)
 //            short sequences still keep two per CU busy under a causal mask.
-//  3. finish: with head halves, dK = scale * (sum of the halves), dV = sum of the halves; and
-//            dL/dS_h = -(sum of the partials of head h), summed in a fixed order.
+//  3. finish: with head halves, dK = scale * (sum of the halves), dV = sum of the halves.
+//  dL/dS_h = -(sum of the partials of head h), in a fixed order, by one workgroup per query head
+//  at the end of the finish launch; or, for a dK/dV launch without halves of at most
+//  kDsinkFoldMaxBlocks workgroups, at the end of that launch, which then needs no finish launch
+//  (one launch more cost such a step more than its work).
 #include <type_traits>
 
 #include "kernels.h"
@@ -53,7 +56,43 @@ constexpr int kKvTileBytes = 8192;  // one Q or dO row tile (64 rows at D = 64, 
 // Head dim D = 64 or 128. A step is one 8 KiB row tile: 64 rows (two product blocks) at D = 64,
 // 32 rows at D = 128, whose dK/dV accumulators and K/V operands take twice the registers; that
 // instance runs one wave per SIMD and one head stream per workgroup (two workgroups per CU).
-template <int NS, int D>  // head streams per workgroup: 1 or 2 (waves = 2 key halves x NS)
+// dL/dS_h = -(sum of head h's partials src[0 .. n_slots)), in a fixed order: each thread sums its
+// slots in batches of eight loads in flight, then a shuffle tree per wave, then the waves in
+// order. The dQ pass wrote every slot (a partial or a zero) whenever there are rows (T > 0, as
+// cu[B] - cu[0] = T); it ran to completion before this launch began. Not inlined and given plain
+// scalars: inlined into the dK/dV kernel, it changed how the compiler kept that kernel's
+// arguments, and one more scalar value was reloaded inside the main loop.
+template <int kWaves>
+__device__ __attribute__((noinline)) void dsink_reduce(const float* src, int n_slots, int T, float* dst,
+                                                       float* part) {
+  constexpr int kThreads = 64 * kWaves, kBatch = 8;
+  float acc = 0.0f;
+  if (T > 0) {
+    for (int base = threadIdx.x; base < n_slots; base += kBatch * kThreads) {
+      float v[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) v[u] = base + u * kThreads < n_slots ? src[base + u * kThreads] : 0.0f;
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) acc += v[u];
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float sum = part[0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) sum += part[w];
+    *dst = -sum;
+  }
+}
+
+// kDsink: the launch ends with the dSink workgroups (no head halves, few key-block workgroups).
+// An instance of its own: the branch costs each workgroup two more scalar loads in a row before
+// its first tile (the compiler sinks the sequence-offset loads below it), which a small launch
+// repays by saving the finish launch, and a long one (thousands of workgroups) does not.
+template <int NS, int D, bool kDsink>  // head streams per workgroup: 1 or 2 (waves = 2 key halves x NS)
 __global__ __launch_bounds__(128 * NS, D == 64 ? 2 : 1) void attn_sink_bwd_dkdv_kernel(BwdArgs a) {
   using G_ = Geo<D>;
   constexpr int kKvRows = G_::kTileRows;                            // query rows per step
@@ -76,6 +115,15 @@ __global__ __launch_bounds__(128 * NS, D == 64 ? 2 : 1) void attn_sink_bwd_dkdv_
   // times in this order, and took 40% longer. Under a causal mask the first key blocks of a
   // sequence see the most query rows, so each sequence's longest workgroups start first.
   const int bid = blockIdx.x;
+  if constexpr (kDsink) {
+    const int n_dkdv = a.n_kblocks * a.B * a.Hkv;
+    if (bid >= n_dkdv) {  // the last Hq workgroups: dL/dS_h of one head each
+      const int h = bid - n_dkdv;
+      dsink_reduce<2 * NS>(a.dsink_part + (size_t)h * a.n_slots, a.n_slots, a.T, a.dsinks + h,
+                           reinterpret_cast<float*>(smem));
+      return;
+    }
+  }
   const int g = bid % a.Hkv;
   int rest = bid / a.Hkv;
   const int hh = rest % a.n_halves;
@@ -673,7 +721,7 @@ __global__ __launch_bounds__(256, 2) void attn_sink_bwd_dq_kernel(BwdArgs a) {
   }
   // The slots no row block maps to (a few between consecutive sequences with rows, those before
   // the first and after the last) get zeros from the neighbouring first / last row blocks, so
-  // that every slot is written exactly once and the finish pass can sum all of them.
+  // that every slot is written exactly once and the dSink workgroups can sum all of them.
   if (rows_live) {
     float* part = a.dsink_part + (size_t)h * a.n_slots;
     if (q0 + kRows >= len) {  // last row block: up to the first slot of the next sequence with rows
@@ -689,25 +737,15 @@ __global__ __launch_bounds__(256, 2) void attn_sink_bwd_dq_kernel(BwdArgs a) {
 }
 
 // ------------------------------------------------------------------------------------------
-// 3. Finish: with head halves, dK = scale * (sum of the halves' partials), dV = sum of the
-//    partials (blocks below n_sum_blocks, grid-stride; none with a single half, whose dK/dV pass
-//    wrote dK and dV), and dL/dS_h = -(sum of the partials of head h) (one block per head after
-//    those, fixed summation order).
+// 3. Finish (head halves only): dK = scale * (sum of the halves' partials), dV = sum of the
+//    partials (blocks below n_sum_blocks, grid-stride over float4s), then dL/dS_h (one block
+//    per head after those).
 // ------------------------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void attn_sink_bwd_finish_kernel(BwdArgs a, int n_sum_blocks) {
   if ((int)blockIdx.x >= n_sum_blocks) {
-    const int h = blockIdx.x - n_sum_blocks;
     __shared__ float part[4];
-    float acc = 0.0f;
-    // The dQ pass wrote every slot (partials or zeros), unless no sequence has rows.
-    if (a.cu[a.B] != a.cu[0]) {
-      for (int i = threadIdx.x; i < a.n_slots; i += 256) acc += a.dsink_part[(size_t)h * a.n_slots + i];
-    }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
-    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = acc;
-    __syncthreads();
-    if (threadIdx.x == 0) a.dsinks[h] = -(part[0] + part[1] + part[2] + part[3]);
+    const int h = blockIdx.x - n_sum_blocks;
+    dsink_reduce<4>(a.dsink_part + (size_t)h * a.n_slots, a.n_slots, a.T, a.dsinks + h, part);
     return;
   }
   const size_t plane4 = (size_t)a.T * a.Hkv * (a.D / 4);  // float4 per partial plane
@@ -725,22 +763,32 @@ __global__ __launch_bounds__(256) void attn_sink_bwd_finish_kernel(BwdArgs a, in
 
 }  // namespace
 
-template <int D>
+static constexpr long long kDsinkFoldMaxBlocks = 2048;
+
+// Whether the dK/dV launch reduces dSink itself (and no finish kernel is launched).
+static bool dsink_in_dkdv(const BwdArgs& a) {
+  return a.n_halves == 1 && (long long)a.n_kblocks * a.B * a.Hkv <= kDsinkFoldMaxBlocks;
+}
+
+template <int D, bool kDsink>
 void launch_dkdv_d(const BwdArgs& a, dim3 grid, hipStream_t stream) {
   if (D == 64 && a.kv_streams == 2) {  // head_dim 128 always runs one stream per workgroup
-    hipLaunchKernelGGL((attn_sink_bwd_dkdv_kernel<2, 64>), grid, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((attn_sink_bwd_dkdv_kernel<2, 64, kDsink>), grid, dim3(256), 0, stream, a);
   } else {
-    hipLaunchKernelGGL((attn_sink_bwd_dkdv_kernel<1, D>), grid, dim3(128), 0, stream, a);
+    hipLaunchKernelGGL((attn_sink_bwd_dkdv_kernel<1, D, kDsink>), grid, dim3(128), 0, stream, a);
   }
 }
 
 hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream) {
-  const long long nblocks = (long long)a.n_kblocks * a.B * a.Hkv * a.n_halves;
+  // key-block workgroups, then possibly one dSink workgroup per query head
+  const bool with_dsink = dsink_in_dkdv(a);
+  const long long nblocks = (long long)a.n_kblocks * a.B * a.Hkv * a.n_halves + (with_dsink ? a.Hq : 0);
   if (nblocks <= 0) return hipSuccess;
+  const dim3 grid((unsigned)nblocks);
   if (a.D == 128) {
-    launch_dkdv_d<128>(a, dim3((unsigned)nblocks), stream);
+    with_dsink ? launch_dkdv_d<128, true>(a, grid, stream) : launch_dkdv_d<128, false>(a, grid, stream);
   } else {
-    launch_dkdv_d<64>(a, dim3((unsigned)nblocks), stream);
+    with_dsink ? launch_dkdv_d<64, true>(a, grid, stream) : launch_dkdv_d<64, false>(a, grid, stream);
   }
   return hipGetLastError();
 }
@@ -767,6 +815,7 @@ hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream) {
 }
 
 hipError_t launch_bwd_finish(const BwdArgs& a, hipStream_t stream) {
+  if (dsink_in_dkdv(a)) return hipSuccess;  // the dK/dV launch wrote dK, dV and dSink itself
   const long long n4 = (long long)a.T * a.Hkv * (a.D / 4);
   long long nsum = (n4 + 255) / 256;
   if (nsum > 4096) nsum = 4096;

@@ -17,8 +17,8 @@ constexpr int kBwdNumKernels = 3;
 constexpr int kDecodeNumKernels = 2;  // partial, combine
 constexpr int kDecodeMaxCols = 1024;  // (new token, query head) pairs per KV head: max_q * Hq / Hkv
 hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream);      // dQ, -D_i, -LSE/scale, dSink partials
-hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream);    // dK, dV (or partials per head half)
-hipError_t launch_bwd_finish(const BwdArgs& a, hipStream_t stream);  // dK, dV = sum of halves; dSink
+hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream);    // dK, dV (or partials per head half); dSink without halves
+hipError_t launch_bwd_finish(const BwdArgs& a, hipStream_t stream);  // with head halves: dK, dV = sum of halves; dSink
 
 // Inference-shaped forward: per-chunk partials, then the combine with the sink.
 // events: NULL, or kDecodeNumKernels + 1 events recorded before, between and after the kernels

@@ -149,7 +149,12 @@ int attn_sink_bwd_noalloc(const void* q, const void* k, const void* v, const flo
  * per-kernel timing. `events` holds hipEvent_t handles created by the caller; num_events must be
  * attn_sink_bwd_num_kernels() + 1. An entry may be NULL: nothing is recorded at that point (each
  * record costs a few microseconds of GPU time, so a caller timing one kernel passes only the two
- * events around it). Passing events == NULL behaves like attn_sink_bwd.
+ * events around it). Passing events == NULL behaves like attn_sink_bwd. A kernel the call does not
+ * need is not launched and its two events are recorded back to back: the third kernel
+ * (attn_sink_bwd_finish_kernel: the sum of the dK/dV head halves, if any, then the dSink
+ * reduction) is left out when the dK/dV pass has no head halves and at most 2048 key blocks of 64
+ * over all sequences and KV heads; that launch then reduces dSink itself. (The pass splits the
+ * heads for an even Hq/Hkv with fewer than 2048 such blocks, or fewer than 512 with a window.)
  */
 int attn_sink_bwd_timed(const void* q, const void* k, const void* v, const float* sinks, const void* out,
                         const float* lse, const void* dout, int causal, int window, const int32_t* cu_seqlens,

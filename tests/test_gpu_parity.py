@@ -153,12 +153,23 @@ def test_tiny_workload_full_parity():
     check_full(inp, run_gpu(inp))
 
 
-def test_empty_input():
-    say("[gpu] empty input (T = 0)")
-    inp = make_inputs((0,), 4, 2, 64, seed=1)
+@pytest.mark.parametrize("hq,hkv,window", [(4, 2, 0), (3, 1, 0), (3, 1, 16)])
+def test_empty_input(hq, hkv, window):
+    # Even GQA ratios split the dK/dV pass's heads into halves and reduce dSink in the finish
+    # kernel; odd ones reduce it at the end of the dK/dV launch. Either way every head's dSink is
+    # written (zero) although no row exists: the buffer starts as NaN.
+    say(f"[gpu] empty input (T = 0), heads {hq}/{hkv}, window {window}")
+    inp = make_inputs((0,), hq, hkv, 64, window=window, seed=1)
     g = run_gpu(inp)
     assert g["out"].numel() == 0
     assert torch.all(g["dsinks"] == 0)
+    dev = torch.device("cuda:0")
+    q, k, v, dout = (t.to(dev).contiguous() for t in (inp.q, inp.k, inp.v, inp.dout))
+    ds = torch.full((hq,), float("nan"), device=dev)
+    asa.bwd(q, k, v, inp.sinks.to(dev), g["out"], g["lse"], dout, inp.cu_seqlens.to(dev), inp.max_seqlen,
+            inp.causal, inp.window, dsinks=ds)
+    torch.cuda.synchronize()
+    assert torch.all(ds == 0)
 
 
 @pytest.mark.parametrize("d", [64, 128])
