@@ -79,19 +79,21 @@ KERNEL_FLOPS_PER_PAIR_D = {
 # (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch) scaled by what the same counters read for the
 # copy probe; valid only for kernel sources with the recorded digest.
 TRAFFIC = {
-    ("causal4k", "attn_sink_bwd_dkdv_kernel"): {"bytes": 146634536, "digest": "44f8c43fa5eb5433"},
-    ("window4k", "attn_sink_bwd_dkdv_kernel"): {"bytes": 105793227, "digest": "44f8c43fa5eb5433"},
-    ("window4k", "attn_sink_bwd_dq_kernel"): {"bytes": 213175578, "digest": "44f8c43fa5eb5433"},
-    ("varlen_window", "attn_sink_bwd_dkdv_kernel"): {"bytes": 1706812248, "digest": "44f8c43fa5eb5433"},
-    ("varlen_window", "attn_sink_bwd_dq_kernel"): {"bytes": 3648308856, "digest": "44f8c43fa5eb5433"},
-    ("band4k", "attn_sink_bwd_dkdv_kernel"): {"bytes": 119770026, "digest": "44f8c43fa5eb5433"},
-    ("band4k", "attn_sink_bwd_dq_kernel"): {"bytes": 213320701, "digest": "44f8c43fa5eb5433"},
-    ("decode32k", "attn_sink_decode_partial_kernel"): {"bytes": 368462096, "digest": "44f8c43fa5eb5433"},
-    ("causal4k", "attn_sink_fwd_kernel"): {"bytes": 114545573, "digest": "44f8c43fa5eb5433"},
-    ("causal4k", "attn_sink_bwd_dq_kernel"): {"bytes": 221308528, "digest": "44f8c43fa5eb5433"},
-    ("varlen_causal", "attn_sink_bwd_dkdv_kernel"): {"bytes": 8740251349, "digest": "44f8c43fa5eb5433"},
-    ("long32k", "attn_sink_bwd_dkdv_kernel"): {"bytes": 35438920660, "digest": "44f8c43fa5eb5433"},
+    ("causal4k", "attn_sink_bwd_dkdv_kernel"): {"bytes": 146656344, "digest": "a3a1135a4abf74c7"},
+    ("window4k", "attn_sink_bwd_dkdv_kernel"): {"bytes": 106700506, "digest": "a3a1135a4abf74c7"},
+    ("window4k", "attn_sink_bwd_dq_kernel"): {"bytes": 213161614, "digest": "a3a1135a4abf74c7"},
+    ("varlen_window", "attn_sink_bwd_dkdv_kernel"): {"bytes": 1708273888, "digest": "a3a1135a4abf74c7"},
+    ("varlen_window", "attn_sink_bwd_dq_kernel"): {"bytes": 3648234371, "digest": "a3a1135a4abf74c7"},
+    ("band4k", "attn_sink_bwd_dkdv_kernel"): {"bytes": 121165482, "digest": "a3a1135a4abf74c7"},
+    ("band4k", "attn_sink_bwd_dq_kernel"): {"bytes": 213207535, "digest": "a3a1135a4abf74c7"},
+    ("decode32k", "attn_sink_decode_partial_kernel"): {"bytes": 368469960, "digest": "a3a1135a4abf74c7"},
+    ("causal4k", "attn_sink_fwd_kernel"): {"bytes": 114557098, "digest": "a3a1135a4abf74c7"},
+    ("causal4k", "attn_sink_bwd_dq_kernel"): {"bytes": 221363909, "digest": "a3a1135a4abf74c7"},
+    ("varlen_causal", "attn_sink_bwd_dkdv_kernel"): {"bytes": 8728681667, "digest": "a3a1135a4abf74c7"},
+    ("long32k", "attn_sink_bwd_dkdv_kernel"): {"bytes": 35308073228, "digest": "a3a1135a4abf74c7"},
 }
+
+
 def _code_only(text: str) -> str:
     """C/C++ source without its comments and with whitespace runs collapsed (string literals kept)."""
     out = re.sub(r'"(?:\\.|[^"\\\n])*"|//[^\n]*|/\*.*?\*/',
