@@ -172,6 +172,18 @@ def test_empty_input(hq, hkv, window):
     assert torch.all(ds == 0)
 
 
+@pytest.mark.parametrize("nseq", [256, 257])
+def test_dsink_reduction_either_side_of_the_fold_limit(nseq):
+    # 8 KV heads x nseq sequences of at most 64 tokens (one key block each), window 32, so no head
+    # halves: 2048 key-block workgroups reduce dSink at the end of the dK/dV launch, 2056 leave it
+    # to the finish kernel. Every element against the oracle.
+    rng = np.random.default_rng(nseq)
+    lengths = tuple(int(x) for x in rng.integers(1, 65, nseq - 1)) + (64,)
+    say(f"[gpu] dSink reduction at the fold limit: {nseq} sequences x 8 KV heads, {sum(lengths)} tokens")
+    inp = make_inputs(lengths, 16, 8, 64, causal=True, window=32, seed=nseq)
+    check_full(inp, run_gpu(inp))
+
+
 @pytest.mark.parametrize("d", [64, 128])
 def test_backward_is_deterministic(d):
     inp = make_inputs((700, 333), 16, 2, d, causal=True, window=0, seed=2)
