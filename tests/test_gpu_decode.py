@@ -50,8 +50,10 @@ def bf16_half_ulp(x):
     return np.ldexp(1.0, (e - 8).astype(np.int64))
 
 
-def check_against_oracle(d, out, lse, scale=None):
-    ro, rl = oracle.decode_forward(d.q, d.k, d.v, d.sinks, d.cu_q, d.cu_k, d.window, scale)
+def check_against_oracle(d, out, lse, scale=None, ref=None):
+    """O and LSE of a decode call against the oracle (``ref``: its (out, lse), if already computed)."""
+    ro, rl = ref if ref is not None else oracle.decode_forward(d.q, d.k, d.v, d.sinks, d.cu_q, d.cu_k, d.window,
+                                                               scale)
     o = out.double().cpu().numpy()
     l = lse.double().cpu().numpy()
     assert np.isfinite(o).all(), "out has non-finite values"
@@ -154,10 +156,20 @@ def test_decode_rejects_too_many_columns():
 
 @pytest.mark.parametrize("name", ["decode32k", "decode32k_nq4", "decode32k_window"])
 def test_decode_full_size(name):
+    """Both decode forwards on caches of 16k-32k tokens per sequence, every element against the oracle."""
     d = make_decode_workload_inputs(name, seed=0)
     say(f"decode {name}: Lk={[int(x) for x in (d.cu_k[1:] - d.cu_k[:-1])]} max_q={d.max_q}")
+    ref = oracle.decode_forward(d.q, d.k, d.v, d.sinks, d.cu_q, d.cu_k, d.window, None)
     out, lse = run_decode(d, torch.bfloat16)
-    check_against_oracle(d, out, lse)
+    say("  split-KV decode:")
+    check_against_oracle(d, out, lse, ref=ref)
+    dev = torch.device("cuda:0")
+    q, k, v = (t.to(dev).contiguous() for t in (d.q, d.k, d.v))
+    out_o, lse_o = asa.decode_fwd_ordered(q, k, v, d.sinks.to(dev), d.cu_q.to(dev), d.cu_k.to(dev), d.max_q, d.max_k,
+                                          window=d.window, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    say("  order-preserving decode:")
+    check_against_oracle(d, out_o, lse_o, ref=ref)
 
 
 @pytest.mark.parametrize("window,d", [(0, 64), (128, 64), (0, 128)])
