@@ -17,8 +17,11 @@ def say(msg):
     sys.stdout.flush()
 
 
-def test_training_step_graph_replays_match_eager():
-    inp = make_inputs((700, 1, 333), 16, 2, causal=True, window=0, seed=21)
+@pytest.mark.parametrize("hq,hkv", [(16, 2), (3, 1)])
+def test_training_step_graph_replays_match_eager(hq, hkv):
+    # GQA 8: the backward's three kernels (head halves, finish); GQA 3: two (the dK/dV launch
+    # reduces dSink).
+    inp = make_inputs((700, 1, 333), hq, hkv, causal=True, window=0, seed=21)
     dev = torch.device("cuda:0")
     q, k, v, dout = (t.to(dev).contiguous() for t in (inp.q, inp.k, inp.v, inp.dout))
     sinks, cu = inp.sinks.to(dev), inp.cu_seqlens.to(dev)
